@@ -1,0 +1,25 @@
+"""MI355X-native fused scaled-dot-product-attention forward.
+
+Python front end of the C-ABI library ``libsdpa_mi355x.so`` (see
+``include/sdpa.h``): ``prefill`` (causal or full, GQA) and ``decode`` (two-phase
+split-KV), plus the host planner ``plan``.  The compute runs in hand-written
+HIP kernels for gfx950; PyTorch only provides device memory and streams.
+"""
+from .binding import (  # noqa: F401
+    BF16,
+    F16,
+    FP8_E4M3,
+    Plan,
+    Problem,
+    SdpaError,
+    decode,
+    decode_workspace,
+    load,
+    loop_counts,
+    make_problem,
+    plan,
+    prefill,
+)
+
+__all__ = ["prefill", "decode", "decode_workspace", "plan", "loop_counts", "make_problem", "load", "Problem", "Plan",
+           "SdpaError", "F16", "BF16", "FP8_E4M3"]

@@ -1,0 +1,223 @@
+"""ctypes binding of libsdpa_mi355x.so (the C ABI in include/sdpa.h).
+
+Argument marshalling only: every step of attention runs in the HIP kernels.
+PyTorch supplies device memory and the current HIP stream.  There is no CPU
+fallback: if the library is missing, importing the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdpa_mi355x.so")
+
+F16, BF16, FP8_E4M3 = 0, 1, 2
+STATUS = {
+    0: "SDPA_OK", 1: "SDPA_ERR_NULL_PTR", 2: "SDPA_ERR_BAD_SHAPE", 3: "SDPA_ERR_BAD_SCALE",
+    4: "SDPA_ERR_UNSUPPORTED", 5: "SDPA_ERR_MISALIGNED", 6: "SDPA_ERR_WORKSPACE", 7: "SDPA_ERR_HIP",
+}
+
+# every symbol include/sdpa.h declares
+EXPORTS = (
+    "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
+    "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
+    "sdpa_loop_counts",
+)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+        ("head_q", ctypes.c_int32), ("head_kv", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("scale", ctypes.c_float), ("q_descale", ctypes.c_float),
+        ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kernel", "waves_per_group", "rows_per_wave", "heads_per_group", "qtiles_per_group", "block_q",
+        "block_k", "stages", "q_tiles", "kv_blocks", "num_groups", "num_splits", "blocks_per_split",
+        "combine_groups")] + [("lds_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class LoopCounts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "q_blocks", "k_blocks", "d_loops", "vv_loops", "blocks_visited", "blocks_masked", "qk_tiles", "pv_tiles",
+        "softmax_tiles")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Loads the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m attention_flash_sdpa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Problem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.sdpa_abi_version.restype = ctypes.c_int
+    lib.sdpa_status_string.restype = ctypes.c_char_p
+    lib.sdpa_status_string.argtypes = [ctypes.c_int]
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_plan.restype = ctypes.c_int
+    lib.sdpa_plan.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Plan)]
+    lib.sdpa_loop_counts.restype = ctypes.c_int
+    lib.sdpa_loop_counts.argtypes = [ctypes.c_int] * 9 + [ctypes.POINTER(LoopCounts)]
+    lib.sdpa_prefill_workspace_bytes.restype = sz
+    lib.sdpa_prefill_workspace_bytes.argtypes = [P]
+    lib.sdpa_decode_workspace_bytes.restype = sz
+    lib.sdpa_decode_workspace_bytes.argtypes = [P, ctypes.c_int]
+    lib.sdpa_prefill_fwd.restype = ctypes.c_int
+    lib.sdpa_prefill_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sdpa_decode_fwd.restype = ctypes.c_int
+    lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SdpaError(status, (load().sdpa_last_error() or b"").decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    m = {torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def make_problem(*, batch, q_len, kv_len, head_q, head_kv, d_qk, d_v, in_dtype, out_dtype, causal, scale,
+                 descale=(1.0, 1.0, 1.0)) -> Problem:
+    return Problem(int(batch), int(q_len), int(kv_len), int(head_q), int(head_kv), int(d_qk), int(d_v),
+                   int(in_dtype), int(out_dtype), int(bool(causal)), float(scale), float(descale[0]),
+                   float(descale[1]), float(descale[2]))
+
+
+def plan(problem: Problem, *, decode: bool = False, num_cus: int = 0, num_splits: int = 0) -> Plan:
+    out = Plan()
+    _check(load().sdpa_plan(ctypes.byref(problem), int(decode), int(num_cus), int(num_splits), ctypes.byref(out)))
+    return out
+
+
+def loop_counts(*, q_len, kv_len, d_qk, d_v, block_q, block_k, block_d, block_v, causal) -> LoopCounts:
+    out = LoopCounts()
+    _check(load().sdpa_loop_counts(int(q_len), int(kv_len), int(d_qk), int(d_v), int(block_q), int(block_k),
+                                   int(block_d), int(block_v), int(bool(causal)), ctypes.byref(out)))
+    return out
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1.0, 1.0, 1.0), out_dtype=None,
+            stream=None):
+    """O = softmax(Q K^T * scale + mask) V on the GPU.
+
+    q [B, Sq, Hq, D], k [B, Sk, Hkv, D], v [B, Sk, Hkv, Dv] contiguous device
+    tensors; returns O [B, Sq, Hq, Dv] (``out`` if given).  ``lse`` is an
+    optional fp32 [B, Hq, Sq] tensor to receive the log-sum-exp."""
+    import torch
+
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    Dv = v.shape[-1]
+    for t in (q, k, v):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is None:
+        out = torch.empty(B, Sq, Hq, Dv, dtype=out_dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    pr = make_problem(batch=B, q_len=Sq, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=Dv,
+                      in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=causal, scale=scale,
+                      descale=descale)
+    lib = load()
+    ws_bytes = lib.sdpa_prefill_workspace_bytes(ctypes.byref(pr))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check(lib.sdpa_prefill_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
+                                ws_bytes, _stream_handle(stream)))
+    return out
+
+
+@dataclass
+class DecodeWorkspace:
+    tensor: object
+    nbytes: int
+
+
+def decode_workspace(q, k, v, *, num_splits=0, descale=(1.0, 1.0, 1.0)):
+    """Allocates the decode workspace for these shapes (reusable across calls)."""
+    import torch
+
+    pr = _decode_problem(q, k, v, 1.0, descale, None)
+    n = load().sdpa_decode_workspace_bytes(ctypes.byref(pr), int(num_splits))
+    if n == 0:
+        raise SdpaError(2, "invalid decode problem")
+    return DecodeWorkspace(torch.empty(n, dtype=torch.uint8, device=q.device), n)
+
+
+def _decode_problem(q, k, v, scale, descale, out):
+    B, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    Dv = v.shape[-1]
+    od = _dtype_code(out) if out is not None else _dtype_code(q)
+    return make_problem(batch=B, q_len=1, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=Dv,
+                        in_dtype=_dtype_code(q), out_dtype=od, causal=False, scale=scale, descale=descale)
+
+
+def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=None, descale=(1.0, 1.0, 1.0),
+           stream=None):
+    """Two-phase split-KV decode: q [B, Hq, D], k/v cache [B, Sk, Hkv, D|Dv];
+    returns O [B, Hq, Dv].  ``lse`` is an optional fp32 [B, Hq] tensor."""
+    import torch
+
+    B, Hq, D = q.shape
+    Dv = v.shape[-1]
+    for t in (q, k, v):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if out is None:
+        out = torch.empty(B, Hq, Dv, dtype=q.dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    pr = _decode_problem(q, k, v, scale, descale, out)
+    lib = load()
+    if workspace is None:
+        workspace = decode_workspace(q, k, v, num_splits=num_splits, descale=descale)
+    _check(lib.sdpa_decode_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(num_splits),
+                               _ptr(workspace.tensor), workspace.nbytes, _stream_handle(stream)))
+    return out

@@ -1,0 +1,220 @@
+// planner.cpp -- argument validation and the tile-config / launch planner.
+// Pure host code: no HIP calls, testable without a GPU through sdpa_plan().
+//
+// The planner plays the role the pages give to host-side dispatch: the launcher
+// selection keyed on dtype and head dim ("Xe SDPA Forward Mainloop", section
+// "Who decides the instantiated mainloop?") and loop counts precomputed on the
+// host ("xe2-sdp-kernels", section "Inner-loop rules").
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sdpa_bounds.h"
+#include "sdpa_internal.h"
+
+namespace sdpa {
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is16(int dt) { return dt == SDPA_F16 || dt == SDPA_BF16; }
+
+int prefill_kernel_id(const sdpa_problem_t& p) {
+  if (is16(p.in_dtype) && p.out_dtype == p.in_dtype && p.d_qk == p.d_v) {
+    const bool bf = p.in_dtype == SDPA_BF16;
+    if (p.d_qk == 64) return bf ? kPrefillBf16D64 : kPrefillF16D64;
+    if (p.d_qk == 128) return bf ? kPrefillBf16D128 : kPrefillF16D128;
+  }
+  if (p.in_dtype == SDPA_FP8_E4M3 && p.d_qk == 192 && p.d_v == 128 && p.out_dtype == SDPA_BF16)
+    return kPrefillFp8D192;
+  return -1;
+}
+
+int decode_kernel_id(const sdpa_problem_t& p) {
+  if (is16(p.in_dtype) && p.out_dtype == p.in_dtype && p.d_qk == p.d_v) {
+    const bool bf = p.in_dtype == SDPA_BF16;
+    if (p.d_qk == 64) return bf ? kDecodeBf16D64 : kDecodeF16D64;
+    if (p.d_qk == 128) return bf ? kDecodeBf16D128 : kDecodeF16D128;
+  }
+  return -1;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_last_error[0] = 0; }
+
+const char* last_error_text() { return g_last_error; }
+
+sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
+                        sdpa_plan_t* plan) {
+  memset(plan, 0, sizeof *plan);
+  if (num_cus <= 0) num_cus = kDefaultCUs;
+  if (p.batch < 0 || p.q_len < 0 || p.kv_len < 0) {
+    set_error("negative size: batch=%d q_len=%d kv_len=%d", p.batch, p.q_len, p.kv_len);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (p.head_q <= 0 || p.head_kv <= 0 || p.head_q % p.head_kv != 0) {
+    set_error("head_q=%d must be a positive multiple of head_kv=%d", p.head_q, p.head_kv);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (p.d_qk <= 0 || p.d_v <= 0) {
+    set_error("head dims must be positive (d_qk=%d d_v=%d)", p.d_qk, p.d_v);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (!isfinite(p.scale) || p.scale < 0.f) {
+    set_error("scale must be finite and >= 0 (got %g)", (double)p.scale);
+    return SDPA_ERR_BAD_SCALE;
+  }
+  const float ds[3] = {p.q_descale, p.k_descale, p.v_descale};
+  for (float d : ds)
+    if (!isfinite(d) || d < 0.f) {
+      set_error("descale factors must be finite and >= 0 (got %g)", (double)d);
+      return SDPA_ERR_BAD_SCALE;
+    }
+  const int64_t G = p.head_q / p.head_kv;
+  // element offsets inside one batch entry are 32-bit in the kernels
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)p.q_len * p.head_q * (p.d_qk > p.d_v ? p.d_qk : p.d_v) >= lim ||
+      (int64_t)p.kv_len * p.head_kv * (p.d_qk > p.d_v ? p.d_qk : p.d_v) * 2 >= lim) {
+    set_error("one batch entry exceeds 2^31 elements (q_len=%d kv_len=%d)", p.q_len, p.kv_len);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+
+  if (!is_decode) {
+    const int kid = prefill_kernel_id(p);
+    if (kid < 0 || kid == kPrefillFp8D192) {
+      set_error("unsupported prefill (in_dtype=%d, out_dtype=%d, d_qk=%d, d_v=%d)", p.in_dtype, p.out_dtype,
+                p.d_qk, p.d_v);
+      return SDPA_ERR_UNSUPPORTED;
+    }
+    plan->kernel = kid;
+    plan->waves_per_group = kPrefillWaves;
+    plan->rows_per_wave = kRowsPerWave;
+    // Pack query heads of one GQA group into the workgroup when the group
+    // size allows it (K/V blocks in LDS are then shared by several heads);
+    // otherwise stack consecutive query tiles of one head.  Short queries
+    // pack heads even when the group size is not a multiple of the pack.
+    int hp;
+    if (G % 4 == 0) hp = 4;
+    else if (G % 2 == 0) hp = 2;
+    else hp = 1;
+    if (p.q_len <= kRowsPerWave) hp = (int)(G < kPrefillWaves ? G : kPrefillWaves);
+    while (kPrefillWaves % hp) --hp;
+    plan->heads_per_group = hp;
+    plan->qtiles_per_group = kPrefillWaves / hp;
+    plan->block_q = kRowsPerWave * plan->qtiles_per_group;
+    plan->block_k = kPrefillBlockK;
+    plan->stages = 2;
+    plan->q_tiles = (int32_t)ceil_div(p.q_len, plan->block_q);
+    plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);
+    const int64_t head_groups = ceil_div(G, hp);
+    const int64_t groups = (int64_t)p.batch * p.head_kv * head_groups * plan->q_tiles;
+    if (groups >= lim) {
+      set_error("grid too large (%lld workgroups)", (long long)groups);
+      return SDPA_ERR_BAD_SHAPE;
+    }
+    plan->num_groups = (int32_t)groups;
+    const int esz = p.in_dtype == SDPA_FP8_E4M3 ? 1 : 2;
+    plan->lds_bytes = (uint64_t)plan->stages * plan->block_k * (p.d_qk + p.d_v) * esz;
+    plan->workspace_bytes = 0;
+    return SDPA_OK;
+  }
+
+  // ---- split-KV decode ----------------------------------------------------
+  if (p.q_len != 1) {
+    set_error("decode needs q_len == 1 (got %d)", p.q_len);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  const int kid = decode_kernel_id(p);
+  if (kid < 0) {
+    set_error("unsupported decode (in_dtype=%d, out_dtype=%d, d_qk=%d, d_v=%d)", p.in_dtype, p.out_dtype, p.d_qk,
+              p.d_v);
+    return SDPA_ERR_UNSUPPORTED;
+  }
+  if (G > kDecodeMaxGroup) {
+    set_error("decode supports at most %d query heads per KV head (got %lld)", kDecodeMaxGroup, (long long)G);
+    return SDPA_ERR_UNSUPPORTED;
+  }
+  if (num_splits < 0 || num_splits > 4096) {
+    set_error("num_splits must be in [0, 4096] (got %d)", num_splits);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  plan->kernel = kid;
+  plan->waves_per_group = kDecodeWaves;
+  plan->rows_per_wave = kDecodeMaxGroup;
+  plan->heads_per_group = (int32_t)G;
+  plan->qtiles_per_group = 1;
+  plan->block_q = 1;
+  plan->block_k = kDecodeBlockK;
+  plan->stages = 2;
+  plan->q_tiles = 1;
+  plan->kv_blocks = (int32_t)ceil_div(p.kv_len, kDecodeBlockK);
+  const int64_t pairs = (int64_t)p.batch * p.head_kv;
+  int64_t S;
+  if (num_splits > 0) {
+    S = num_splits;
+    plan->blocks_per_split = (int32_t)(plan->kv_blocks > 0 ? ceil_div(plan->kv_blocks, S) : 1);
+  } else {
+    // Enough wavefronts to keep every CU streaming (8 per CU), but no split
+    // shorter than two blocks, so the per-split overhead (Q load, partial
+    // write, combine) stays a few percent of the K/V bytes.
+    const int64_t target = (int64_t)num_cus * 8;
+    S = pairs > 0 ? ceil_div(target, pairs) : 1;
+    const int64_t max_s = plan->kv_blocks / 2 > 0 ? plan->kv_blocks / 2 : 1;
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
+    plan->blocks_per_split = (int32_t)(plan->kv_blocks > 0 ? ceil_div(plan->kv_blocks, S) : 1);
+    S = plan->kv_blocks > 0 ? ceil_div(plan->kv_blocks, plan->blocks_per_split) : 1;
+  }
+  plan->num_splits = (int32_t)S;
+  const int64_t waves = pairs * S;
+  if (waves >= lim) {
+    set_error("grid too large (%lld waves)", (long long)waves);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  plan->num_groups = (int32_t)ceil_div(waves, kDecodeWaves);
+  plan->combine_groups = (int32_t)((int64_t)p.batch * p.head_q);
+  plan->lds_bytes = (uint64_t)kDecodeWaves * 2 * kDecodeBlockK * p.d_v * 2;
+  const uint64_t po = (uint64_t)p.batch * p.head_q * S * p.d_v * 4;
+  const uint64_t pml = (uint64_t)p.batch * p.head_q * S * 2 * 4;
+  plan->workspace_bytes = ((po + 255) / 256) * 256 + pml;
+  return SDPA_OK;
+}
+
+sdpa_status_t loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k, int block_d,
+                          int block_v, bool causal, sdpa_loop_counts_t* out) {
+  memset(out, 0, sizeof *out);
+  if (q_len < 0 || kv_len < 0 || d_qk <= 0 || d_v <= 0 || block_q <= 0 || block_k <= 0 || block_d <= 0 ||
+      block_v <= 0) {
+    set_error("loop counts need non-negative lengths and positive dims / tiles");
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  out->q_blocks = ceil_div(q_len, block_q);
+  out->k_blocks = ceil_div(kv_len, block_k);
+  out->d_loops = ceil_div(d_qk, block_d);
+  out->vv_loops = ceil_div(d_v, block_v);
+  for (int64_t qb = 0; qb < out->q_blocks; ++qb) {
+    const int row0 = (int)(qb * block_q);
+    const int row_end = row0 + block_q < q_len ? row0 + block_q : q_len;
+    const KBlockRange r = kblock_range(row0, row_end, q_len, kv_len, block_k, causal);
+    out->blocks_visited += r.n_blocks;
+    out->blocks_masked += r.n_blocks - r.n_full;
+  }
+  out->qk_tiles = out->blocks_visited * out->d_loops;
+  out->pv_tiles = out->blocks_visited * out->vv_loops;
+  out->softmax_tiles = out->blocks_visited;
+  return SDPA_OK;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,342 @@
+// prefill.hip -- fused SDPA forward mainloop for gfx950 (16-bit inputs).
+//
+// Structure follows "Xe SDPA Forward Mainloop -- Key Loops + Shapes"
+// (sections "Startup prefetch + init", "mainloop_body(K)", "softmax()
+// helper", "Outer K-block loop"): a resident Q tile, K/V blocks streamed
+// through a two-stage prefetch pipeline, S = Q K^T on the matrix cores, mask,
+// online softmax with exp2 and a log2(e)-folded scale, and P V accumulated in
+// fp32.  The MI355X mapping:
+//
+//  * One workgroup = 4 wavefronts that all read the same K/V blocks: either
+//    up to 4 query heads of one GQA group on the same 32 query rows, or
+//    consecutive 32-row tiles of one head (the planner picks).
+//  * Each wave computes S^T = K Q^T (the operand order the page's source
+//    comment "S = K * Q" uses), so lane l and lane l^32 together hold all the
+//    scores of query row l%32.  Row max / row sum are in-lane reductions plus
+//    one permlane32 swap; the running max, sum and rescale factor stay in
+//    scalar registers of that lane.
+//  * The probabilities are packed to 16 bits in place and used directly as the
+//    B operand of O^T = V^T P^T, so P never leaves registers; O^T stays in
+//    the MFMA accumulators and its rescale by 2^(m_old - m_new) is lane-local.
+//  * K/V blocks of 64 keys go global -> LDS with direct 16-byte-per-lane loads
+//    (no register staging), double buffered, into rows whose 16-byte slots
+//    are XOR-swizzled so that K fragment reads (ds_read_b128) and transposed
+//    V fragment reads (ds_read_b64_tr_b16) are free of bank conflicts.
+//  * The K loop is split on the host-computable block count into a branch-free
+//    unmasked part and a peeled masked tail ("xe2-sdp-kernels", section
+//    "Inner-loop rules"): only the tail blocks evaluate the causal/remainder
+//    predicate.
+#include <math.h>
+
+#include <type_traits>
+
+#include "sdpa_bounds.h"
+#include "sdpa_device.h"
+#include "sdpa_internal.h"
+
+namespace sdpa {
+
+// Spreads consecutive logical workgroup ids over one XCD: hardware dispatches
+// workgroup i to XCD i % 8, so logical ids [x*n/8, (x+1)*n/8) (which share
+// K/V heads) are served by XCD x and its L2.
+__device__ __forceinline__ int remap_xcd(int i, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = i & 7, j = i >> 3;
+  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+template <class T, int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(const PrefillArgs a) {
+  constexpr int BK = kPrefillBlockK;
+  constexpr int NW = kPrefillWaves;
+  constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
+  constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte slots per row
+  constexpr int KBYTES = BK * KROW, VBYTES = BK * VROW;
+  constexpr int STAGE = KBYTES + VBYTES;
+  constexpr int K_INSTR = BK * KCPR / 64 / NW;  // 1 KiB direct loads per wave per block
+  constexpr int V_INSTR = BK * VCPR / 64 / NW;
+  constexpr int NT = DV / 32;                   // O^T accumulator tiles
+  static_assert(KCPR >= 8 && VCPR >= 8, "swizzle needs >= 8 slots per row");
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "block too small for the fill");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem;
+
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5;  // lane half
+  const int l32 = lane & 31;
+
+  // ---- work decode -------------------------------------------------------
+  int wg = remap_xcd(blockIdx.x, a.num_groups);
+  int qt = wg % a.q_tiles;
+  int rest = wg / a.q_tiles;
+  const int hg = rest % a.head_groups;
+  rest /= a.head_groups;
+  const int g = rest % a.head_kv;
+  const int b = rest / a.head_kv;
+  if (CAUSAL) qt = a.q_tiles - 1 - qt;  // heaviest causal tiles first
+  const int hp_i = wave % a.heads_per_group;
+  const int qp_i = wave / a.heads_per_group;
+  // heads_per_group need not divide the group size: waves past the group's
+  // last head run the loop (uniform barriers) but store nothing
+  const bool head_ok = hg * a.heads_per_group + hp_i < a.group;
+  const int h = g * a.group + min(hg * a.heads_per_group + hp_i, a.group - 1);
+  const int Sq = a.q_len, Sk = a.kv_len, off = Sk - Sq;
+  const int wg_row0 = qt * (kRowsPerWave * a.qtiles_per_group);
+  const int row0 = wg_row0 + kRowsPerWave * qp_i;
+  const int wg_row_end = min(wg_row0 + kRowsPerWave * a.qtiles_per_group, Sq);
+
+  // K blocks of the workgroup: [0, n_full) unmasked, [n_full, n_blocks) masked
+  const KBlockRange kr = kblock_range(wg_row0, wg_row_end, Sq, Sk, BK, CAUSAL);
+  const int n_blocks = kr.n_blocks;
+  const int n_full = kr.n_full;
+
+  const int qrow = row0 + l32;
+  const bool row_ok = head_ok && qrow < Sq;
+  typedef uint16_t elem_t;
+  elem_t* __restrict__ optr = (elem_t*)a.o;
+
+  if (n_blocks == 0) {  // no visible key for any row of this workgroup
+    if (row_ok) {
+      elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
+      for (int c = hl * (DV / 2); c < (hl + 1) * (DV / 2); c += 8) *(u32x4_t*)(orow + c) = u32x4_t{0, 0, 0, 0};
+      if (a.lse != nullptr && hl == 0) a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = -INFINITY;
+    }
+    return;
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once ---------------
+  u32x4_t qf[D / 16];
+  {
+    const elem_t* qptr = (const elem_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4_t v = *(const u32x4_t*)(qptr + 16 * s);
+      qf[s] = row_ok ? v : u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  // ---- per-lane fill addresses (direct global -> LDS) ---------------------
+  const char* kg = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * (D * 2);
+  const char* vg = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * (DV * 2);
+  const int kstride = a.head_kv * D * 2;   // bytes between consecutive keys
+  const int vstride = a.head_kv * DV * 2;
+  int krow[K_INSTR], kcol[K_INSTR], vrow[V_INSTR], vcol[V_INSTR];
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) {
+    const int slot = (wave * K_INSTR + i) * 64 + lane;
+    const int r = slot / KCPR;
+    krow[i] = r;
+    kcol[i] = (((slot % KCPR) ^ (int)swz(r)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) {
+    const int slot = (wave * V_INSTR + i) * 64 + lane;
+    const int r = slot / VCPR;
+    vrow[i] = r;
+    vcol[i] = (((slot % VCPR) ^ (int)swz(r)) * 16);
+  }
+  const int last_key = Sk - 1;
+  auto issue_fill = [&](int kb, int stage) {
+    const uint32_t kl = lds0 + stage * STAGE + wave * K_INSTR * 1024;
+    const uint32_t vl = lds0 + stage * STAGE + KBYTES + wave * V_INSTR * 1024;
+#pragma unroll
+    for (int i = 0; i < K_INSTR; ++i) {
+      const int key = min(kb * BK + krow[i], last_key);
+      global_to_lds_16(kg + (size_t)key * kstride + kcol[i], kl + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < V_INSTR; ++i) {
+      const int key = min(kb * BK + vrow[i], last_key);
+      global_to_lds_16(vg + (size_t)key * vstride + vcol[i], vl + i * 1024);
+    }
+  };
+
+  // ---- per-lane LDS read offsets -----------------------------------------
+  // K fragment (A operand): key row l%32 (+32 for the second score tile),
+  // head-dim slot 2*s + l/32.
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) koff[s] = l32 * KROW + ((((2 * s + hl)) ^ (int)swz(l32)) << 4);
+  // V^T fragment (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16: lane
+  // (group gq = l/16, s = l%16) addresses key row 4*(gq/2) + s/4 (+8 for the
+  // second half, +16 per key chunk) at value columns 32t + 16*(gq%2) + 4*(s%4).
+  uint32_t voff[NT];
+  {
+    const int gq = lane >> 4, s = lane & 15;
+    const int r = 4 * (gq >> 1) + (s >> 2);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = 32 * t + 16 * (gq & 1) + 4 * (s & 3);
+      voff[t] = r * VROW + ((((col >> 3) ^ (int)swz(r))) << 4) + ((col & 7) << 1);
+    }
+  }
+
+  // ---- online softmax state ----------------------------------------------
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  float m_run = -INFINITY;  // running max of s2*S for query l%32 (log2 domain)
+  float l_run = 0.f;        // this lane's share of the running sum
+  const float s2 = a.s2;
+
+  auto block = [&](int kb, int stage, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const uint32_t ks = lds0 + stage * STAGE;
+    const uint32_t vs = ks + KBYTES;
+
+    // GEMM 1: S^T[key][query] over the head dimension
+    f32x16_t sc[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[0][r] = 0.f;
+      sc[1][r] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4_t k0 = lds_read_b128(ks + koff[s]);
+      const u32x4_t k1 = lds_read_b128(ks + koff[s] + 32 * KROW);
+      sc[0] = mfma32x32x16<T>(k0, qf[s], sc[0]);
+      sc[1] = mfma32x32x16<T>(k1, qf[s], sc[1]);
+    }
+
+    // mask (tail blocks only) + block row max in the log2 domain
+    float bmax;
+    if constexpr (MASKED) {
+      const int key0 = kb * BK + 4 * hl;
+      const int lim = CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1;  // last visible key
+      bmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * t + 8 * (r >> 2) + (r & 3);
+          const float x = key <= lim ? sc[t][r] * s2 : -INFINITY;
+          sc[t][r] = x;
+          bmax = fmaxf(bmax, x);
+        }
+    } else {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+      bmax = mx * s2;
+    }
+    bmax = pair_max(bmax);
+    const float m_new = fmaxf(m_run, bmax);
+    // rows that have seen no visible key keep m = -inf; subtract 0 instead so
+    // that no (-inf) - (-inf) appears (only possible in masked blocks)
+    const float m_sub = MASKED ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
+    const float alpha = fast_exp2(m_run - m_sub);
+    m_run = m_new;
+
+    // P = 2^(s2*S - m), row sum, and packing into the PV B operand
+    float psum = 0.f;
+    u32x4_t pf[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0, p1;
+        if constexpr (MASKED) {
+          p0 = fast_exp2(sc[t][r] - m_sub);
+          p1 = fast_exp2(sc[t][r + 1] - m_sub);
+        } else {
+          p0 = fast_exp2(fmaf(sc[t][r], s2, -m_sub));
+          p1 = fast_exp2(fmaf(sc[t][r + 1], s2, -m_sub));
+        }
+        psum += p0 + p1;
+        pf[2 * t + (r >> 3)][(r & 7) >> 1] = pack2<T>(p0, p1);
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+
+    // GEMM 2: O^T[dv][query] += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x2_t lo = lds_read_tr16(vs + voff[t] + (16 * c) * VROW);
+        const u32x2_t hi = lds_read_tr16(vs + voff[t] + (16 * c + 8) * VROW);
+        const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
+        acc[t] = mfma32x32x16<T>(vf, pf[c], acc[t]);
+      }
+  };
+
+  using Unmasked = std::false_type;
+  using Masked = std::true_type;
+
+  // ---- K-block pipeline ---------------------------------------------------
+  issue_fill(0, 0);
+  int kb = 0;
+  const int n_pref = n_blocks - 1;  // blocks that have a successor to prefetch
+  for (; kb < min(n_full, n_pref); ++kb) {
+    issue_fill(kb + 1, (kb + 1) & 1);
+    wait_vmcnt<K_INSTR + V_INSTR>();
+    __syncthreads();
+    block(kb, kb & 1, Unmasked{});
+    __syncthreads();
+  }
+  for (; kb < n_pref; ++kb) {
+    issue_fill(kb + 1, (kb + 1) & 1);
+    wait_vmcnt<K_INSTR + V_INSTR>();
+    __syncthreads();
+    block(kb, kb & 1, Masked{});
+    __syncthreads();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (kb < n_full)
+    block(kb, kb & 1, Unmasked{});
+  else
+    block(kb, kb & 1, Masked{});
+
+  // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
+  if (row_ok) {
+    elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = 32 * t + 8 * q4 + 4 * hl;
+        u32x2_t w;
+        w.x = pack2<T>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
+        w.y = pack2<T>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
+        *(u32x2_t*)(orow + col) = w;
+      }
+    if (a.lse != nullptr && hl == 0)
+      a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <class T, int D>
+static int launch_one(const PrefillArgs& a, int causal, ihipStream_t* stream) {
+  dim3 grid(a.num_groups), block(64 * kPrefillWaves);
+  if (causal)
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, true>), grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, false>), grid, block, 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
+  switch (plan.kernel) {
+    case kPrefillF16D64: return launch_one<F16, 64>(a, causal, stream);
+    case kPrefillBf16D64: return launch_one<Bf16, 64>(a, causal, stream);
+    case kPrefillF16D128: return launch_one<F16, 128>(a, causal, stream);
+    case kPrefillBf16D128: return launch_one<Bf16, 128>(a, causal, stream);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,192 @@
+// sdpa_abi.cpp -- the extern "C" front end declared in include/sdpa.h:
+// validation, planning and kernel launch.  Nothing here allocates device
+// memory or synchronises; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sdpa_internal.h"
+
+namespace sdpa {
+const char* last_error_text();
+}
+
+using namespace sdpa;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute-unit count of the current device, cached per device id.
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kDefaultCUs;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+sdpa_status_t hip_status(int err, const char* what) {
+  if (err == 0) return SDPA_OK;
+  set_error("%s: %s", what, hipGetErrorString((hipError_t)err));
+  return SDPA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_abi_version(void) { return SDPA_ABI_VERSION; }
+
+const char* sdpa_status_string(int status) {
+  switch (status) {
+    case SDPA_OK: return "SDPA_OK";
+    case SDPA_ERR_NULL_PTR: return "SDPA_ERR_NULL_PTR: a required pointer is NULL";
+    case SDPA_ERR_BAD_SHAPE: return "SDPA_ERR_BAD_SHAPE: invalid problem shape";
+    case SDPA_ERR_BAD_SCALE: return "SDPA_ERR_BAD_SCALE: scale or descale not finite or negative";
+    case SDPA_ERR_UNSUPPORTED: return "SDPA_ERR_UNSUPPORTED: dtype / head-dim combination not supported";
+    case SDPA_ERR_MISALIGNED: return "SDPA_ERR_MISALIGNED: data pointer not 16-byte aligned";
+    case SDPA_ERR_WORKSPACE: return "SDPA_ERR_WORKSPACE: workspace missing or too small";
+    case SDPA_ERR_HIP: return "SDPA_ERR_HIP: HIP runtime error";
+    default: return "unknown sdpa status";
+  }
+}
+
+const char* sdpa_last_error(void) { return last_error_text(); }
+
+sdpa_status_t sdpa_plan(const sdpa_problem_t* problem, int is_decode, int num_cus, int num_splits,
+                        sdpa_plan_t* plan) {
+  clear_error();
+  if (problem == nullptr || plan == nullptr) {
+    set_error("problem and plan must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  return make_plan(*problem, is_decode != 0, num_cus, num_splits, plan);
+}
+
+sdpa_status_t sdpa_loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k,
+                               int block_d, int block_v, int causal, sdpa_loop_counts_t* out) {
+  clear_error();
+  if (out == nullptr) {
+    set_error("out must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  return loop_counts(q_len, kv_len, d_qk, d_v, block_q, block_k, block_d, block_v, causal != 0, out);
+}
+
+size_t sdpa_prefill_workspace_bytes(const sdpa_problem_t* problem) {
+  if (problem == nullptr) return 0;
+  sdpa_plan_t plan;
+  if (make_plan(*problem, false, kDefaultCUs, 0, &plan) != SDPA_OK) return 0;
+  return (size_t)plan.workspace_bytes;
+}
+
+size_t sdpa_decode_workspace_bytes(const sdpa_problem_t* problem, int num_splits) {
+  if (problem == nullptr) return 0;
+  sdpa_plan_t plan;
+  if (make_plan(*problem, true, device_cus(), num_splits, &plan) != SDPA_OK) return 0;
+  return (size_t)plan.workspace_bytes;
+}
+
+sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
+                               void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  const sdpa_problem_t& p = *problem;
+  sdpa_plan_t plan;
+  sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan);
+  if (st != SDPA_OK) return st;
+  if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
+  if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr))) {
+    set_error("q, k, v and o must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u)) {
+    set_error("q, k, v, o must be 16-byte aligned and lse 4-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  if (plan.workspace_bytes > workspace_bytes || (plan.workspace_bytes > 0 && workspace == nullptr)) {
+    set_error("workspace of %llu bytes needed, %llu given", (unsigned long long)plan.workspace_bytes,
+              (unsigned long long)workspace_bytes);
+    return SDPA_ERR_WORKSPACE;
+  }
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.batch = p.batch;
+  a.q_len = p.q_len;
+  a.kv_len = p.kv_len;
+  a.head_q = p.head_q;
+  a.head_kv = p.head_kv;
+  a.group = p.head_q / p.head_kv;
+  a.heads_per_group = plan.heads_per_group;
+  a.qtiles_per_group = plan.qtiles_per_group;
+  a.q_tiles = plan.q_tiles;
+  a.head_groups = (a.group + plan.heads_per_group - 1) / plan.heads_per_group;
+  a.num_groups = plan.num_groups;
+  a.s2 = (float)((double)p.scale * 1.4426950408889634 * (double)p.q_descale * (double)p.k_descale);
+  a.v_descale = p.v_descale;
+  return hip_status(launch_prefill(a, plan, p.causal != 0, (ihipStream_t*)stream), "prefill launch");
+}
+
+sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
+                              void* o, float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  const sdpa_problem_t& p = *problem;
+  sdpa_plan_t plan;
+  sdpa_status_t st = make_plan(p, true, device_cus(), num_splits, &plan);
+  if (st != SDPA_OK) return st;
+  if (p.batch == 0) return SDPA_OK;
+  if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr))) {
+    set_error("q, k, v and o must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
+      ((uintptr_t)lse & 3u)) {
+    set_error("q, k, v, o, workspace must be 16-byte aligned and lse 4-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+    set_error("workspace of %llu bytes needed, %llu given", (unsigned long long)plan.workspace_bytes,
+              (unsigned long long)workspace_bytes);
+    return SDPA_ERR_WORKSPACE;
+  }
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  const uint64_t po = (uint64_t)p.batch * p.head_q * plan.num_splits * p.d_v * 4;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + ((po + 255) / 256) * 256);
+  a.batch = p.batch;
+  a.kv_len = p.kv_len;
+  a.head_q = p.head_q;
+  a.head_kv = p.head_kv;
+  a.group = p.head_q / p.head_kv;
+  a.num_splits = plan.num_splits;
+  a.blocks_per_split = plan.blocks_per_split;
+  a.split_waves = plan.num_splits;
+  a.s2 = (float)((double)p.scale * 1.4426950408889634 * (double)p.q_descale * (double)p.k_descale);
+  a.v_descale = p.v_descale;
+  return hip_status(launch_decode(a, plan, (ihipStream_t*)stream), "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// sdpa_device.h -- gfx950 device primitives shared by the attention kernels:
+// MFMA wrappers, cross-lane row reductions, packing of probabilities into MFMA
+// operands, direct global->LDS loads and the LDS swizzle.
+//
+// MFMA operand layouts used throughout (CDNA4, 64-lane wavefronts):
+//   32x32x16 (bf16/f16):  A[m][k]: lane l holds m = l%32, k = 8*(l/32) + j
+//                         B[k][n]: lane l holds n = l%32, k = 8*(l/32) + j
+//                         C[m][n]: lane l, register r holds n = l%32,
+//                                  m = 8*(r/4) + 4*(l/32) + r%4
+//   16x16x32 (bf16/f16):  A: m = l%16, k = 8*(l/16) + j; B: n = l%16, same k;
+//                         C: n = l%16, m = 4*(l/16) + r
+//   32x32x64 (fp8 e4m3):  as 32x32x16 with 32 k-contiguous bytes per lane.
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element r
+// (r = 0..3) from the 8-byte row addressed by group lane 4r + i/4, at
+// position i%4 -- a 4x16 -> 16x4 transpose of 16-bit elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+#define SDPA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type tags of the 16-bit inputs.
+struct Bf16 {
+  static constexpr bool is_bf16 = true;
+};
+struct F16 {
+  static constexpr bool is_bf16 = false;
+};
+
+// 32x32x16 MFMA on 8 packed 16-bit elements per lane (bit patterns in u32x4).
+template <class T>
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (T::is_bf16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <class T>
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (T::is_bf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Packs two fp32 values into one dword of 16-bit elements, round to nearest even.
+template <class T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (T::is_bf16) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  } else {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap(a, b) swaps
+// the upper half of a with the lower half of b, so with a = b = x the returned
+// pair is (own, partner) in lanes 0-31 and (partner, own) in lanes 32-63: the
+// max / sum of the pair is the same in both halves.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Butterfly over lanes with the given xor distance (ds_bpermute based).
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+  const int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// Transposed 8-byte LDS read (see the layout note at the top of the file).
+__device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t byte_addr) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS s16x4_t*)(uintptr_t)byte_addr);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t byte_addr) {
+  return *(SDPA_LDS const u32x4_t*)(uintptr_t)byte_addr;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds_base + 16*i (lds_base is wavefront-uniform).
+__device__ __forceinline__ void global_to_lds_16(const void* gptr, uint32_t lds_base) {
+  __builtin_amdgcn_global_load_lds((const void*)gptr, (SDPA_LDS void*)(uintptr_t)lds_base, 16, 0, 0);
+}
+
+// Waits until at most n vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS swizzle of 16-byte slots within a row: slot' = slot ^ swz(row) with
+// swz(row) = rotate-left of the low three row bits.  Eight consecutive rows
+// read at the same slot (K fragments) hit eight distinct slots, and four
+// consecutive rows read at two adjacent slots (transposed V fragments) hit
+// eight distinct slots, so neither access pattern has a bank conflict.
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return ((row & 3u) << 1) | ((row >> 2) & 1u); }
+
+}  // namespace sdpa

@@ -1,0 +1,74 @@
+// sdpa_internal.h -- host-side interfaces between the C-ABI front end, the
+// planner and the kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/sdpa.h"
+
+struct ihipStream_t;
+
+namespace sdpa {
+
+// Kernel instantiation ids chosen by the planner.
+enum KernelId : int32_t {
+  kPrefillF16D64 = 0,
+  kPrefillBf16D64 = 1,
+  kPrefillF16D128 = 2,
+  kPrefillBf16D128 = 3,
+  kPrefillFp8D192 = 4,
+  kDecodeF16D64 = 16,
+  kDecodeBf16D64 = 17,
+  kDecodeF16D128 = 18,
+  kDecodeBf16D128 = 19,
+};
+
+constexpr int kRowsPerWave = 32;   // prefill: query rows per wave (MFMA N)
+constexpr int kPrefillWaves = 4;   // prefill: waves per workgroup
+constexpr int kPrefillBlockK = 64; // prefill: keys per K/V block
+constexpr int kDecodeBlockK = 32;  // decode: keys per K/V block
+constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
+constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
+constexpr int kDefaultCUs = 256;
+
+// Validates the problem; fills *plan.  Writes a detail message through
+// set_error() on failure.  Pure host code.
+sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
+                        sdpa_plan_t* plan);
+
+sdpa_status_t loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k, int block_d,
+                          int block_v, bool causal, sdpa_loop_counts_t* out);
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t batch, q_len, kv_len, head_q, head_kv, group;
+  int32_t heads_per_group, qtiles_per_group, q_tiles, head_groups, num_groups;
+  float s2;         // scale * log2(e) * q_descale * k_descale
+  float v_descale;  // applied to the output (fp8 inputs), else 1
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* part_o;    // [batch, head_q, splits, d_v]
+  float* part_ml;   // [batch, head_q, splits, 2] = (max in log2 domain, sum)
+  int32_t batch, kv_len, head_q, head_kv, group;
+  int32_t num_splits, blocks_per_split, split_waves;
+  float s2;
+  float v_descale;
+};
+
+int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
+
+}  // namespace sdpa

@@ -1,0 +1,204 @@
+/*
+ * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product-attention
+ * forward library: a causal/full prefill mainloop and a two-phase split-KV
+ * decode, both computing
+ *
+ *     O = softmax(Q K^T * scale + mask) V
+ *
+ * with an online (blocked) softmax in fp32, as described on the page
+ * "Xe SDPA Forward Mainloop -- Key Loops + Shapes" (sections "mainloop_body(K)",
+ * "softmax() helper", "Full simplified pseudocode"), and the two-phase decode
+ * named on the page "xe2-sdp-kernels" (section "Assets").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major, batch outermost (the GQA layouts of
+ *    "xe2-sdp-kernels", section "GQA layout", with a leading batch):
+ *        Q [batch, q_len, head_q, d_qk]
+ *        K [batch, kv_len, head_kv, d_qk]
+ *        V [batch, kv_len, head_kv, d_v]
+ *        O [batch, q_len, head_q, d_v]
+ *        lse (optional) [batch, head_q, q_len] fp32, natural-log sum-exp of the
+ *        scaled visible scores; -inf for a row with no visible key.
+ *    For decode q_len is 1, so Q is [batch, head_q, d_qk] and O is
+ *    [batch, head_q, d_v].
+ *  - GQA: query head h reads KV head h / (head_q / head_kv).
+ *  - Causal (causal != 0) is aligned bottom-right: key j is visible to query i
+ *    iff j <= i + kv_len - q_len.  A row with no visible key (q_len > kv_len,
+ *    or kv_len == 0) yields O = 0 and lse = -inf, never NaN.
+ *  - Data pointers are device addresses, 16-byte aligned, owned by the caller
+ *    and left untouched except O, lse and the workspace.  The library never
+ *    allocates, frees or synchronises: work is enqueued on `stream` (a
+ *    hipStream_t passed as void*, NULL = the null stream) and results are
+ *    ready when the stream reaches that point.
+ *  - All validation happens before any launch; on an error nothing is
+ *    enqueued.  Calls are stateless and thread-safe; sdpa_last_error() keeps
+ *    a per-thread text for the last failing call.
+ *  - Supported (in_dtype, d_qk, d_v): fp16/bf16 with d_qk == d_v in {64, 128};
+ *    fp8 e4m3 (OCP "fn" variant, largest finite 448) with (192, 128).
+ *    out_dtype is fp16 or bf16.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDPA_ABI_VERSION 1
+
+typedef enum {
+  SDPA_F16 = 0,
+  SDPA_BF16 = 1,
+  SDPA_FP8_E4M3 = 2
+} sdpa_dtype_t;
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                     */
+  SDPA_ERR_BAD_SHAPE = 2,   /* negative size, head_q % head_kv != 0, decode
+                               with q_len != 1, sizes overflowing 32-bit
+                               element offsets per batch entry, ...          */
+  SDPA_ERR_BAD_SCALE = 3,   /* scale or a descale not finite, or negative     */
+  SDPA_ERR_UNSUPPORTED = 4, /* (dtype, d_qk, d_v) outside the supported set   */
+  SDPA_ERR_MISALIGNED = 5,  /* a data pointer not 16-byte aligned             */
+  SDPA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required        */
+  SDPA_ERR_HIP = 7          /* the HIP runtime reported an error              */
+} sdpa_status_t;
+
+/* One attention problem.  scale multiplies Q K^T (callers usually pass
+ * 1/sqrt(d_qk)); it is folded with log2(e) so that every exponential is a
+ * base-2 exponential ("Xe SDPA Forward Mainloop", section "Arguments /
+ * params").  q/k/v_descale are the per-tensor dequantisation factors of fp8
+ * inputs (x = x_q * descale); they must be 1 for fp16/bf16 inputs. */
+typedef struct sdpa_problem {
+  int32_t batch;
+  int32_t q_len;
+  int32_t kv_len;
+  int32_t head_q;
+  int32_t head_kv;
+  int32_t d_qk;
+  int32_t d_v;
+  int32_t in_dtype;  /* sdpa_dtype_t of Q, K and V */
+  int32_t out_dtype; /* sdpa_dtype_t of O: SDPA_F16 or SDPA_BF16 */
+  int32_t causal;    /* 0 = full, otherwise bottom-right causal */
+  float scale;       /* finite, >= 0 */
+  float q_descale;
+  float k_descale;
+  float v_descale;
+} sdpa_problem_t;
+
+/* Launch plan chosen by the host planner (pure host code, no GPU needed).
+ * Every wave owns rows_per_wave query rows of one head; a workgroup holds
+ * heads_per_group query heads of one KV group times qtiles_per_group
+ * consecutive query tiles, so all its waves read the same K/V blocks. */
+typedef struct sdpa_plan {
+  int32_t kernel;           /* internal instantiation id                       */
+  int32_t waves_per_group;  /* waves in one workgroup                           */
+  int32_t rows_per_wave;    /* query rows per wave (MFMA N dimension)           */
+  int32_t heads_per_group;  /* query heads sharing one workgroup                */
+  int32_t qtiles_per_group; /* wave-sized query tiles per head per workgroup    */
+  int32_t block_q;          /* query rows per head per workgroup                */
+  int32_t block_k;          /* keys per K/V block (one mainloop iteration)      */
+  int32_t stages;           /* K/V blocks resident in LDS (prefetch depth + 1)  */
+  int32_t q_tiles;          /* workgroup-sized query tiles per head             */
+  int32_t kv_blocks;        /* ceil(kv_len / block_k)                           */
+  int32_t num_groups;       /* workgroups of the main kernel                    */
+  int32_t num_splits;       /* decode: key-range splits per (batch, KV head)    */
+  int32_t blocks_per_split; /* decode: K/V blocks per split                     */
+  int32_t combine_groups;   /* decode: workgroups of the combine kernel         */
+  uint64_t lds_bytes;       /* LDS per workgroup of the main kernel             */
+  uint64_t workspace_bytes; /* device workspace the call needs                  */
+} sdpa_plan_t;
+
+/* Tile-level loop counts of one attention head for a given tiling, in the
+ * units the page "Xe SDPA Forward Mainloop -- Key Loops + Shapes" uses in its
+ * section "Loop counts for seq_q=512, seq_k=512, head_dim=128": query blocks
+ * of block_q rows, K blocks of block_k keys, QK MMA steps of block_d head-dim
+ * columns and PV MMA steps of block_v value columns per K block.  For causal
+ * problems only the K blocks a query block can see are visited (the planner's
+ * and the kernels' shared loop bound). */
+typedef struct sdpa_loop_counts {
+  int64_t q_blocks;         /* ceil(q_len / block_q)                          */
+  int64_t k_blocks;         /* ceil(kv_len / block_k)                         */
+  int64_t d_loops;          /* ceil(d_qk / block_d) QK steps per K block      */
+  int64_t vv_loops;         /* ceil(d_v / block_v) PV steps per K block       */
+  int64_t blocks_visited;   /* K blocks visited, summed over query blocks     */
+  int64_t blocks_masked;    /* of those, blocks that need the mask (peeled)   */
+  int64_t qk_tiles;         /* blocks_visited * d_loops                       */
+  int64_t pv_tiles;         /* blocks_visited * vv_loops                      */
+  int64_t softmax_tiles;    /* blocks_visited ([block_q, block_k] tiles)      */
+} sdpa_loop_counts_t;
+
+/* Fills *out for one head (all sizes > 0 except q_len/kv_len >= 0).
+ * Host-only. */
+sdpa_status_t sdpa_loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k,
+                               int block_d, int block_v, int causal, sdpa_loop_counts_t* out);
+
+/* ABI version of the loaded library (SDPA_ABI_VERSION it was built with). */
+int sdpa_abi_version(void);
+
+/* Static text for a status code. */
+const char* sdpa_status_string(int status);
+
+/* Detail text of the last failing call on the calling thread ("" if none). */
+const char* sdpa_last_error(void);
+
+/* Validates a problem and fills the plan the entry points would use.
+ * is_decode selects the split-KV decode path (q_len must be 1).  num_cus is
+ * the compute-unit count to plan for (<= 0: 256, the MI355X count).
+ * num_splits (decode only) forces a split count, 0 lets the planner choose.
+ * Host-only: touches no GPU. */
+sdpa_status_t sdpa_plan(const sdpa_problem_t* problem, int is_decode, int num_cus,
+                        int num_splits, sdpa_plan_t* plan);
+
+/* Device workspace bytes sdpa_prefill_fwd needs (0 for every current plan). */
+size_t sdpa_prefill_workspace_bytes(const sdpa_problem_t* problem);
+
+/* Device workspace bytes sdpa_decode_fwd needs for num_splits (0 = the
+ * planner's choice): fp32 partial outputs [batch, head_q, splits, d_v] and
+ * partial (max, sum) pairs [batch, head_q, splits, 2].  Returns 0 for an
+ * invalid problem. */
+size_t sdpa_decode_workspace_bytes(const sdpa_problem_t* problem, int num_splits);
+
+/* Prefill / general forward: one fused kernel.  Streams K/V blocks past each
+ * resident Q tile ("Xe SDPA Forward Mainloop", sections "Outer K-block loop"
+ * and "mainloop_body(K)"): S = Q K^T (MFMA, fp32 accumulate), mask on the
+ * boundary blocks only, online softmax with exp2, P V (MFMA) into an fp32
+ * accumulator, then O = acc / rowsum in the epilogue.
+ *   q, k, v : device inputs in the layouts above, dtype problem->in_dtype
+ *   o       : device output, dtype problem->out_dtype
+ *   lse     : device fp32 [batch, head_q, q_len] or NULL
+ *   workspace, workspace_bytes: may be NULL / 0 while
+ *             sdpa_prefill_workspace_bytes() returns 0
+ *   stream  : hipStream_t or NULL
+ * batch == 0 or q_len == 0 is a successful no-op. */
+sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, const void* k,
+                               const void* v, void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Two-phase split-KV decode ("xe2-sdp-kernels", section "Assets": production
+ * decode, two-phase) for one new token per sequence (q_len == 1).
+ * Phase 1: one workgroup per (batch, KV head, split) streams its key range
+ * once for all head_q/head_kv query heads of the group and writes unnormalised
+ * partial outputs with their running max and sum into the workspace.
+ * Phase 2: one workgroup per (batch, query head) rescales and merges the
+ * splits (the same rescale the online softmax applies between K blocks) and
+ * writes O (and lse).  Both kernels run on `stream`; nothing synchronises.
+ *   q : [batch, head_q, d_qk]; k, v : [batch, kv_len, head_kv, d_qk|d_v]
+ *   o : [batch, head_q, d_v]; lse : [batch, head_q] fp32 or NULL
+ *   num_splits : 0 = planner's choice, otherwise the split count to use
+ *   workspace  : >= sdpa_decode_workspace_bytes(problem, num_splits) bytes,
+ *                16-byte aligned; its contents on entry are ignored. */
+sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, const void* k,
+                              const void* v, void* o, float* lse, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

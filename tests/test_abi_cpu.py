@@ -1,0 +1,161 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+symbol include/sdpa.h declares, validates arguments, and its planner reproduces
+the loop counts printed on the pages and plans the workloads sensibly."""
+import json
+import os
+import re
+
+import pytest
+
+import attention_flash_sdpa_amd as sdpa
+from attention_flash_sdpa_amd import binding, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "sdpa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sdpa.load()
+    declared = _header_functions()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(binding.EXPORTS)
+    assert lib.sdpa_abi_version() == 1
+
+
+def test_status_strings():
+    lib = sdpa.load()
+    for code in range(8):
+        assert lib.sdpa_status_string(code).startswith(b"SDPA_")
+    assert b"unknown" in lib.sdpa_status_string(99)
+
+
+def test_page_loop_counts_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sagev1_loop_counts.json")))
+    p, t, e = g["problem"], g["tile"], g["expected"]
+    c = sdpa.loop_counts(q_len=p["q_len"], kv_len=p["kv_len"], d_qk=p["d_qk"], d_v=p["d_v"], block_q=t["block_q"],
+                         block_k=t["block_k"], block_d=t["block_d"], block_v=t["block_v"], causal=p["causal"])
+    assert c.q_blocks == e["q_blocks"]
+    assert c.k_blocks == e["k_blocks"]
+    assert c.d_loops == e["d_loops_per_k_block"]
+    assert c.vv_loops == e["vv_loops_per_k_block"]
+    assert c.blocks_visited // c.q_blocks == e["per_q_block"]["k_blocks"]
+    assert c.qk_tiles // c.q_blocks == e["per_q_block"]["qk_tiles"]
+    assert c.pv_tiles // c.q_blocks == e["per_q_block"]["pv_tiles"]
+    assert c.softmax_tiles // c.q_blocks == e["per_q_block"]["softmax_tiles"]
+    assert c.qk_tiles == e["per_head"]["qk_tiles"]
+    assert c.pv_tiles == e["per_head"]["pv_tiles"]
+    assert c.softmax_tiles == e["per_head"]["softmax_tiles"]
+    assert c.blocks_masked == 0
+
+
+def _brute_blocks(q_len, kv_len, bq, bk, causal):
+    """Blocks visited / masked by brute force over every (row, key) pair."""
+    visited = masked = 0
+    for r0 in range(0, q_len, bq):
+        rows = range(r0, min(r0 + bq, q_len))
+        for kb in range(0, kv_len, bk):
+            keys = range(kb, min(kb + bk, kv_len))
+            vis = [[(not causal) or (j <= i + kv_len - q_len) for j in keys] for i in rows]
+            n_vis = sum(map(sum, vis))
+            if n_vis:
+                visited += 1
+                if n_vis != len(rows) * bk:
+                    masked += 1
+            elif causal:
+                # a causal row block sees a prefix of keys; nothing visible
+                # in this block means nothing visible in later blocks either
+                break
+    return visited, masked
+
+
+@pytest.mark.parametrize("q_len,kv_len,causal", [(512, 1024, True), (1001, 1023, False), (7, 5, True),
+                                                   (5, 7, True), (33, 64, True), (64, 64, True), (1, 8192, False),
+                                                   (130, 2, True), (3, 0, False), (0, 5, True)])
+@pytest.mark.parametrize("bq,bk", [(32, 64), (128, 64), (256, 64)])
+def test_loop_counts_match_brute_force(q_len, kv_len, causal, bq, bk):
+    c = sdpa.loop_counts(q_len=q_len, kv_len=kv_len, d_qk=128, d_v=128, block_q=bq, block_k=bk, block_d=16,
+                         block_v=32, causal=causal)
+    v, m = _brute_blocks(q_len, kv_len, bq, bk, causal)
+    assert (c.blocks_visited, c.blocks_masked) == (v, m)
+
+
+def _problem(w: inputs.Workload, **over):
+    code = {"f16": sdpa.F16, "bf16": sdpa.BF16, "fp8_e4m3": sdpa.FP8_E4M3}
+    d = dict(batch=w.batch, q_len=w.q_len, kv_len=w.kv_len, head_q=w.head_q, head_kv=w.head_kv, d_qk=w.d_qk,
+             d_v=w.d_v, in_dtype=code[w.dtype], out_dtype=code[w.out_dtype], causal=w.causal, scale=w.scale)
+    d.update(over)
+    return sdpa.make_problem(**d)
+
+
+def test_plans_for_workloads():
+    W = inputs.WORKLOADS
+    p = sdpa.plan(_problem(W["gqa_causal_prefill_bf16"]))
+    assert (p.heads_per_group, p.block_q, p.block_k, p.q_tiles, p.kv_blocks) == (4, 32, 64, 16, 16)
+    assert p.num_groups == 8 * 16 and p.workspace_bytes == 0 and p.lds_bytes == 65536
+    p = sdpa.plan(_problem(W["unaligned_full_bf16"]))
+    assert (p.heads_per_group, p.qtiles_per_group, p.q_tiles) == (1, 4, 8)
+    assert p.num_groups == 2 * 4 * 7 * 8
+    p = sdpa.plan(_problem(W["tiny_causal_bf16"]))
+    assert (p.heads_per_group, p.q_tiles, p.num_groups) == (4, 1, 2 * 4 * 2)
+    d = sdpa.plan(_problem(W["splitkv_decode_bf16"]), decode=True, num_cus=256)
+    assert (d.num_splits, d.blocks_per_split, d.block_k) == (16, 16, 32)
+    assert d.num_groups * d.waves_per_group == 16 * 8 * 16
+    assert d.combine_groups == 16 * 32
+    assert d.workspace_bytes == 16 * 32 * 16 * 128 * 4 + 16 * 32 * 16 * 2 * 4
+
+
+def test_decode_split_choices():
+    w = inputs.WORKLOADS["splitkv_decode_bf16"]
+    for kv_len, cus in ((1, 256), (31, 256), (64, 256), (100000, 256), (8192, 80)):
+        d = sdpa.plan(_problem(w, kv_len=kv_len), decode=True, num_cus=cus)
+        blocks = -(-kv_len // 32)
+        assert d.num_splits >= 1 and d.blocks_per_split >= 1
+        assert d.num_splits * d.blocks_per_split >= blocks                 # covers every key
+        assert (d.num_splits - 1) * d.blocks_per_split < blocks            # no empty split
+    forced = sdpa.plan(_problem(w, kv_len=100), decode=True, num_splits=9)
+    assert forced.num_splits == 9 and forced.blocks_per_split == 1      # 4 blocks: 5 empty splits allowed
+
+
+@pytest.mark.parametrize("over,decode,code", [
+    (dict(head_q=30), False, 2), (dict(q_len=-1), False, 2), (dict(scale=-1.0), False, 3),
+    (dict(scale=float("inf")), False, 3), (dict(scale=float("nan")), False, 3), (dict(d_qk=96, d_v=96), False, 4),
+    (dict(d_qk=128, d_v=64), False, 4), (dict(out_dtype=sdpa.F16), False, 4), (dict(descale=(1.0, -2.0, 1.0)), False, 3),
+    (dict(q_len=2), True, 2), (dict(head_q=8 * 17), True, 4), (dict(in_dtype=sdpa.FP8_E4M3), True, 4),
+])
+def test_validation_errors(over, decode, code):
+    base = inputs.WORKLOADS["splitkv_decode_bf16" if decode else "gqa_causal_prefill_bf16"]
+    with pytest.raises(sdpa.SdpaError) as ei:
+        sdpa.plan(_problem(base, **over), decode=decode)
+    assert ei.value.status == code
+    assert sdpa.load().sdpa_last_error() != b""
+
+
+def test_null_and_workspace_errors_before_any_launch():
+    """These return before touching the GPU, so they run on the CPU."""
+    import ctypes
+
+    lib = sdpa.load()
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    pr = _problem(w)
+    null = ctypes.c_void_p(0)
+    assert lib.sdpa_prefill_fwd(None, null, null, null, null, null, null, 0, null) == 1
+    assert lib.sdpa_prefill_fwd(ctypes.byref(pr), null, null, null, null, null, null, 0, null) == 1
+    mis = ctypes.c_void_p(0x1008)
+    assert lib.sdpa_prefill_fwd(ctypes.byref(pr), mis, mis, mis, mis, null, null, 0, null) == 5
+    dw = inputs.WORKLOADS["splitkv_decode_bf16"]
+    dp = _problem(dw)
+    a = ctypes.c_void_p(0x1000)
+    need = lib.sdpa_decode_workspace_bytes(ctypes.byref(dp), 0)
+    assert need > 0
+    assert lib.sdpa_decode_fwd(ctypes.byref(dp), a, a, a, a, null, 0, a, need - 16, null) == 6
+    assert lib.sdpa_decode_fwd(ctypes.byref(dp), a, a, a, a, null, 0, null, need, null) in (5, 6)
+    # empty problems are successful no-ops with no pointer checks
+    empty = _problem(w, q_len=0)
+    assert lib.sdpa_prefill_fwd(ctypes.byref(empty), null, null, null, null, null, null, 0, null) == 0
