@@ -6,15 +6,16 @@
 // "Xe SDPA Forward Mainloop" (section "Outer K-block loop"), and the merge is
 // the online-softmax rescale of its "softmax() helper" applied across splits.
 //
-// Phase 1 (decode_split_kernel): one wavefront per (batch, KV head, split).
-// The G = head_q / head_kv query heads of the group are the MFMA N dimension
-// (16x16x32 MFMA, G <= 16), so every K/V byte is read from HBM exactly once
-// for all heads of the group.  K fragments go straight from HBM into
-// registers (they already have the A-operand layout: one key row per lane, 16
-// contiguous bytes); V blocks go HBM -> LDS with direct loads and come back
-// transposed with ds_read_b64_tr_b16.  Both are prefetched one 32-key block
-// ahead, ping-ponging between two register sets and two LDS stages.  The wave
-// writes its unnormalised partial output and its (max, sum) pair.
+// Phase 1 (decode_split_kernel): one wavefront per (batch, KV head, split);
+// a workgroup holds 4 adjacent KV heads of one split so that its loads of a
+// key are contiguous.  The G = head_q / head_kv query heads of the group are
+// the MFMA N dimension (16x16x32 MFMA, G <= 16), so every K/V byte is read
+// from HBM exactly once for all heads of the group.  K and V blocks of 32
+// keys go HBM -> LDS with direct 16-byte loads (whole key rows per 16 lanes),
+// one block ahead, into two wave-private stages; K fragments come back with
+// ds_read_b128 and V^T fragments with ds_read_b64_tr_b16, both swizzled to
+// avoid bank conflicts.  The wave writes its unnormalised partial output and
+// its (max, sum) pair.
 //
 // Phase 2 (decode_combine_kernel): one wavefront per (batch, query head)
 // merges the splits: M = max_s m_s, w_s = 2^(m_s - M), O = sum w_s O_s /
@@ -29,27 +30,29 @@ namespace sdpa {
 template <class T, int D, int DV>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   constexpr int BK = kDecodeBlockK;           // 32 keys per block (two 16-key tiles)
-  constexpr int VROW = DV * 2;
-  constexpr int VCPR = DV / 8;
-  constexpr int VBYTES = BK * VROW;           // one V stage
-  constexpr int V_INSTR = VBYTES / 1024;      // 1 KiB direct loads per block
+  constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
+  constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte slots per row
+  constexpr int KBYTES = BK * KROW, VBYTES = BK * VROW;
+  constexpr int STAGE = KBYTES + VBYTES;      // one K/V block of one wave
+  constexpr int K_INSTR = KBYTES / 1024, V_INSTR = VBYTES / 1024;  // 1 KiB direct loads
   constexpr int KS = D / 32;                  // k-steps of the QK MFMA
   constexpr int NT = DV / 16;                 // O^T accumulator tiles
-  constexpr int K_LOADS = 2 * KS;             // 16-byte K loads per lane per block
-  static_assert(VCPR >= 8, "swizzle needs >= 8 slots per row");
-  static_assert(V_INSTR * 1024 == VBYTES, "V block must be whole 1 KiB pieces");
+  static_assert(K_INSTR * 1024 == KBYTES && V_INSTR * 1024 == VBYTES, "whole 1 KiB pieces");
 
-  __shared__ __attribute__((aligned(1024))) char smem[kDecodeWaves * 2 * VBYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[kDecodeWaves * 2 * STAGE];
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t lds_w = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem + wave * 2 * VBYTES;
+  const uint32_t lds_w = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem + wave * 2 * STAGE;
 
+  // workgroup = (batch, split, group of 4 adjacent KV heads); wave = KV head,
+  // so the workgroup's loads of one key cover 4 consecutive head rows
   const int S = a.num_splits;
-  const int wid = blockIdx.x * kDecodeWaves + wave;
-  if (wid >= a.batch * a.head_kv * S) return;  // no barriers in this kernel
-  const int split = wid % S;
-  const int g = (wid / S) % a.head_kv;
-  const int b = wid / (S * a.head_kv);
+  const int hgroups = (a.head_kv + kDecodeWaves - 1) / kDecodeWaves;
+  const int hgi = blockIdx.x % hgroups;
+  const int split = (blockIdx.x / hgroups) % S;
+  const int b = blockIdx.x / (hgroups * S);
+  const int g = hgi * kDecodeWaves + wave;
+  if (g >= a.head_kv) return;  // no barriers in this kernel
   const int G = a.group;
   const int Sk = a.kv_len;
   const int k_begin = min(split * a.blocks_per_split * BK, Sk);
@@ -72,49 +75,53 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     }
   }
 
-  const size_t row_k = (size_t)a.head_kv * D;   // elements between keys
-  const size_t row_v = (size_t)a.head_kv * DV;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * Sk * a.head_kv + g) * D + 8 * gq;
-  const char* vbase = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * (DV * 2);
-  const int last_key = Sk - 1;
-
-  // K fragment loads for block kb: lane reads key (tile*16 + n16), dims
-  // 32s + 8*gq .. +7 (the A-operand layout of 16x16x32).
-  auto load_k = [&](int kb, u32x4_t (&kf)[K_LOADS]) {
+  // direct global -> LDS fill of one block: instruction i covers rows
+  // [i*1024/ROW, ...), lane p the 16-byte slot p % CPR of its row, which holds
+  // chunk slot ^ swizzle(row) -- so 16 (or 8) lanes read one whole key row
+  const char* kbase = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * KROW;
+  const char* vbase = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * VROW;
+  const size_t kstride = (size_t)a.head_kv * KROW, vstride = (size_t)a.head_kv * VROW;
+  int krow[K_INSTR], kcol[K_INSTR], vrow[V_INSTR], vcol[V_INSTR];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key = min(kb + 16 * t + n16, last_key);
-      const uint16_t* kp = kbase + (size_t)key * row_k;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[t * KS + s] = *(const u32x4_t*)(kp + 32 * s);
-    }
-  };
-  // V block kb into LDS stage: rows of DV values, 16-byte slots swizzled.
-  int vrow[V_INSTR], vcol[V_INSTR];
+  for (int i = 0; i < K_INSTR; ++i) {
+    const int slot = i * 64 + lane, r = slot / KCPR;
+    krow[i] = r;
+    kcol[i] = ((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16;
+  }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
-    const int slot = i * 64 + lane;
-    const int r = slot / VCPR;
+    const int slot = i * 64 + lane, r = slot / VCPR;
     vrow[i] = r;
-    vcol[i] = ((slot % VCPR) ^ (int)swz(r)) * 16;
+    vcol[i] = ((slot % VCPR) ^ (int)swz_decode<VCPR>(r)) * 16;
   }
-  auto load_v = [&](int kb, int stage) {
+  const int last_key = Sk - 1;
+  auto issue_fill = [&](int key0, int stage) {
+    const uint32_t kl = lds_w + stage * STAGE, vl = kl + KBYTES;
 #pragma unroll
-    for (int i = 0; i < V_INSTR; ++i) {
-      const int key = min(kb + vrow[i], last_key);
-      global_to_lds_16(vbase + (size_t)key * row_v * 2 + vcol[i], lds_w + stage * VBYTES + i * 1024);
-    }
+    for (int i = 0; i < K_INSTR; ++i)
+      global_to_lds_16(kbase + (size_t)min(key0 + krow[i], last_key) * kstride + kcol[i], kl + i * 1024);
+#pragma unroll
+    for (int i = 0; i < V_INSTR; ++i)
+      global_to_lds_16(vbase + (size_t)min(key0 + vrow[i], last_key) * vstride + vcol[i], vl + i * 1024);
   };
-  // transposed V^T fragment offsets: lane (gq, s = l%16) addresses key row
-  // 4*gq + s/4 (+16 for the second half) at value columns 16t + 4*(s%4)
-  uint32_t voff[NT];
+
+  // K fragment (A operand of 16x16x32): key row 16t + l%16, slot 4s + l/16
+  uint32_t koff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = n16 * KROW + (((4 * s + gq) ^ (int)swz_prefill<KCPR>(n16)) << 4);
+  // V^T fragment offsets for ds_read_b64_tr_b16: lane (gq, s = l%16) addresses
+  // key row 4*gq + s/4 (+16 for the second half) at value columns 16t + 4*(s%4)
+  uint32_t voff[2][NT];
   {
     const int s = lane & 15;
-    const int r = 4 * gq + (s >> 2);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = 16 * t + 4 * (s & 3);
-      voff[t] = r * VROW + (((col >> 3) ^ (int)swz(r)) << 4) + ((col & 7) << 1);
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = 16 * hf + 4 * gq + (s >> 2);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int col = 16 * t + 4 * (s & 3);
+        voff[hf][t] = r * VROW + (((col >> 3) ^ (int)swz_decode<VCPR>(r)) << 4) + ((col & 7) << 1);
+      }
     }
   }
 
@@ -124,13 +131,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float s2 = a.s2;
 
-  auto block = [&](int kb, int stage, const u32x4_t (&kf)[K_LOADS], bool prefetched, bool masked) {
+  auto block = [&](int key0, int stage, bool masked) {
+    const uint32_t ks = lds_w + stage * STAGE, vs = ks + KBYTES;
     f32x4_t sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sc[t] = mfma16x16x32<T>(kf[t * KS + s], qf[s], sc[t]);
+      for (int s = 0; s < KS; ++s) sc[t] = mfma16x16x32<T>(lds_read_b128(ks + koff[s] + 16 * t * KROW), qf[s], sc[t]);
     }
     // scores in the log2 domain; keys past the split end are masked (only in
     // the split's last block)
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = sc[t][r] * s2;
-        if (masked) v = (kb + 16 * t + 4 * gq + r < k_end) ? v : -INFINITY;
+        if (masked) v = (key0 + 16 * t + 4 * gq + r < k_end) ? v : -INFINITY;
         x[4 * t + r] = v;
         bmax = fmaxf(bmax, v);
       }
@@ -151,58 +159,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     const float m_sub = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_sub);
     m_run = m_new;
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(x[i] - m_sub);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
     // P^T as the B operand: k = 8*gq + j takes tile 0 register j (j < 4) and
     // tile 1 register j-4 (j >= 4)
     u32x4_t pf;
-    pf.x = pack2<T>(p[0], p[1]);
-    pf.y = pack2<T>(p[2], p[3]);
-    pf.z = pack2<T>(p[4], p[5]);
-    pf.w = pack2<T>(p[6], p[7]);
+    pf.x = pack2<T>(fast_exp2(x[0] - m_sub), fast_exp2(x[1] - m_sub));
+    pf.y = pack2<T>(fast_exp2(x[2] - m_sub), fast_exp2(x[3] - m_sub));
+    pf.z = pack2<T>(fast_exp2(x[4] - m_sub), fast_exp2(x[5] - m_sub));
+    pf.w = pack2<T>(fast_exp2(x[6] - m_sub), fast_exp2(x[7] - m_sub));
+    float psum = add_pair<T>(pf.x, 0.f);
+    psum = add_pair<T>(pf.y, psum);
+    psum = add_pair<T>(pf.z, psum);
+    psum = add_pair<T>(pf.w, psum);
+    l_run = l_run * alpha + psum;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-    if (prefetched)
-      wait_vmcnt<K_LOADS + V_INSTR>();
-    else
-      wait_vmcnt<0>();
-    const uint32_t vs = lds_w + stage * VBYTES;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x2_t lo = lds_read_tr16(vs + voff[t]);
-      const u32x2_t hi = lds_read_tr16(vs + voff[t] + 16 * VROW);
+      const u32x2_t lo = lds_read_tr16(vs + voff[0][t]);
+      const u32x2_t hi = lds_read_tr16(vs + voff[1][t]);
       const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
       acc[t] = mfma16x16x32<T>(vf, pf, acc[t]);
     }
   };
 
+  // K/V pipeline: block i+1 is in flight while block i computes.  All loads
+  // are direct-to-LDS and invisible to the compiler's wait counting, so every
+  // wait below is explicit; the buffers are private to the wave (no barrier).
   if (nb > 0) {
-    u32x4_t ka[K_LOADS], kb2[K_LOADS];
-    load_k(k_begin, ka);
-    load_v(k_begin, 0);
-    for (int i = 0; i < nb; i += 2) {
-      const int key0 = k_begin + i * BK;
-      const bool has1 = i + 1 < nb;
-      if (has1) {
-        load_k(key0 + BK, kb2);
-        load_v(key0 + BK, 1);
-      }
-      block(key0, 0, ka, has1, !has1);
-      if (has1) {
-        const bool has2 = i + 2 < nb;
-        if (has2) {
-          load_k(key0 + 2 * BK, ka);
-          load_v(key0 + 2 * BK, 0);
-        }
-        block(key0 + BK, 1, kb2, has2, !has2);
-      }
+    issue_fill(k_begin, 0);
+    int i = 0;
+    for (; i < nb - 1; ++i) {
+      issue_fill(k_begin + (i + 1) * BK, (i + 1) & 1);
+      wait_vmcnt<K_INSTR + V_INSTR>();
+      block(k_begin + i * BK, i & 1, false);
     }
+    wait_vmcnt<0>();
+    block(k_begin + i * BK, i & 1, true);  // last block: keys past k_end masked
   }
 
   // partial results: unnormalised O^T (lane holds head n16, values 16t + 4*gq + r)
@@ -226,21 +218,53 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   const int lane = threadIdx.x;
   const int S = a.num_splits;
   const float* ml = a.part_ml + (size_t)bh * S * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-  const float m_sub = M == -INFINITY ? 0.f : M;
-  float den = 0.f;
+  const float* po = a.part_o + (size_t)bh * S * DV;
   constexpr int PER = DV / 64;
+
+  // pass 1: global max over splits (lane s covers splits s, s+64, ...)
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, xor_lane(M, d));
+  const float m_sub = M == -INFINITY ? 0.f : M;
+
+  // pass 2: chunks of 64 splits; each lane owns one split's weight, the
+  // weighted partial outputs are summed with all loads of a chunk in flight
+  float den = 0.f;
   float num[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) num[j] = 0.f;
-  const float* po = a.part_o + (size_t)bh * S * DV;
-  for (int s = 0; s < S; ++s) {
-    const float w = fast_exp2(ml[2 * s] - m_sub);  // 0 for an empty split
-    den += w * ml[2 * s + 1];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < S) {
+      w = fast_exp2(ml[2 * s] - m_sub);  // 0 for an empty split (m = -inf)
+      den += w * ml[2 * s + 1];
+    }
+    const int n = min(64, S - s0);
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+      float vals[8][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) num[j] += w * po[(size_t)s * DV + lane + 64 * j];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) vals[u][j] = po[(size_t)(s0 + i + u) * DV + lane + 64 * j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i + u));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) num[j] = fmaf(wu, vals[u][j], num[j]);
+      }
+    }
+    for (; i < n; ++i) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+#pragma unroll
+      for (int j = 0; j < PER; ++j) num[j] = fmaf(wu, po[(size_t)(s0 + i) * DV + lane + 64 * j], num[j]);
+    }
   }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) den += xor_lane(den, d);
+
   const float inv = den > 0.f ? a.v_descale / den : 0.f;
   uint16_t* o = (uint16_t*)a.o + (size_t)bh * DV;
 #pragma unroll

@@ -20,8 +20,9 @@
 //    the MFMA accumulators and its rescale by 2^(m_old - m_new) is lane-local.
 //  * K/V blocks of 64 keys go global -> LDS with direct 16-byte-per-lane loads
 //    (no register staging), double buffered, into rows whose 16-byte slots
-//    are XOR-swizzled so that K fragment reads (ds_read_b128) and transposed
-//    V fragment reads (ds_read_b64_tr_b16) are free of bank conflicts.
+//    are XOR-swizzled (swz_prefill) so that K fragment reads (ds_read_b128)
+//    and transposed V fragment reads (ds_read_b64_tr_b16) are free of bank
+//    conflicts.
 //  * The K loop is split on the host-computable block count into a branch-free
 //    unmasked part and a peeled masked tail ("xe2-sdp-kernels", section
 //    "Inner-loop rules"): only the tail blocks evaluate the causal/remainder
@@ -35,6 +36,10 @@
 #include "sdpa_internal.h"
 
 namespace sdpa {
+
+// Largest growth (log2 units) of a row max tolerated before O and l are
+// rescaled: probabilities then stay <= 2^8, far inside fp16/bf16 range.
+constexpr float kSlack = 8.0f;
 
 // Spreads consecutive logical workgroup ids over one XCD: hardware dispatches
 // workgroup i to XCD i % 8, so logical ids [x*n/8, (x+1)*n/8) (which share
@@ -129,14 +134,14 @@ void prefill_kernel(const PrefillArgs a) {
     const int slot = (wave * K_INSTR + i) * 64 + lane;
     const int r = slot / KCPR;
     krow[i] = r;
-    kcol[i] = (((slot % KCPR) ^ (int)swz(r)) * 16);
+    kcol[i] = (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int slot = (wave * V_INSTR + i) * 64 + lane;
     const int r = slot / VCPR;
     vrow[i] = r;
-    vcol[i] = (((slot % VCPR) ^ (int)swz(r)) * 16);
+    vcol[i] = (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
   }
   const int last_key = Sk - 1;
   auto issue_fill = [&](int kb, int stage) {
@@ -159,18 +164,23 @@ void prefill_kernel(const PrefillArgs a) {
   // head-dim slot 2*s + l/32.
   uint32_t koff[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) koff[s] = l32 * KROW + ((((2 * s + hl)) ^ (int)swz(l32)) << 4);
+  for (int s = 0; s < D / 16; ++s) koff[s] = l32 * KROW + ((((2 * s + hl)) ^ (int)swz_prefill<KCPR>(l32)) << 4);
   // V^T fragment (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16: lane
   // (group gq = l/16, s = l%16) addresses key row 4*(gq/2) + s/4 (+8 for the
   // second half, +16 per key chunk) at value columns 32t + 16*(gq%2) + 4*(s%4).
-  uint32_t voff[NT];
+  // (the swizzle of rows r and r + 8 differs, so both halves get offsets;
+  // +16 rows per key chunk leaves it unchanged)
+  uint32_t voff[2][NT];
   {
     const int gq = lane >> 4, s = lane & 15;
-    const int r = 4 * (gq >> 1) + (s >> 2);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = 32 * t + 16 * (gq & 1) + 4 * (s & 3);
-      voff[t] = r * VROW + ((((col >> 3) ^ (int)swz(r))) << 4) + ((col & 7) << 1);
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = 8 * hf + 4 * (gq >> 1) + (s >> 2);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int col = 32 * t + 16 * (gq & 1) + 4 * (s & 3);
+        voff[hf][t] = r * VROW + ((((col >> 3) ^ (int)swz_prefill<VCPR>(r))) << 4) + ((col & 7) << 1);
+      }
     }
   }
 
@@ -207,15 +217,15 @@ void prefill_kernel(const PrefillArgs a) {
     // mask (tail blocks only) + block row max in the log2 domain
     float bmax;
     if constexpr (MASKED) {
-      const int key0 = kb * BK + 4 * hl;
-      const int lim = CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1;  // last visible key
+      // register r of tile t holds key kb*BK + 4*hl + 32t + 8(r/4) + r%4; it is
+      // visible iff that key <= the row's last visible key
+      const int lim = (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl);
       bmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * t + 8 * (r >> 2) + (r & 3);
-          const float x = key <= lim ? sc[t][r] * s2 : -INFINITY;
+          const float x = (32 * t + 8 * (r >> 2) + (r & 3)) <= lim ? sc[t][r] * s2 : -INFINITY;
           sc[t][r] = x;
           bmax = fmaxf(bmax, x);
         }
@@ -228,15 +238,26 @@ void prefill_kernel(const PrefillArgs a) {
       bmax = mx * s2;
     }
     bmax = pair_max(bmax);
+    // Lazy rescale: the running max only moves (and O, l are rescaled by
+    // 2^(m_old - m_new)) when some row's block max exceeds it by more than
+    // kSlack; otherwise the stale max is kept, so P <= 2^kSlack.  The final
+    // O / l is unchanged because l accumulates the same P values.
     const float m_new = fmaxf(m_run, bmax);
-    // rows that have seen no visible key keep m = -inf; subtract 0 instead so
-    // that no (-inf) - (-inf) appears (only possible in masked blocks)
-    const float m_sub = MASKED ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
-    const float alpha = fast_exp2(m_run - m_sub);
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kSlack)) {
+      // rows that have seen no visible key keep m = -inf (masked blocks only)
+      const float m_tgt = MASKED ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
+      const float alpha = fast_exp2(m_run - m_tgt);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_sub = MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
 
-    // P = 2^(s2*S - m), row sum, and packing into the PV B operand
-    float psum = 0.f;
+    // P = 2^(s2*S - m), packed to 16 bits as the PV B operand; the row sum is
+    // taken over the packed values
     u32x4_t pf[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -250,22 +271,18 @@ void prefill_kernel(const PrefillArgs a) {
           p0 = fast_exp2(fmaf(sc[t][r], s2, -m_sub));
           p1 = fast_exp2(fmaf(sc[t][r + 1], s2, -m_sub));
         }
-        psum += p0 + p1;
-        pf[2 * t + (r >> 3)][(r & 7) >> 1] = pack2<T>(p0, p1);
+        const uint32_t pk = pack2<T>(p0, p1);
+        pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
+        l_run = add_pair<T>(pk, l_run);
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
 
     // GEMM 2: O^T[dv][query] += V^T P^T, 16 keys per MFMA
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x2_t lo = lds_read_tr16(vs + voff[t] + (16 * c) * VROW);
-        const u32x2_t hi = lds_read_tr16(vs + voff[t] + (16 * c + 8) * VROW);
+        const u32x2_t lo = lds_read_tr16(vs + voff[0][t] + (16 * c) * VROW);
+        const u32x2_t hi = lds_read_tr16(vs + voff[1][t] + (16 * c) * VROW);
         const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
         acc[t] = mfma32x32x16<T>(vf, pf[c], acc[t]);
       }
@@ -294,10 +311,9 @@ void prefill_kernel(const PrefillArgs a) {
   }
   wait_vmcnt<0>();
   __syncthreads();
-  if (kb < n_full)
-    block(kb, kb & 1, Unmasked{});
-  else
-    block(kb, kb & 1, Masked{});
+  // the last block (peeled): masked unless every key of it is visible to
+  // every row, in which case the mask is a no-op
+  block(kb, kb & 1, Masked{});
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------
   const float l_tot = pair_sum(l_run);

@@ -63,15 +63,31 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Packs two fp32 values into one dword of 16-bit elements, round to nearest even.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Packs two fp32 values into one dword of 16-bit elements, round to nearest
+// even (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
 template <class T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  if constexpr (T::is_bf16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// acc + lo + hi of a packed pair of 16-bit values (one v_dot2 with ones), so
+// row sums use exactly the rounded probabilities the MFMA consumes.
+template <class T>
+__device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
   if constexpr (T::is_bf16) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), ones, acc, false);
   } else {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), ones, acc, false);
   }
 }
 
@@ -107,9 +123,13 @@ __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t byte_addr) {
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land
-// at lds_base + 16*i (lds_base is wavefront-uniform).
+// at lds_base + 16*i (lds_base is wavefront-uniform and goes through M0).
+// Written as inline assembly so that the compiler's wait-count insertion does
+// not see an LDS write here and force a full drain (vmcnt(0)) before every
+// later LDS read; completion is tracked explicitly with wait_vmcnt<N>() and a
+// workgroup barrier before the data is read.
 __device__ __forceinline__ void global_to_lds_16(const void* gptr, uint32_t lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)gptr, (SDPA_LDS void*)(uintptr_t)lds_base, 16, 0, 0);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
 // Waits until at most n vector-memory operations of this wave are in flight.
@@ -120,11 +140,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// LDS swizzle of 16-byte slots within a row: slot' = slot ^ swz(row) with
-// swz(row) = rotate-left of the low three row bits.  Eight consecutive rows
-// read at the same slot (K fragments) hit eight distinct slots, and four
-// consecutive rows read at two adjacent slots (transposed V fragments) hit
-// eight distinct slots, so neither access pattern has a bank conflict.
-__device__ __forceinline__ uint32_t swz(uint32_t row) { return ((row & 3u) << 1) | ((row >> 2) & 1u); }
+// LDS swizzles of the 16-byte slots within a K/V row: the slot holding
+// chunk c of row r is c ^ f(r).  The LDS serves 16 lanes x 16 bytes (64 banks
+// of 4 bytes) per cycle, so a read is conflict-free when the 16 lanes of each
+// quarter-wave hit 16 distinct 16-byte positions of a 256-byte bank line.
+//
+// Prefill (SLOTS = row bytes / 16 = 16 or 8):
+//  * K fragments (ds_read_b128): 16 consecutive rows at one chunk;
+//  * V^T fragments (ds_read_b64_tr_b16): 4 consecutive rows x 4 chunks per
+//    half-wave.
+// With 16-byte slots per 256-byte row, f swaps the two 2-bit fields of r%16;
+// with 8 slots (two rows per bank line) f applies the 3-bit analogue to r/2.
+// Both patterns then touch 16 distinct positions (checked on the CPU).
+template <int SLOTS>
+__host__ __device__ __forceinline__ uint32_t swz_prefill(uint32_t r) {
+  static_assert(SLOTS == 16 || SLOTS == 8, "row of 128 or 256 bytes");
+  if constexpr (SLOTS == 16) return ((r & 3u) << 2) | ((r >> 2) & 3u);
+  const uint32_t x = r >> 1;
+  return ((x & 1u) << 2) | ((x >> 1) & 3u);
+}
+
+// Decode V^T fragments (16x16x32 MFMA, ds_read_b64_tr_b16): each half-wave
+// reads 8 consecutive rows x 2 adjacent chunks.
+template <int SLOTS>
+__host__ __device__ __forceinline__ uint32_t swz_decode(uint32_t r) {
+  static_assert(SLOTS == 16 || SLOTS == 8, "row of 128 or 256 bytes");
+  if constexpr (SLOTS == 16) return (r & 7u) << 1;
+  return ((r >> 1) & 3u) << 1;
+}
 
 }  // namespace sdpa

@@ -20,6 +20,13 @@ pytestmark = pytest.mark.gpu
 TOL16 = 2e-2
 
 
+def _lse_tol(dtype):
+    """The row sum l is taken over the probabilities after rounding to the MFMA
+    operand type, so |d lse| <= |d l| / l <= one half-ulp of that type
+    (2^-9 bf16, 2^-12 fp16); twice that bound plus fp32 slack is allowed."""
+    return 4e-3 if dtype == torch.bfloat16 else 1e-3
+
+
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -59,7 +66,7 @@ def _prefill_case(dev, oracle_mod, q, k, v, *, causal, scale, tol=TOL16, rows=No
             want = ref["lse"]
             assert np.array_equal(np.isneginf(got), np.isneginf(want))
             fin = np.isfinite(want)
-            assert np.abs(got[fin] - want[fin]).max(initial=0) <= 1e-3
+            assert np.abs(got[fin] - want[fin]).max(initial=0) <= _lse_tol(q.dtype)
     else:
         r = torch.as_tensor(rows)
         sel = out.cpu()[r[:, 0], r[:, 1], r[:, 2]]
@@ -68,7 +75,7 @@ def _prefill_case(dev, oracle_mod, q, k, v, *, causal, scale, tol=TOL16, rows=No
             got = lse.cpu()[r[:, 0], r[:, 2], r[:, 1]].double().numpy()
             fin = np.isfinite(ref["lse"])
             assert np.array_equal(np.isneginf(got), np.isneginf(ref["lse"]))
-            assert np.abs(got[fin] - ref["lse"][fin]).max(initial=0) <= 1e-3
+            assert np.abs(got[fin] - ref["lse"][fin]).max(initial=0) <= _lse_tol(q.dtype)
     return out
 
 
@@ -158,10 +165,11 @@ def test_prefill_special_values(dev, oracle_mod):
     v = torch.randn(B, Sk, Hkv, D, generator=g).to(torch.bfloat16)
     # scale = 0: uniform average of the visible values
     _prefill_case(dev, oracle_mod, q, k, v, causal=True, scale=0.0, what="scale=0")
-    # constant V rows give that constant exactly (bf16-representable 0.75)
+    # constant V rows give that constant exactly (bf16-representable 0.75):
+    # the row sum is taken over the same rounded probabilities the PV MFMA uses
     vc = torch.full_like(v, 0.75)
     out = _prefill_case(dev, oracle_mod, q, k, vc, causal=True, scale=0.1, what="constant V")
-    assert torch.allclose(out.float().cpu(), torch.full((B, Sq, Hq, D), 0.75), atol=4e-3)
+    assert torch.equal(out.float().cpu(), torch.full((B, Sq, Hq, D), 0.75))
     # large logits: near one-hot rows, no overflow
     _prefill_case(dev, oracle_mod, (q.float() * 8).to(torch.bfloat16), k, v, causal=False, scale=1.0,
                   what="large logits", check_lse=False)
@@ -192,7 +200,7 @@ def _decode_case(dev, oracle_mod, q, k, v, *, scale, num_splits=0, tol=TOL16, wh
     want = ref["lse"][:, :, 0]
     assert np.array_equal(np.isneginf(got), np.isneginf(want))
     fin = np.isfinite(want)
-    assert np.abs(got[fin] - want[fin]).max(initial=0) <= 1e-3
+    assert np.abs(got[fin] - want[fin]).max(initial=0) <= _lse_tol(q.dtype)
     return out
 
 
