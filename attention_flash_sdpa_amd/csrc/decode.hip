@@ -214,26 +214,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 
 template <class T, int DV>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
-  const int bh = blockIdx.x;  // b * head_q + h
+  constexpr int PER = DV / 64;   // value columns per lane (contiguous)
+  constexpr int CH = 16;         // splits whose partials are loaded together
+  typedef float vec_t __attribute__((ext_vector_type(PER)));
+  const int bh = blockIdx.x;     // b * head_q + h
   const int lane = threadIdx.x;
   const int S = a.num_splits;
   const float* ml = a.part_ml + (size_t)bh * S * 2;
-  const float* po = a.part_o + (size_t)bh * S * DV;
-  constexpr int PER = DV / 64;
+  const float* po = a.part_o + (size_t)bh * S * DV + PER * lane;
 
-  // pass 1: global max over splits (lane s covers splits s, s+64, ...)
+  // global max over splits (lane s covers splits s, s+64, ...)
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, xor_lane(M, d));
   const float m_sub = M == -INFINITY ? 0.f : M;
 
-  // pass 2: chunks of 64 splits; each lane owns one split's weight, the
-  // weighted partial outputs are summed with all loads of a chunk in flight
+  // weighted sums: one split weight per lane, CH partial rows loaded at once
   float den = 0.f;
-  float num[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) num[j] = 0.f;
+  vec_t num = (vec_t)0.f;
   for (int s0 = 0; s0 < S; s0 += 64) {
     const int s = s0 + lane;
     float w = 0.f;
@@ -242,35 +241,27 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
       den += w * ml[2 * s + 1];
     }
     const int n = min(64, S - s0);
-    int i = 0;
-    for (; i + 8 <= n; i += 8) {
-      float vals[8][PER];
+    for (int c0 = 0; c0 < n; c0 += CH) {
+      vec_t vals[CH];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < CH; ++u)
+        vals[u] = c0 + u < n ? *(const vec_t*)(po + (size_t)(s0 + c0 + u) * DV) : (vec_t)0.f;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) vals[u][j] = po[(size_t)(s0 + i + u) * DV + lane + 64 * j];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i + u));
-#pragma unroll
-        for (int j = 0; j < PER; ++j) num[j] = fmaf(wu, vals[u][j], num[j]);
+      for (int u = 0; u < CH; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(c0 + u, 63)));
+        num += (c0 + u < n ? wu : 0.f) * vals[u];
       }
-    }
-    for (; i < n; ++i) {
-      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
-#pragma unroll
-      for (int j = 0; j < PER; ++j) num[j] = fmaf(wu, po[(size_t)(s0 + i) * DV + lane + 64 * j], num[j]);
     }
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) den += xor_lane(den, d);
 
   const float inv = den > 0.f ? a.v_descale / den : 0.f;
-  uint16_t* o = (uint16_t*)a.o + (size_t)bh * DV;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const uint32_t w = pack2<T>(num[j] * inv, 0.f);
-    o[lane + 64 * j] = (uint16_t)(w & 0xffff);
+  uint16_t* o = (uint16_t*)a.o + (size_t)bh * DV + PER * lane;
+  if constexpr (PER == 2) {
+    *(uint32_t*)o = pack2<T>(num[0] * inv, num[1] * inv);
+  } else {
+    o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
   }
   if (a.lse != nullptr && lane == 0) a.lse[bh] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
 }

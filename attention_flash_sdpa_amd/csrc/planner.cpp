@@ -93,7 +93,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
 
   if (!is_decode) {
     const int kid = prefill_kernel_id(p);
-    if (kid < 0 || kid == kPrefillFp8D192) {
+    if (kid < 0) {
       set_error("unsupported prefill (in_dtype=%d, out_dtype=%d, d_qk=%d, d_v=%d)", p.in_dtype, p.out_dtype,
                 p.d_qk, p.d_v);
       return SDPA_ERR_UNSUPPORTED;

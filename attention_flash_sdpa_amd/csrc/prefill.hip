@@ -37,19 +37,6 @@
 
 namespace sdpa {
 
-// Largest growth (log2 units) of a row max tolerated before O and l are
-// rescaled: probabilities then stay <= 2^8, far inside fp16/bf16 range.
-constexpr float kSlack = 8.0f;
-
-// Spreads consecutive logical workgroup ids over one XCD: hardware dispatches
-// workgroup i to XCD i % 8, so logical ids [x*n/8, (x+1)*n/8) (which share
-// K/V heads) are served by XCD x and its L2.
-__device__ __forceinline__ int remap_xcd(int i, int n) {
-  const int per = n >> 3, rem = n & 7;
-  const int x = i & 7, j = i >> 3;
-  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
-}
-
 template <class T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const PrefillArgs a) {
@@ -351,6 +338,7 @@ int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ih
     case kPrefillBf16D64: return launch_one<Bf16, 64>(a, causal, stream);
     case kPrefillF16D128: return launch_one<F16, 128>(a, causal, stream);
     case kPrefillBf16D128: return launch_one<Bf16, 128>(a, causal, stream);
+    case kPrefillFp8D192: return launch_prefill_fp8(a, causal, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -28,11 +28,29 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
 
 #define SDPA_LDS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Largest growth (log2 units) of a row max tolerated before O and l are
+// rescaled: probabilities then stay <= 2^8, far inside fp16/bf16 range.
+constexpr float kSlack = 8.0f;
+
+// Spreads consecutive logical workgroup ids over one XCD: hardware dispatches
+// workgroup i to XCD i % 8, so logical ids [x*n/8, (x+1)*n/8) (which share
+// K/V heads) are served by XCD x and its L2.
+__device__ __forceinline__ int remap_xcd(int i, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = i & 7, j = i >> 3;
+  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
 
 // Element-type tags of the 16-bit inputs.
 struct Bf16 {
@@ -63,9 +81,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Packs two fp32 values into one dword of 16-bit elements, round to nearest
 // even (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
@@ -93,6 +108,19 @@ __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 32x32x64 MFMA on OCP fp8 e4m3 operands (32 bytes per lane), unit block
+// scales (E8M0 exponent 127 = 2^0).
+__device__ __forceinline__ f32x16_t mfma32x32x64_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four e4m3 bytes (one dword) widened exactly to four bf16 values (two dwords).
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap(a, b) swaps
 // the upper half of a with the lower half of b, so with a = b = x the returned
 // pair is (own, partner) in lanes 0-31 and (partner, own) in lanes 32-63: the
@@ -115,6 +143,14 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
 // Transposed 8-byte LDS read (see the layout note at the top of the file).
 __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t byte_addr) {
   s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SDPA_LDS s16x4_t*)(uintptr_t)byte_addr);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Transposed 8-byte LDS read of 8-bit elements: within each 16-lane group,
+// lane i receives byte r (r = 0..7) of the 8-byte row addressed by group lane
+// 2r + i/8, at position i%8 -- an 8x16 -> 16x8 byte transpose.
+__device__ __forceinline__ u32x2_t lds_read_tr8(uint32_t byte_addr) {
+  i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SDPA_LDS i32x2_t*)(uintptr_t)byte_addr);
   return __builtin_bit_cast(u32x2_t, v);
 }
 
@@ -159,6 +195,10 @@ __host__ __device__ __forceinline__ uint32_t swz_prefill(uint32_t r) {
   const uint32_t x = r >> 1;
   return ((x & 1u) << 2) | ((x >> 1) & 3u);
 }
+
+// 64-byte rows (4 slots, four rows per bank line), read as 16 consecutive rows
+// at one chunk: f = (r / 4) % 4 spreads them over the 16 positions.
+__host__ __device__ __forceinline__ uint32_t swz_quarter(uint32_t r) { return (r >> 2) & 3u; }
 
 // Decode V^T fragments (16x16x32 MFMA, ds_read_b64_tr_b16): each half-wave
 // reads 8 consecutive rows x 2 adjacent chunks.

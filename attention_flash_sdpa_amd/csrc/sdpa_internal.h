@@ -69,6 +69,7 @@ struct DecodeArgs {
 };
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 }  // namespace sdpa
