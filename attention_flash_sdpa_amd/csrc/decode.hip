@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     vcol[i] = ((slot % VCPR) ^ (int)swz_decode<VCPR>(r)) * 16;
   }
   const int last_key = Sk - 1;
-  auto issue_fill = [&](int key0, int stage) {
+  auto issue_fill = [&](int key0, int stage) __attribute__((always_inline)) {
     const uint32_t kl = lds_w + stage * STAGE, vl = kl + KBYTES;
 #pragma unroll
     for (int i = 0; i < K_INSTR; ++i)
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float s2 = a.s2;
 
-  auto block = [&](int key0, int stage, bool masked) {
+  auto block = [&](int key0, int stage, bool masked) __attribute__((always_inline)) {
     const uint32_t ks = lds_w + stage * STAGE, vs = ks + KBYTES;
     f32x4_t sc[2];
 #pragma unroll

@@ -3,9 +3,9 @@
 // Structure follows "Xe SDPA Forward Mainloop -- Key Loops + Shapes"
 // (sections "Startup prefetch + init", "mainloop_body(K)", "softmax()
 // helper", "Outer K-block loop"): a resident Q tile, K/V blocks streamed
-// through a two-stage prefetch pipeline, S = Q K^T on the matrix cores, mask,
-// online softmax with exp2 and a log2(e)-folded scale, and P V accumulated in
-// fp32.  The MI355X mapping:
+// through a prefetch pipeline, S = Q K^T on the matrix cores, mask, online
+// softmax with exp2 and a log2(e)-folded scale, and P V accumulated in fp32.
+// The MI355X mapping:
 //
 //  * One workgroup = 4 wavefronts that all read the same K/V blocks: either
 //    up to 4 query heads of one GQA group on the same 32 query rows, or
@@ -14,19 +14,24 @@
 //    comment "S = K * Q" uses), so lane l and lane l^32 together hold all the
 //    scores of query row l%32.  Row max / row sum are in-lane reductions plus
 //    one permlane32 swap; the running max, sum and rescale factor stay in
-//    scalar registers of that lane.
+//    registers of that lane.
 //  * The probabilities are packed to 16 bits in place and used directly as the
 //    B operand of O^T = V^T P^T, so P never leaves registers; O^T stays in
 //    the MFMA accumulators and its rescale by 2^(m_old - m_new) is lane-local.
+//  * Software pipeline: iteration j issues the QK MFMAs of block j+1 before
+//    the softmax of block j, so the exp/VALU work of one block overlaps the
+//    matrix-core work of the next, then runs the PV MFMAs of block j.  K and V
+//    therefore have separate double buffers: K(j+2) and V(j+1) are loaded
+//    during iteration j, each with a whole iteration to arrive.
 //  * K/V blocks of 64 keys go global -> LDS with direct 16-byte-per-lane loads
-//    (no register staging), double buffered, into rows whose 16-byte slots
-//    are XOR-swizzled (swz_prefill) so that K fragment reads (ds_read_b128)
-//    and transposed V fragment reads (ds_read_b64_tr_b16) are free of bank
-//    conflicts.
-//  * The K loop is split on the host-computable block count into a branch-free
-//    unmasked part and a peeled masked tail ("xe2-sdp-kernels", section
-//    "Inner-loop rules"): only the tail blocks evaluate the causal/remainder
-//    predicate.
+//    (no register staging, scalar base address + per-lane offset) into rows
+//    whose 16-byte slots are swizzled (swz_prefill) so that K fragment reads
+//    (ds_read_b128) and transposed V fragment reads (ds_read_b64_tr_b16) are
+//    free of bank conflicts.  Buffer parity is a compile-time parameter, so
+//    every LDS read uses an immediate offset.
+//  * The K loop is split on the block counts into a branch-free unmasked part
+//    and a peeled masked tail ("xe2-sdp-kernels", section "Inner-loop
+//    rules"): only the tail blocks evaluate the causal/remainder predicate.
 #include <math.h>
 
 #include <type_traits>
@@ -45,14 +50,15 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
   constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte slots per row
   constexpr int KBYTES = BK * KROW, VBYTES = BK * VROW;
-  constexpr int STAGE = KBYTES + VBYTES;
   constexpr int K_INSTR = BK * KCPR / 64 / NW;  // 1 KiB direct loads per wave per block
   constexpr int V_INSTR = BK * VCPR / 64 / NW;
   constexpr int NT = DV / 32;                   // O^T accumulator tiles
-  static_assert(KCPR >= 8 && VCPR >= 8, "swizzle needs >= 8 slots per row");
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "block too small for the fill");
+  // LDS: K buffers 0/1, then V buffers 0/1
+  constexpr uint32_t KBUF0 = 0, KBUF1 = KBYTES;
+  constexpr uint32_t VBUF0 = 2 * KBYTES, VBUF1 = 2 * KBYTES + VBYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem;
 
   const int lane = __lane_id();
@@ -110,39 +116,58 @@ void prefill_kernel(const PrefillArgs a) {
     }
   }
 
-  // ---- per-lane fill addresses (direct global -> LDS) ---------------------
+  // ---- direct global -> LDS fills ------------------------------------------
+  // Instruction i of this wave covers the 64 16-byte slots starting at slot
+  // (wave*INSTR + i)*64; lane p holds slot P: row P / CPR, position P % CPR,
+  // which receives chunk (P % CPR) ^ swizzle(row) of that key row.
   const char* kg = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * (D * 2);
   const char* vg = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * (DV * 2);
-  const int kstride = a.head_kv * D * 2;   // bytes between consecutive keys
+  const int kstride = a.head_kv * D * 2;  // bytes between consecutive keys
   const int vstride = a.head_kv * DV * 2;
-  int krow[K_INSTR], kcol[K_INSTR], vrow[V_INSTR], vcol[V_INSTR];
+  uint32_t kfo[K_INSTR], vfo[V_INSTR];    // byte offsets within a whole block
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
-    const int slot = (wave * K_INSTR + i) * 64 + lane;
-    const int r = slot / KCPR;
-    krow[i] = r;
-    kcol[i] = (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
+    const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
+    kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
-    const int slot = (wave * V_INSTR + i) * 64 + lane;
-    const int r = slot / VCPR;
-    vrow[i] = r;
-    vcol[i] = (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
+    const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
+    vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
   }
   const int last_key = Sk - 1;
-  auto issue_fill = [&](int kb, int stage) {
-    const uint32_t kl = lds0 + stage * STAGE + wave * K_INSTR * 1024;
-    const uint32_t vl = lds0 + stage * STAGE + KBYTES + wave * V_INSTR * 1024;
+  // A block is whole if all its BK keys exist; in the last block of a ragged
+  // key range the rows past the end re-read the last key (they are masked).
+  auto fill_k = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
+    const uint32_t l = lds0 + buf + wave * K_INSTR * 1024;
+    if ((kb + 1) * BK <= Sk) {
+      const char* base = kg + (size_t)kb * BK * kstride;
 #pragma unroll
-    for (int i = 0; i < K_INSTR; ++i) {
-      const int key = min(kb * BK + krow[i], last_key);
-      global_to_lds_16(kg + (size_t)key * kstride + kcol[i], kl + i * 1024);
+      for (int i = 0; i < K_INSTR; ++i) global_to_lds_16_sbase(base, kfo[i], l + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K_INSTR; ++i) {
+        const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
+        const int key = min(kb * BK + r, last_key);
+        global_to_lds_16(kg + (size_t)key * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16),
+                         l + i * 1024);
+      }
     }
+  };
+  auto fill_v = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
+    const uint32_t l = lds0 + buf + wave * V_INSTR * 1024;
+    if ((kb + 1) * BK <= Sk) {
+      const char* base = vg + (size_t)kb * BK * vstride;
 #pragma unroll
-    for (int i = 0; i < V_INSTR; ++i) {
-      const int key = min(kb * BK + vrow[i], last_key);
-      global_to_lds_16(vg + (size_t)key * vstride + vcol[i], vl + i * 1024);
+      for (int i = 0; i < V_INSTR; ++i) global_to_lds_16_sbase(base, vfo[i], l + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V_INSTR; ++i) {
+        const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
+        const int key = min(kb * BK + r, last_key);
+        global_to_lds_16(vg + (size_t)key * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16),
+                         l + i * 1024);
+      }
     }
   };
 
@@ -151,12 +176,13 @@ void prefill_kernel(const PrefillArgs a) {
   // head-dim slot 2*s + l/32.
   uint32_t koff[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) koff[s] = l32 * KROW + ((((2 * s + hl)) ^ (int)swz_prefill<KCPR>(l32)) << 4);
+  for (int s = 0; s < D / 16; ++s)
+    koff[s] = lds0 + l32 * KROW + ((((2 * s + hl)) ^ (int)swz_prefill<KCPR>(l32)) << 4);
   // V^T fragment (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16: lane
   // (group gq = l/16, s = l%16) addresses key row 4*(gq/2) + s/4 (+8 for the
-  // second half, +16 per key chunk) at value columns 32t + 16*(gq%2) + 4*(s%4).
-  // (the swizzle of rows r and r + 8 differs, so both halves get offsets;
-  // +16 rows per key chunk leaves it unchanged)
+  // second half, +16 per key chunk) at value columns 32t + 16*(gq%2) +
+  // 4*(s%4).  The swizzle of rows r and r + 8 differs, so both halves get
+  // offsets; +16 rows per key chunk leaves it unchanged.
   uint32_t voff[2][NT];
   {
     const int gq = lane >> 4, s = lane & 15;
@@ -166,7 +192,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int col = 32 * t + 16 * (gq & 1) + 4 * (s & 3);
-        voff[hf][t] = r * VROW + ((((col >> 3) ^ (int)swz_prefill<VCPR>(r))) << 4) + ((col & 7) << 1);
+        voff[hf][t] = lds0 + r * VROW + ((((col >> 3) ^ (int)swz_prefill<VCPR>(r))) << 4) + ((col & 7) << 1);
       }
     }
   }
@@ -180,14 +206,11 @@ void prefill_kernel(const PrefillArgs a) {
   float m_run = -INFINITY;  // running max of s2*S for query l%32 (log2 domain)
   float l_run = 0.f;        // this lane's share of the running sum
   const float s2 = a.s2;
+  f32x16_t sa[2], sb[2];    // score tiles of two consecutive blocks
 
-  auto block = [&](int kb, int stage, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const uint32_t ks = lds0 + stage * STAGE;
-    const uint32_t vs = ks + KBYTES;
-
-    // GEMM 1: S^T[key][query] over the head dimension
-    f32x16_t sc[2];
+  // GEMM 1: S^T[key][query] of the block in K buffer KB
+  auto qk = [&](auto kb_tag, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
+    constexpr uint32_t KB = decltype(kb_tag)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sc[0][r] = 0.f;
@@ -195,13 +218,17 @@ void prefill_kernel(const PrefillArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const u32x4_t k0 = lds_read_b128(ks + koff[s]);
-      const u32x4_t k1 = lds_read_b128(ks + koff[s] + 32 * KROW);
+      const u32x4_t k0 = lds_read_b128(koff[s] + KB);
+      const u32x4_t k1 = lds_read_b128(koff[s] + KB + 32 * KROW);
       sc[0] = mfma32x32x16<T>(k0, qf[s], sc[0]);
       sc[1] = mfma32x32x16<T>(k1, qf[s], sc[1]);
     }
+  };
 
-    // mask (tail blocks only) + block row max in the log2 domain
+  // Softmax part 1: mask (tail blocks only), block row max, lazy rescale.
+  // Returns the subtrahend m of P = 2^(s2*S - m).
+  auto softmax_max = [&](int kb, f32x16_t (&sc)[2], auto masked_tag) __attribute__((always_inline)) -> float {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     float bmax;
     if constexpr (MASKED) {
       // register r of tile t holds key kb*BK + 4*hl + 32t + 8(r/4) + r%4; it is
@@ -241,11 +268,13 @@ void prefill_kernel(const PrefillArgs a) {
         for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
       m_run = m_new;
     }
-    const float m_sub = MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+    return MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+  };
 
-    // P = 2^(s2*S - m), packed to 16 bits as the PV B operand; the row sum is
-    // taken over the packed values
-    u32x4_t pf[4];
+  // Softmax part 2: P = 2^(s2*S - m) packed to 16 bits as the PV B operand;
+  // the row sum is taken over the packed values.
+  auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -262,45 +291,110 @@ void prefill_kernel(const PrefillArgs a) {
         pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
         l_run = add_pair<T>(pk, l_run);
       }
+  };
 
-    // GEMM 2: O^T[dv][query] += V^T P^T, 16 keys per MFMA
+  // GEMM 2: O^T[dv][query] += V^T P^T from V buffer VB, 16 keys per MFMA
+  auto pv = [&](auto vb_tag, const u32x4_t (&pf)[4]) __attribute__((always_inline)) {
+    constexpr uint32_t VB = decltype(vb_tag)::value;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x2_t lo = lds_read_tr16(vs + voff[0][t] + (16 * c) * VROW);
-        const u32x2_t hi = lds_read_tr16(vs + voff[1][t] + (16 * c) * VROW);
+        const u32x2_t lo = lds_read_tr16(voff[0][t] + VB + (16 * c) * VROW);
+        const u32x2_t hi = lds_read_tr16(voff[1][t] + VB + (16 * c) * VROW);
         const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
         acc[t] = mfma32x32x16<T>(vf, pf[c], acc[t]);
       }
   };
 
-  using Unmasked = std::false_type;
-  using Masked = std::true_type;
+  // One pipeline iteration j (PAR = j & 1): the scores of block j are in
+  // registers, K(j+1) sits in K buffer 1-PAR and V(j) in V buffer PAR.  It
+  // starts the loads of V(j+1) and K(j+2) into the buffers freed by the
+  // previous iteration, computes the scores of block j+1, then the softmax
+  // and P V of block j.
+  auto iteration = [&](int j, auto masked_tag, auto next_tag, auto par_tag) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr uint32_t KB_NEXT = PAR ? KBUF0 : KBUF1;   // holds K(j+1)
+    constexpr uint32_t KB_FREE = PAR ? KBUF1 : KBUF0;   // receives K(j+2)
+    constexpr uint32_t VB_CUR = PAR ? VBUF1 : VBUF0;    // holds V(j)
+    constexpr uint32_t VB_FREE = PAR ? VBUF0 : VBUF1;   // receives V(j+1)
+    f32x16_t(&s_cur)[2] = PAR ? sb : sa;
+    f32x16_t(&s_nxt)[2] = PAR ? sa : sb;
+    if constexpr (NEXT) {
+      fill_v(j + 1, VB_FREE);
+      if (j + 2 < n_blocks) {
+        fill_k(j + 2, KB_FREE);
+        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) have landed
+      } else {
+        wait_vmcnt<V_INSTR>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const float m_sub = softmax_max(j, s_cur, masked_tag);
+    u32x4_t pf[4];
+    // Phase fence, then the QK MFMAs of block j+1 interleaved with the
+    // exponentials of block j: after each K fragment read and MFMA the wave
+    // issues a few independent VALU instructions, which execute while the
+    // matrix core works on that MFMA.
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) qk(std::integral_constant<uint32_t, KB_NEXT>{}, s_nxt);
+    softmax_exp(s_cur, m_sub, pf, masked_tag);
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) __syncthreads();  // this iteration's buffers are refilled next
+  };
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  // Iterations [j0, j1) of one flavour, unrolled by two so that the score
+  // tiles visibly alternate (block j in sa for even j, in sb for odd j).
+  auto run = [&](int j0, int j1, auto masked_tag, auto next_tag) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) iteration(j++, masked_tag, next_tag, Par1{});
+    for (; j + 1 < j1; j += 2) {
+      iteration(j, masked_tag, next_tag, Par0{});
+      iteration(j + 1, masked_tag, next_tag, Par1{});
+    }
+    if (j < j1) iteration(j, masked_tag, next_tag, Par0{});
+  };
 
   // ---- K-block pipeline ---------------------------------------------------
-  issue_fill(0, 0);
-  int kb = 0;
-  const int n_pref = n_blocks - 1;  // blocks that have a successor to prefetch
-  for (; kb < min(n_full, n_pref); ++kb) {
-    issue_fill(kb + 1, (kb + 1) & 1);
-    wait_vmcnt<K_INSTR + V_INSTR>();
-    __syncthreads();
-    block(kb, kb & 1, Unmasked{});
-    __syncthreads();
+  using Unmasked = std::false_type;
+  using Masked = std::true_type;
+  using Next = std::true_type;
+  using Last = std::false_type;
+  fill_k(0, KBUF0);
+  fill_v(0, VBUF0);
+  if (n_blocks > 1) {
+    fill_k(1, KBUF1);
+    wait_vmcnt<K_INSTR + V_INSTR>();  // K(0) has landed
+  } else {
+    wait_vmcnt<V_INSTR>();
   }
-  for (; kb < n_pref; ++kb) {
-    issue_fill(kb + 1, (kb + 1) & 1);
-    wait_vmcnt<K_INSTR + V_INSTR>();
-    __syncthreads();
-    block(kb, kb & 1, Masked{});
-    __syncthreads();
-  }
-  wait_vmcnt<0>();
   __syncthreads();
+  qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
+  __syncthreads();  // K buffer 0 is refilled by the first iteration
+  const int n_next = n_blocks - 1;  // iterations that have a next block
+  const int j_mask = min(n_full, n_next);
+  run(0, j_mask, Unmasked{}, Next{});
+  run(j_mask, n_next, Masked{}, Next{});
   // the last block (peeled): masked unless every key of it is visible to
   // every row, in which case the mask is a no-op
-  block(kb, kb & 1, Masked{});
+  if (n_next & 1)
+    iteration(n_next, Masked{}, Last{}, Par1{});
+  else
+    iteration(n_next, Masked{}, Last{}, Par0{});
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------
   const float l_tot = pair_sum(l_run);

@@ -127,7 +127,7 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     v_col[i] = ((slot % 8) ^ (int)swz_prefill<8>(r)) * 16;
   }
   const int last_key = Sk - 1;
-  auto issue_fill = [&](int kb, int stage) {
+  auto issue_fill = [&](int kb, int stage) __attribute__((always_inline)) {
     const uint32_t base = lds0 + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < KA_INSTR; ++i)
@@ -180,7 +180,7 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   float l_run = 0.f;
   const float s2 = a.s2;
 
-  auto block = [&](int kb, int stage, auto masked_tag) {
+  auto block = [&](int kb, int stage, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const uint32_t base = lds0 + stage * STAGE;
 

@@ -164,8 +164,24 @@ __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t byte_addr) {
 // not see an LDS write here and force a full drain (vmcnt(0)) before every
 // later LDS read; completion is tracked explicitly with wait_vmcnt<N>() and a
 // workgroup barrier before the data is read.
+//
+// Hazards: the compiler does not see inside the asm, so the wait states the
+// load needs after its inputs are written are inserted here -- one after an
+// SALU write of M0 (s_nop 0), five after a VALU write (v_readfirstlane) of
+// the SGPR base used by the scalar-base form below (s_nop 4).
 __device__ __forceinline__ void global_to_lds_16(const void* gptr, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+
+// As global_to_lds_16 with a wavefront-uniform 64-bit base in SGPRs and a
+// per-lane 32-bit byte offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void global_to_lds_16_sbase(const void* sbase, uint32_t voffset, uint32_t lds_base) {
+  // the base is uniform by construction; readfirstlane makes that explicit
+  // for the compiler so the operand lands in SGPRs
+  const uint64_t p = (uint64_t)(uintptr_t)sbase;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(u), "{m0}"(lds_base) : "memory");
 }
 
 // Waits until at most n vector-memory operations of this wave are in flight.

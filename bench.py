@@ -157,16 +157,20 @@ def main():
 
     # ---------------- other prefill workloads (context lines) ----------------
     extra = {}
-    for name in ("unaligned_full_bf16",):
+    for name in ("single_head_f16_128", "unaligned_full_bf16", "tiny_causal_bf16", "mla_fp8_causal_prefill"):
         xw = inputs.WORKLOADS[name]
-        xq, xk, xv, _ = inputs.make_qkv(xw)
+        xq, xk, xv, xds = inputs.make_qkv(xw)
         xq, xk, xv = (t.to(dev) for t in (xq, xk, xv))
-        xo = torch.empty(xw.batch, xw.q_len, xw.head_q, xw.d_v, dtype=xq.dtype, device=dev)
-        xms = _time(lambda i: sdpa.prefill(xq, xk, xv, scale=xw.scale, causal=xw.causal, out=xo),
-                    max(args.steps // 4, 1), args.warmup, stream)
+        odt = torch.bfloat16 if xw.out_dtype == "bf16" else torch.float16
+        xo = torch.empty(xw.batch, xw.q_len, xw.head_q, xw.d_v, dtype=odt, device=dev)
+        n = 100 if xw.flops() < 1e9 else max(args.steps // 4, 1)
+        xms = _time(lambda i: sdpa.prefill(xq, xk, xv, scale=xw.scale, causal=xw.causal, out=xo, descale=xds),
+                    n, args.warmup, stream)
         xt = xw.flops() / (xms * 1e-3) / 1e12
-        extra[name] = {"value": round(xt, 3), "unit": "TFLOP/s", "ms_per_call": round(xms, 6),
-                       "frac_of_peak": round(xt / PEAK_BF16_TFLOPS, 5)}
+        peak = PEAK_FP8_TFLOPS if xw.dtype == "fp8_e4m3" else PEAK_BF16_TFLOPS
+        extra[name] = {"value": round(xt, 3), "unit": "TFLOP/s", "ms_per_call": round(xms, 6), "steps": n,
+                       "algorithmic_gflop": round(xw.flops() / 1e9, 4), "peak": peak,
+                       "frac_of_peak": round(xt / peak, 5)}
         del xq, xk, xv, xo
     # launch floor: a one-element device op timed the same way
     one = torch.zeros(1, device=dev)
