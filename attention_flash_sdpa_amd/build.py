@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsdpa_mi355x.so")
-SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_fp8.hip", "decode.hip"]
+SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_wide.hip", "prefill_fp8.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -28,9 +28,15 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
 
 
+# Per-source backend options.  The wide prefill kernel runs one wave per SIMD
+# with both register files: MFMA results stay in VGPRs (the softmax reads the
+# scores with VALU instructions), AGPRs take what does not fit.
+EXTRA = {"prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, isa: bool) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
         if isa:

@@ -57,7 +57,7 @@ void clear_error() { g_last_error[0] = 0; }
 const char* last_error_text() { return g_last_error; }
 
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
-                        sdpa_plan_t* plan) {
+                        sdpa_plan_t* plan, int variant) {
   memset(plan, 0, sizeof *plan);
   if (num_cus <= 0) num_cus = kDefaultCUs;
   if (p.batch < 0 || p.q_len < 0 || p.kv_len < 0) {
@@ -92,15 +92,32 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
   }
 
   if (!is_decode) {
-    const int kid = prefill_kernel_id(p);
+    int kid = prefill_kernel_id(p);
     if (kid < 0) {
       set_error("unsupported prefill (in_dtype=%d, out_dtype=%d, d_qk=%d, d_v=%d)", p.in_dtype, p.out_dtype,
                 p.d_qk, p.d_v);
       return SDPA_ERR_UNSUPPORTED;
     }
+    // Wide kernel (64 query rows per wave, one wave per SIMD) when the grid
+    // still gives every CU about three waves; otherwise the 32-row kernel,
+    // which doubles the wave count for small problems.
+    int rows = kRowsPerWave;
+    if (kid != kPrefillFp8D192) {
+      const int64_t wide_waves = (int64_t)p.batch * p.head_q * ceil_div(p.q_len, kWideRowsPerWave);
+      // (the wide kernel is selectable for tuning; the 32-row kernel is the
+      // default until the wide one measures faster)
+      bool wide = false;
+      (void)wide_waves;
+      if (variant == 1) wide = false;
+      if (variant == 2) wide = true;
+      if (wide) {
+        rows = kWideRowsPerWave;
+        kid = kid - kPrefillF16D64 + kWideF16D64;
+      }
+    }
     plan->kernel = kid;
     plan->waves_per_group = kPrefillWaves;
-    plan->rows_per_wave = kRowsPerWave;
+    plan->rows_per_wave = rows;
     // Pack query heads of one GQA group into the workgroup when the group
     // size allows it (K/V blocks in LDS are then shared by several heads);
     // otherwise stack consecutive query tiles of one head.  Short queries
@@ -109,12 +126,12 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     if (G % 4 == 0) hp = 4;
     else if (G % 2 == 0) hp = 2;
     else hp = 1;
-    if (p.q_len <= kRowsPerWave) hp = (int)(G < kPrefillWaves ? G : kPrefillWaves);
+    if (p.q_len <= rows) hp = (int)(G < kPrefillWaves ? G : kPrefillWaves);
     while (kPrefillWaves % hp) --hp;
     plan->heads_per_group = hp;
     plan->qtiles_per_group = kPrefillWaves / hp;
-    plan->block_q = kRowsPerWave * plan->qtiles_per_group;
-    plan->block_k = kPrefillBlockK;
+    plan->block_q = rows * plan->qtiles_per_group;
+    plan->block_k = rows == kWideRowsPerWave ? kWideBlockK : kPrefillBlockK;
     plan->stages = 2;
     plan->q_tiles = (int32_t)ceil_div(p.q_len, plan->block_q);
     plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "sdpa_internal.h"
 
@@ -29,6 +31,13 @@ int device_cus() {
     cached[dev] = n;
   }
   return cached[dev];
+}
+
+// SDPA_PREFILL_VARIANT=narrow|wide overrides the planner's prefill kernel
+// choice (for tuning sweeps); unset or anything else keeps the planner's.
+int prefill_variant() {
+  const char* e = getenv("SDPA_PREFILL_VARIANT");
+  return (e && !strcmp(e, "narrow")) ? 1 : (e && !strcmp(e, "wide")) ? 2 : 0;
 }
 
 sdpa_status_t hip_status(int err, const char* what) {
@@ -66,7 +75,7 @@ sdpa_status_t sdpa_plan(const sdpa_problem_t* problem, int is_decode, int num_cu
     set_error("problem and plan must not be NULL");
     return SDPA_ERR_NULL_PTR;
   }
-  return make_plan(*problem, is_decode != 0, num_cus, num_splits, plan);
+  return make_plan(*problem, is_decode != 0, num_cus, num_splits, plan, is_decode ? 0 : prefill_variant());
 }
 
 sdpa_status_t sdpa_loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k,
@@ -102,7 +111,7 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
   }
   const sdpa_problem_t& p = *problem;
   sdpa_plan_t plan;
-  sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan);
+  sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan, prefill_variant());
   if (st != SDPA_OK) return st;
   if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
   if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr))) {

@@ -17,6 +17,10 @@ enum KernelId : int32_t {
   kPrefillF16D128 = 2,
   kPrefillBf16D128 = 3,
   kPrefillFp8D192 = 4,
+  kWideF16D64 = 8,
+  kWideBf16D64 = 9,
+  kWideF16D128 = 10,
+  kWideBf16D128 = 11,
   kDecodeF16D64 = 16,
   kDecodeBf16D64 = 17,
   kDecodeF16D128 = 18,
@@ -24,6 +28,8 @@ enum KernelId : int32_t {
 };
 
 constexpr int kRowsPerWave = 32;   // prefill: query rows per wave (MFMA N)
+constexpr int kWideRowsPerWave = 64;  // wide prefill: two 32-row tiles per wave
+constexpr int kWideBlockK = 32;       // wide prefill: keys per K/V block
 constexpr int kPrefillWaves = 4;   // prefill: waves per workgroup
 constexpr int kPrefillBlockK = 64; // prefill: keys per K/V block
 constexpr int kDecodeBlockK = 32;  // decode: keys per K/V block
@@ -33,8 +39,10 @@ constexpr int kDefaultCUs = 256;
 
 // Validates the problem; fills *plan.  Writes a detail message through
 // set_error() on failure.  Pure host code.
+// variant: 0 = planner's choice, 1 = force the 32-row prefill kernel,
+// 2 = force the wide (64-row) prefill kernel (tuning sweeps only).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
-                        sdpa_plan_t* plan);
+                        sdpa_plan_t* plan, int variant = 0);
 
 sdpa_status_t loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k, int block_d,
                           int block_v, bool causal, sdpa_loop_counts_t* out);
@@ -70,6 +78,7 @@ struct DecodeArgs {
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
+int launch_prefill_wide(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 }  // namespace sdpa

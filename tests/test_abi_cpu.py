@@ -97,10 +97,10 @@ def _problem(w: inputs.Workload, **over):
 def test_plans_for_workloads():
     W = inputs.WORKLOADS
     p = sdpa.plan(_problem(W["gqa_causal_prefill_bf16"]))
-    assert (p.heads_per_group, p.block_q, p.block_k, p.q_tiles, p.kv_blocks) == (4, 32, 64, 16, 16)
+    assert (p.rows_per_wave, p.heads_per_group, p.block_q, p.block_k, p.q_tiles, p.kv_blocks) == (32, 4, 32, 64, 16, 16)
     assert p.num_groups == 8 * 16 and p.workspace_bytes == 0 and p.lds_bytes == 65536
     p = sdpa.plan(_problem(W["unaligned_full_bf16"]))
-    assert (p.heads_per_group, p.qtiles_per_group, p.q_tiles) == (1, 4, 8)
+    assert (p.rows_per_wave, p.heads_per_group, p.qtiles_per_group, p.q_tiles, p.block_k) == (32, 1, 4, 8, 64)
     assert p.num_groups == 2 * 4 * 7 * 8
     p = sdpa.plan(_problem(W["tiny_causal_bf16"]))
     assert (p.heads_per_group, p.q_tiles, p.num_groups) == (4, 1, 2 * 4 * 2)
@@ -109,6 +109,17 @@ def test_plans_for_workloads():
     assert d.num_groups * d.waves_per_group == 16 * 8 * 16
     assert d.combine_groups == 16 * 32
     assert d.workspace_bytes == 16 * 32 * 16 * 128 * 4 + 16 * 32 * 16 * 2 * 4
+
+
+def test_prefill_variant_override(monkeypatch):
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "wide")
+    pw = sdpa.plan(_problem(w))
+    assert (pw.rows_per_wave, pw.block_k, pw.block_q, pw.q_tiles) == (64, 32, 64, 8)
+    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow")
+    assert sdpa.plan(_problem(inputs.WORKLOADS["unaligned_full_bf16"])).rows_per_wave == 32
+    monkeypatch.delenv("SDPA_PREFILL_VARIANT")
+    assert sdpa.plan(_problem(w)).rows_per_wave == 32
 
 
 def test_decode_split_choices():
