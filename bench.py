@@ -1,6 +1,9 @@
 """Benchmark of the fused SDPA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --counters-pass              # short run for rocprofv3 --pmc
+    python bench.py --summarize-trace DIR        # kernel-trace CSV -> profiles/
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR
 
 One step = one call of the hot path on its workload:
   * headline: causal GQA bf16 prefill (batch 1, 32 query / 8 KV heads,
@@ -10,9 +13,14 @@ One step = one call of the hot path on its workload:
     head dim 128, bf16), K/V rotated over 4 buffer sets between calls so the
     cache cannot serve them -- achieved HBM GB/s over algorithmic bytes
     (Q + K + V read once, O written once).
-Inputs are resident in HBM before the timed region.  Each timed region is
-W untimed calls, synchronize, K back-to-back calls bracketed by HIP events on
-the stream the kernels run on, synchronize.  Rank 0 prints ONE JSON line.
+Inputs are resident in HBM before the timed region.  The calls go through the
+Python binding and the C ABI; a chunk of C = gcd(K, W) consecutive calls is
+captured once into a HIP graph (the library allocates and synchronizes
+nothing, so its launches capture as they are).  W/C untimed replays, then K/C
+replays bracketed by HIP events on the stream the kernels run on; the prefill
+step is a single kernel, so its time per step is also that kernel's average
+launch duration.  The same K calls issued one by one from Python are timed too
+("eager", host-bound for small workloads).  Rank 0 prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -56,6 +64,7 @@ def _traffic(profile_name, src_names):
 
 
 def _time(fn, steps, warmup, stream):
+    """Eager: K back-to-back calls from Python, after W warmup calls."""
     import torch
 
     for i in range(warmup):
@@ -71,6 +80,33 @@ def _time(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps   # ms per call
 
 
+def _graph_time(fn, steps, warmup, period=1):
+    """K calls as replays of one captured chunk of C calls (C = gcd(K, W), a
+    multiple of `period` so rotating inputs keep their order); W/C untimed
+    replays first.  Returns ms per call."""
+    import torch
+
+    c = math.gcd(steps, warmup) if warmup else steps
+    if c % period:
+        c = steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(c):
+            fn(i)
+    for _ in range(warmup // c):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps // c):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (steps // c * c)
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -81,6 +117,170 @@ def _cpu_model():
     return "unknown"
 
 
+def _problem(sdpa, w):
+    code = {"f16": sdpa.F16, "bf16": sdpa.BF16, "fp8_e4m3": sdpa.FP8_E4M3}
+    return sdpa.make_problem(batch=w.batch, q_len=1 if w.decode else w.q_len, kv_len=w.kv_len, head_q=w.head_q,
+                             head_kv=w.head_kv, d_qk=w.d_qk, d_v=w.d_v, in_dtype=code[w.dtype],
+                             out_dtype=code[w.out_dtype], causal=w.causal, scale=w.scale)
+
+
+def _kernels_of(sdpa, w, num_cus=256):
+    """(kernel name, grid size in work-items) of each launch one call of
+    workload `w` makes, from the host planner."""
+    p = sdpa.plan(_problem(sdpa, w), decode=w.decode, num_cus=num_cus)
+    t = {"f16": "F16", "bf16": "Bf16"}.get(w.dtype)
+    c = "true" if w.causal else "false"
+    if w.decode:
+        return [(f"decode_split_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}>", p.num_groups * p.waves_per_group * 64),
+                (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 64)]
+    if w.dtype == "fp8_e4m3":
+        return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
+    fam = "prefill_wide_kernel" if p.rows_per_wave == 64 else "prefill_kernel"
+    return [(f"{fam}<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
+
+
+# kernel-source files whose text decides each profiled kernel's code
+_SOURCES = {"prefill": ["prefill.hip", "prefill_wide.hip", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
+            "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"]}
+_PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
+
+
+def _counters_pass():
+    """Short run for `rocprofv3 --pmc`: a plain 256 MiB device copy (the
+    calibration of the byte counters), then 5 calls each of the causal GQA
+    prefill and of the split-KV decode (rotating K/V sets)."""
+    import torch
+
+    import attention_flash_sdpa_amd as sdpa
+    from attention_flash_sdpa_amd import inputs
+
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    qd, kd, vd = (t.to(dev) for t in inputs.make_qkv(w)[:3])
+    out = torch.empty(w.batch, w.q_len, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
+    dw = inputs.WORKLOADS["splitkv_decode_bf16"]
+    dq, dk0, dv0, _ = inputs.make_qkv(dw)
+    dqd = dq.reshape(dw.batch, dw.head_q, dw.d_qk).to(dev)
+    sets = [(dk0.to(dev), dv0.to(dev))] + [
+        (torch.empty_like(dk0, device=dev).normal_(), torch.empty_like(dv0, device=dev).normal_())
+        for _ in range(1, dw.kv_sets)]
+    dout = torch.empty(dw.batch, dw.head_q, dw.d_v, dtype=torch.bfloat16, device=dev)
+    ws = sdpa.decode_workspace(dqd, sets[0][0], sets[0][1])
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        sdpa.prefill(qd, kd, vd, scale=w.scale, causal=True, out=out)
+    torch.cuda.synchronize()
+    for i in range(4 * 5):
+        sdpa.decode(dqd, sets[i % 4][0], sets[i % 4][1], scale=dw.scale, out=dout, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20", flush=True)
+
+
+def _read_csv(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _summarize_trace(d):
+    """Per-workload kernel-duration summaries from a `rocprofv3 --kernel-trace
+    --stats` run of bench.py, written to profiles/<kernel>_<workload>_trace.txt."""
+    import statistics
+
+    import attention_flash_sdpa_amd as sdpa
+    from attention_flash_sdpa_amd import inputs
+
+    rows = _read_csv(os.path.join(d, "run_kernel_trace.csv"))
+    cmd = open(os.path.join(d, "command.txt")).read().strip() if os.path.exists(os.path.join(d, "command.txt")) \
+        else "(command not recorded)"
+    for wname, w in inputs.WORKLOADS.items():
+        for kname, grid in _kernels_of(sdpa, w):
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+                    if kname in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid]
+            if not durs:
+                continue
+            r0 = next(r for r in rows if kname in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid)
+            fam = kname.split("<")[0]
+            out = os.path.join(ROOT, "profiles", f"{fam}_{wname}_trace.txt")
+            alg = w.bytes_moved() if w.decode else w.flops()
+            with open(out, "w") as f:
+                f.write(f"kernel: {r0['Kernel_Name']}\nworkload: {wname}\n")
+                f.write(f"command: {cmd}\n")
+                f.write(f"grid work-items: {grid}  workgroup: {r0['Workgroup_Size_X']}  lds_bytes: "
+                        f"{r0['LDS_Block_Size']}  scratch: {r0['Scratch_Size']}  vgpr: {r0['VGPR_Count']}  "
+                        f"agpr: {r0['Accum_VGPR_Count']}  sgpr: {r0['SGPR_Count']}\n")
+                f.write(f"dispatches: {len(durs)}\n")
+                f.write(f"avg_us: {statistics.mean(durs):.3f}\nmedian_us: {statistics.median(durs):.3f}\n"
+                        f"min_us: {min(durs):.3f}\nmax_us: {max(durs):.3f}\n")
+                if w.decode:
+                    f.write(f"algorithmic bytes per call (Q+K+V+O): {alg}\n")
+                else:
+                    med = statistics.median(durs)
+                    f.write(f"algorithmic flop per call: {alg}\nTFLOP/s at median: {alg / med / 1e6:.1f}\n")
+            print("wrote", out)
+
+
+def _summarize_counters(fetch_dir, write_dir):
+    """HBM bytes per launch from two `rocprofv3 --pmc` runs of the counters
+    pass (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter
+    reads for the 256 MiB device copy, written to profiles/*_counters.txt."""
+    import statistics
+
+    import attention_flash_sdpa_amd as sdpa
+    from attention_flash_sdpa_amd import inputs
+
+    copy_bytes = 256 << 20
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        first_sdpa = min(int(r["Dispatch_Id"]) for r in rows if "sdpa::" in r["Kernel_Name"])
+        copies = [r for r in rows if "copy" in r["Kernel_Name"].lower() and int(r["Dispatch_Id"]) < first_sdpa][-3:]
+        kib_copy = statistics.mean(float(r["Counter_Value"]) for r in copies)
+        factor = copy_bytes / (kib_copy * 1024.0)
+        per = {}
+        for wname in _PROFILED:
+            w = inputs.WORKLOADS[wname]
+            for kname, grid in _kernels_of(sdpa, w):
+                vals = [float(r["Counter_Value"]) for r in rows
+                        if kname in r["Kernel_Name"] and int(r["Grid_Size"]) == grid]
+                per[(wname, kname)] = (statistics.mean(vals), len(vals))
+        res[counter] = (kib_copy, factor, per, copies[0]["Kernel_Name"])
+    for wname, stem in _PROFILED.items():
+        w = inputs.WORKLOADS[wname]
+        kind = "decode" if w.decode else "prefill"
+        out = os.path.join(ROOT, "profiles", f"{stem}_counters.txt")
+        total = 0.0
+        with open(out, "w") as f:
+            f.write(f"workload: {wname}\n")
+            f.write("commands:\n  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run "
+                    "-- python3 bench.py --counters-pass\n  rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                    "-d gpurun_out/pmc_write -o run -- python3 bench.py --counters-pass\n"
+                    "  python3 bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write\n")
+            for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                kib_copy, factor, per, cname = res[counter]
+                f.write(f"{counter}: calibration copy of {copy_bytes} B ({cname}) reads {kib_copy:.1f} KiB "
+                        f"-> scale factor {factor:.4f}\n")
+                for (wn, kname), (kib, n) in per.items():
+                    if wn != wname:
+                        continue
+                    b = kib * 1024.0 * factor
+                    total += b
+                    f.write(f"  {kname}: {kib:.1f} KiB/dispatch over {n} dispatches -> {b:.0f} B\n")
+            alg = w.bytes_moved()
+            f.write(f"algorithmic bytes per call (Q+K+V+O once): {alg}\n")
+            f.write(f"hbm_bytes_per_launch: {total:.0f}\n")
+            f.write(f"ratio to algorithmic: {total / alg:.3f}\n")
+            f.write(f"source_sha256: {_src_hash(*_SOURCES[kind])}\n")
+        print("wrote", out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,11 +288,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters-pass", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention path "
-              "shards by heads with no communication, see DESIGN.md)", file=sys.stderr)
+              "shards by heads with no communication; the sharding plan is written up with the design)",
+              file=sys.stderr)
         sys.exit(2)
+    if args.summarize_trace:
+        return _summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return _summarize_counters(*args.summarize_counters)
+    if args.counters_pass:
+        return _counters_pass()
 
     import numpy as np
     import torch
@@ -105,19 +315,22 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     props = torch.cuda.get_device_properties(0)
+    ncu = props.multi_processor_count
 
     # ---------------- headline: causal GQA bf16 prefill ----------------
     w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
     q, k, v, _ = inputs.make_qkv(w)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     out = torch.empty(w.batch, w.q_len, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
-    ms = _time(lambda i: sdpa.prefill(qd, kd, vd, scale=w.scale, causal=True, out=out), args.steps, args.warmup,
-               stream)
+
+    def step(i):
+        sdpa.prefill(qd, kd, vd, scale=w.scale, causal=True, out=out)
+
+    eager_ms = _time(step, args.steps, args.warmup, stream)
+    ms = _graph_time(step, args.steps, args.warmup)
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
-    plan = sdpa.plan(sdpa.make_problem(batch=w.batch, q_len=w.q_len, kv_len=w.kv_len, head_q=w.head_q,
-                                       head_kv=w.head_kv, d_qk=w.d_qk, d_v=w.d_v, in_dtype=sdpa.BF16,
-                                       out_dtype=sdpa.BF16, causal=True, scale=w.scale))
+    plan = sdpa.plan(_problem(sdpa, w), num_cus=ncu)
 
     # sampled parity of the timed output against the oracle
     import oracle
@@ -139,21 +352,23 @@ def main():
                           for t in (dk0, dv0)))
     dout = torch.empty(dw.batch, dw.head_q, dw.d_v, dtype=torch.bfloat16, device=dev)
     ws = sdpa.decode_workspace(dqd, sets[0][0], sets[0][1])
-    dms = _time(lambda i: sdpa.decode(dqd, sets[i % len(sets)][0], sets[i % len(sets)][1], scale=dw.scale,
-                                      out=dout, workspace=ws),
-                args.decode_steps, args.warmup, stream)
+
+    def dstep(i):
+        kk, vv = sets[i % len(sets)]
+        sdpa.decode(dqd, kk, vv, scale=dw.scale, out=dout, workspace=ws)
+
+    deager_ms = _time(dstep, args.decode_steps, args.warmup, stream)
+    dms = _graph_time(dstep, args.decode_steps, args.warmup, period=len(sets))
     dbytes = dw.bytes_moved()
     dgbs = dbytes / (dms * 1e-3) / 1e9
-    dplan = sdpa.plan(sdpa.make_problem(batch=dw.batch, q_len=1, kv_len=dw.kv_len, head_q=dw.head_q,
-                                        head_kv=dw.head_kv, d_qk=dw.d_qk, d_v=dw.d_v, in_dtype=sdpa.BF16,
-                                        out_dtype=sdpa.BF16, causal=False, scale=dw.scale),
-                      decode=True, num_cus=props.multi_processor_count)
+    dplan = sdpa.plan(_problem(sdpa, dw), decode=True, num_cus=ncu)
     sdpa.decode(dqd, sets[0][0], sets[0][1], scale=dw.scale, out=dout, workspace=ws)
     torch.cuda.synchronize()
     drows = np.array([(b, 0, h) for b in (0, 7, 15) for h in (0, 17, 31)], dtype=np.int64)
     dref = oracle.sdpa(dq, dk0, dv0, scale=dw.scale, causal=False, rows=drows, want_lse=False)["out"]
     dgot = dout.cpu()[drows[:, 0], drows[:, 2]].double().numpy()
     decode_err = float(np.abs(dgot - dref).max())
+    del sets
 
     # ---------------- other prefill workloads (context lines) ----------------
     extra = {}
@@ -164,32 +379,37 @@ def main():
         odt = torch.bfloat16 if xw.out_dtype == "bf16" else torch.float16
         xo = torch.empty(xw.batch, xw.q_len, xw.head_q, xw.d_v, dtype=odt, device=dev)
         n = 100 if xw.flops() < 1e9 else max(args.steps // 4, 1)
-        xms = _time(lambda i: sdpa.prefill(xq, xk, xv, scale=xw.scale, causal=xw.causal, out=xo, descale=xds),
-                    n, args.warmup, stream)
+
+        def xstep(i):
+            sdpa.prefill(xq, xk, xv, scale=xw.scale, causal=xw.causal, out=xo, descale=xds)
+
+        xeager = _time(xstep, n, args.warmup, stream)
+        xms = _graph_time(xstep, n, args.warmup)
         xt = xw.flops() / (xms * 1e-3) / 1e12
         peak = PEAK_FP8_TFLOPS if xw.dtype == "fp8_e4m3" else PEAK_BF16_TFLOPS
-        extra[name] = {"value": round(xt, 3), "unit": "TFLOP/s", "ms_per_call": round(xms, 6), "steps": n,
+        extra[name] = {"value": round(xt, 3), "unit": "TFLOP/s", "ms_per_call": round(xms, 6),
+                       "eager_ms_per_call": round(xeager, 6), "steps": n,
                        "algorithmic_gflop": round(xw.flops() / 1e9, 4), "peak": peak,
                        "frac_of_peak": round(xt / peak, 5)}
         del xq, xk, xv, xo
-    # launch floor: a one-element device op timed the same way
+    # launch floor: a one-element device op, eager and replayed from a graph
     one = torch.zeros(1, device=dev)
-    floor_ms = _time(lambda i: one.add_(1.0), args.steps, args.warmup, stream)
+    floor_eager = _time(lambda i: one.add_(1.0), args.steps, args.warmup, stream)
+    floor_graph = _graph_time(lambda i: one.add_(1.0), args.steps, args.warmup)
 
     # ---------------- CPU baseline: the oracle on the host cores ----------------
     cpu = None
     if not args.no_cpu_baseline:
         threads = len(os.sched_getaffinity(0))
-        os.environ["OMP_NUM_THREADS"] = str(threads)
         t0 = time.perf_counter()
         oracle.sdpa(q, k, v, scale=w.scale, causal=True, want_lse=False, threads=threads)
         sec = time.perf_counter() - t0
-        cpu = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": f"whole causal GQA prefill workload ({w.batch * w.q_len * w.head_q} rows, "
+        cpu = {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"whole causal GQA prefill workload ({w.batch * w.q_len * w.head_q} query rows, "
                          f"{flops / 1e9:.2f} GFLOP) in {sec:.2f} s, fp64, {_cpu_model()}"}
 
-    traffic = _traffic("prefill_gqa_causal_bf16_counters.txt", ["prefill.hip", "sdpa_device.h"])
-    dtraffic = _traffic("decode_splitkv_bf16_counters.txt", ["decode.hip", "sdpa_device.h"])
+    traffic = _traffic("prefill_gqa_causal_bf16_counters.txt", _SOURCES["prefill"])
+    dtraffic = _traffic("decode_splitkv_bf16_counters.txt", _SOURCES["decode"])
     line = {
         "metric": "attention TFLOP/s (causal GQA bf16 prefill) + decode achieved HBM GB/s, 1 GPU",
         "value": round(tflops, 3),
@@ -205,13 +425,16 @@ def main():
         "data": "synthetic (seeded N(0,1), bf16)",
         "config": {"workload": w.name, "batch": w.batch, "head_q": w.head_q, "head_kv": w.head_kv,
                    "q_len": w.q_len, "kv_len": w.kv_len, "d_qk": w.d_qk, "d_v": w.d_v, "causal": True,
-                   "algorithmic_gflop": round(flops / 1e9, 4), "grid": plan.num_groups},
+                   "algorithmic_gflop": round(flops / 1e9, 4), "grid": plan.num_groups,
+                   "launch": "hip graph replay of gcd(steps, warmup) calls"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 5), "traffic": traffic},
         "cpu_baseline": cpu,
+        "eager": {"ms_per_step": round(eager_ms, 6), "value": round(flops / (eager_ms * 1e-3) / 1e12, 3)},
         "parity": {"max_abs_err": prefill_err, "nan": prefill_nan, "sampled_rows": int(len(rows))},
         "decode": {
             "workload": dw.name, "value": round(dgbs, 2), "unit": "GB/s", "ms_per_call": round(dms, 6),
+            "eager_ms_per_call": round(deager_ms, 6),
             "steps": args.decode_steps, "kv_sets": dw.kv_sets, "num_splits": dplan.num_splits,
             "algorithmic_bytes": dbytes,
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -219,8 +442,8 @@ def main():
             "parity": {"max_abs_err": decode_err},
         },
         "other_workloads": extra,
-        "launch_floor_us": round(floor_ms * 1e3, 3),
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "launch_floor_us": {"eager": round(floor_eager * 1e3, 3), "graph": round(floor_graph * 1e3, 3)},
+        "device": {"name": props.name, "cus": ncu},
     }
     print(json.dumps(line), flush=True)
 

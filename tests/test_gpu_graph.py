@@ -1,0 +1,71 @@
+"""HIP-graph capture of the C-ABI calls (the way bench.py times them).
+
+The library allocates, frees and synchronizes nothing, so a caller may capture
+its launches into a graph.  Each replay here is checked bit for bit against
+the eager call on the same inputs, with eager work and synchronizations
+between the replays, and the graph's output buffer cleared before each replay
+so that a replay which did nothing cannot pass.
+"""
+import sys
+
+import pytest
+import torch
+
+import attention_flash_sdpa_amd as sdpa
+from attention_flash_sdpa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    sdpa.load()
+    return torch.device("cuda:0")
+
+
+def _replays_match(dev, call, out, n_calls, replays=3):
+    torch.cuda.synchronize()
+    call(0)
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            call(i)
+    for r in range(replays):
+        out.zero_()
+        scratch = torch.randn(1 << 20, device=dev)        # eager work between replays
+        scratch.mul_(2.0).sum().item()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(out, want)
+        _say(f"  replay {r}: bit-identical={same}")
+        assert same, f"replay {r} differs from the eager call"
+
+
+def test_prefill_graph_replay(dev):
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    q, k, v, _ = inputs.make_qkv(w, q_len=200, kv_len=333)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out = torch.empty(w.batch, 200, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.batch, w.head_q, 200, dtype=torch.float32, device=dev)
+    _say("prefill graph: causal GQA bf16 q 200 kv 333")
+    _replays_match(dev, lambda i: sdpa.prefill(qd, kd, vd, scale=w.scale, causal=True, out=out, lse=lse), out, 2)
+
+
+def test_decode_graph_replay(dev):
+    w = inputs.WORKLOADS["splitkv_decode_bf16"]
+    q, k, v, _ = inputs.make_qkv(w, kv_len=1500)
+    qd = q.reshape(w.batch, w.head_q, w.d_qk).to(dev)
+    kd, vd = k.to(dev), v.to(dev)
+    out = torch.empty(w.batch, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
+    ws = sdpa.decode_workspace(qd, kd, vd)
+    _say("decode graph: B16 32/8 heads kv 1500")
+    _replays_match(dev, lambda i: sdpa.decode(qd, kd, vd, scale=w.scale, out=out, workspace=ws), out, 2)
