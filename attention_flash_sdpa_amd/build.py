@@ -31,7 +31,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 # Per-source backend options.  The wide prefill kernel runs one wave per SIMD
 # with both register files: MFMA results stay in VGPRs (the softmax reads the
 # scores with VALU instructions), AGPRs take what does not fit.
-EXTRA = {"prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, isa: bool) -> str:

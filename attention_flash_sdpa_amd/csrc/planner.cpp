@@ -108,7 +108,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
       // default until the wide one measures faster)
       bool wide = false;
       (void)wide_waves;
-      if (variant == 1) wide = false;
+      if (variant == 1 || variant == 3 || variant == 4) wide = false;
       if (variant == 2) wide = true;
       if (wide) {
         rows = kWideRowsPerWave;
@@ -118,32 +118,50 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     plan->kernel = kid;
     plan->waves_per_group = kPrefillWaves;
     plan->rows_per_wave = rows;
+    plan->block_k = rows == kWideRowsPerWave ? kWideBlockK : kPrefillBlockK;
+    plan->stages = 2;
+    plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);
     // Pack query heads of one GQA group into the workgroup when the group
     // size allows it (K/V blocks in LDS are then shared by several heads);
     // otherwise stack consecutive query tiles of one head.  Short queries
     // pack heads even when the group size is not a multiple of the pack.
-    int hp;
-    if (G % 4 == 0) hp = 4;
-    else if (G % 2 == 0) hp = 2;
-    else hp = 1;
-    if (p.q_len <= rows) hp = (int)(G < kPrefillWaves ? G : kPrefillWaves);
-    while (kPrefillWaves % hp) --hp;
+    auto shape = [&](int waves, int* hp_out, int* qt_out) -> int64_t {
+      int hp;
+      if (G % 4 == 0) hp = 4;
+      else if (G % 2 == 0) hp = 2;
+      else hp = 1;
+      if (p.q_len <= rows) hp = (int)(G < waves ? G : waves);
+      if (hp > waves) hp = waves;
+      while (waves % hp) --hp;
+      const int qtiles = waves / hp;
+      *hp_out = hp;
+      *qt_out = qtiles;
+      return (int64_t)p.batch * p.head_kv * ceil_div(G, hp) * ceil_div(p.q_len, (int64_t)rows * qtiles);
+    };
+    int hp, qtiles, ks = 1;
+    int64_t groups = shape(kPrefillWaves, &hp, &qtiles);
+    // Too few workgroups to give every CU one: split the key range of each
+    // workgroup in two halves, each streamed by half of its waves and merged
+    // at the end, which doubles the workgroup count.
+    bool split = rows == kRowsPerWave && kid != kPrefillFp8D192 && groups < num_cus && plan->kv_blocks >= 2;
+    if (variant == 3) split = false;
+    if (variant == 4) split = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (split) {
+      ks = 2;
+      groups = shape(kPrefillWaves / 2, &hp, &qtiles);
+    }
+    plan->num_splits = ks;
     plan->heads_per_group = hp;
-    plan->qtiles_per_group = kPrefillWaves / hp;
-    plan->block_q = rows * plan->qtiles_per_group;
-    plan->block_k = rows == kWideRowsPerWave ? kWideBlockK : kPrefillBlockK;
-    plan->stages = 2;
+    plan->qtiles_per_group = qtiles;
+    plan->block_q = rows * qtiles;
     plan->q_tiles = (int32_t)ceil_div(p.q_len, plan->block_q);
-    plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);
-    const int64_t head_groups = ceil_div(G, hp);
-    const int64_t groups = (int64_t)p.batch * p.head_kv * head_groups * plan->q_tiles;
     if (groups >= lim) {
       set_error("grid too large (%lld workgroups)", (long long)groups);
       return SDPA_ERR_BAD_SHAPE;
     }
     plan->num_groups = (int32_t)groups;
     const int esz = p.in_dtype == SDPA_FP8_E4M3 ? 1 : 2;
-    plan->lds_bytes = (uint64_t)plan->stages * plan->block_k * (p.d_qk + p.d_v) * esz;
+    plan->lds_bytes = (uint64_t)ks * plan->stages * plan->block_k * (p.d_qk + p.d_v) * esz;
     plan->workspace_bytes = 0;
     return SDPA_OK;
   }

@@ -42,28 +42,43 @@
 
 namespace sdpa {
 
-template <class T, int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// LDS reads issued after those of slot n when its MFMA runs: the reads of
+// slots n+1 .. n+pd (one K fragment per QK slot when there is a next block,
+// two transposed V reads per PV slot).
+template <int NQK, int NSLOT, int PD, bool NEXT>
+__host__ __device__ constexpr int reads_ahead(int n) {
+  int c = 0;
+  for (int m = n + 1; m <= n + PD; ++m) c += m < NQK ? (NEXT ? 1 : 0) : (m < NSLOT ? 2 : 0);
+  return c;
+}
+
+template <class T, int D, int DV, bool CAUSAL, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(const PrefillArgs a) {
   constexpr int BK = kPrefillBlockK;
-  constexpr int NW = kPrefillWaves;
-  constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
-  constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte slots per row
+  constexpr int NWS = kPrefillWaves / KS;       // waves sharing one K/V stream
+  constexpr int KROW = D * 2, VROW = DV * 2;    // LDS bytes per key row
+  constexpr int KCPR = D / 8, VCPR = DV / 8;    // 16-byte slots per row
   constexpr int KBYTES = BK * KROW, VBYTES = BK * VROW;
-  constexpr int K_INSTR = BK * KCPR / 64 / NW;  // 1 KiB direct loads per wave per block
-  constexpr int V_INSTR = BK * VCPR / 64 / NW;
+  constexpr int K_INSTR = BK * KCPR / 64 / NWS; // 1 KiB direct loads per wave per block
+  constexpr int V_INSTR = BK * VCPR / 64 / NWS;
   constexpr int NT = DV / 32;                   // O^T accumulator tiles
+  constexpr int KSTEPS = D / 16;                // MFMA k-steps of S^T = K Q^T
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "block too small for the fill");
-  // LDS: K buffers 0/1, then V buffers 0/1
+  static_assert(KS == 1 || KS == 2, "one or two key ranges per workgroup");
+  // LDS per key range: K buffers 0/1, then V buffers 0/1
   constexpr uint32_t KBUF0 = 0, KBUF1 = KBYTES;
   constexpr uint32_t VBUF0 = 2 * KBYTES, VBUF1 = 2 * KBYTES + VBYTES;
+  constexpr uint32_t RANGE_BYTES = 2 * KBYTES + 2 * VBYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem;
+  __shared__ __attribute__((aligned(1024))) char smem[KS * RANGE_BYTES];
 
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hl = lane >> 5;  // lane half
+  const int kr_i = wave / NWS;  // key range of this wave
+  const int wis = wave % NWS;   // wave index within its key range
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem + kr_i * RANGE_BYTES;
+  const int hl = lane >> 5;     // lane half
   const int l32 = lane & 31;
 
   // ---- work decode -------------------------------------------------------
@@ -75,8 +90,8 @@ void prefill_kernel(const PrefillArgs a) {
   const int g = rest % a.head_kv;
   const int b = rest / a.head_kv;
   if (CAUSAL) qt = a.q_tiles - 1 - qt;  // heaviest causal tiles first
-  const int hp_i = wave % a.heads_per_group;
-  const int qp_i = wave / a.heads_per_group;
+  const int hp_i = wis % a.heads_per_group;
+  const int qp_i = wis / a.heads_per_group;
   // heads_per_group need not divide the group size: waves past the group's
   // last head run the loop (uniform barriers) but store nothing
   const bool head_ok = hg * a.heads_per_group + hp_i < a.group;
@@ -97,7 +112,7 @@ void prefill_kernel(const PrefillArgs a) {
   elem_t* __restrict__ optr = (elem_t*)a.o;
 
   if (n_blocks == 0) {  // no visible key for any row of this workgroup
-    if (row_ok) {
+    if (row_ok && kr_i == 0) {
       elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
       for (int c = hl * (DV / 2); c < (hl + 1) * (DV / 2); c += 8) *(u32x4_t*)(orow + c) = u32x4_t{0, 0, 0, 0};
       if (a.lse != nullptr && hl == 0) a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = -INFINITY;
@@ -105,78 +120,101 @@ void prefill_kernel(const PrefillArgs a) {
     return;
   }
 
-  // ---- Q fragments (B operand of S^T = K Q^T), loaded once ---------------
-  u32x4_t qf[D / 16];
-  {
-    const elem_t* qptr = (const elem_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4_t v = *(const u32x4_t*)(qptr + 16 * s);
-      qf[s] = row_ok ? v : u32x4_t{0, 0, 0, 0};
-    }
-  }
+  // Key range of this wave: with two ranges, range 0 takes blocks
+  // [0, half) and range 1 blocks [half, n_blocks); when n_blocks is odd,
+  // range 1 ends with one block past the visible keys, which the mask
+  // removes entirely, so both ranges run the same number of iterations.
+  const int cnt = KS == 1 ? n_blocks : (n_blocks + 1) / 2;
+  const int kb0 = kr_i * cnt;
+  const int n_unmasked = min(max(n_full - kb0, 0), cnt);
 
   // ---- direct global -> LDS fills ------------------------------------------
   // Instruction i of this wave covers the 64 16-byte slots starting at slot
-  // (wave*INSTR + i)*64; lane p holds slot P: row P / CPR, position P % CPR,
+  // (wis*INSTR + i)*64; lane p holds slot P: row P / CPR, position P % CPR,
   // which receives chunk (P % CPR) ^ swizzle(row) of that key row.
   const char* kg = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * (D * 2);
   const char* vg = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * (DV * 2);
   const int kstride = a.head_kv * D * 2;  // bytes between consecutive keys
   const int vstride = a.head_kv * DV * 2;
-  uint32_t kfo[K_INSTR], vfo[V_INSTR];    // byte offsets within a whole block
+  // per fill instruction: the lane's key row within the block and the byte
+  // offset of its 16-byte chunk within the key row
+  int krow[K_INSTR], vrow[V_INSTR];
+  uint32_t kch[K_INSTR], vch[V_INSTR];
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
-    const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
-    kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
+    const int slot = (wis * K_INSTR + i) * 64 + lane, r = slot / KCPR;
+    krow[i] = r;
+    kch[i] = ((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
-    const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
-    vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
+    const int slot = (wis * V_INSTR + i) * 64 + lane, r = slot / VCPR;
+    vrow[i] = r;
+    vch[i] = ((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16;
   }
   const int last_key = Sk - 1;
-  // A block is whole if all its BK keys exist; in the last block of a ragged
-  // key range the rows past the end re-read the last key (they are masked).
-  auto fill_k = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
-    const uint32_t l = lds0 + buf + wave * K_INSTR * 1024;
-    if ((kb + 1) * BK <= Sk) {
-      const char* base = kg + (size_t)kb * BK * kstride;
+  uint32_t kfo[K_INSTR], vfo[V_INSTR];    // lane byte offsets within a whole block
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) kfo[i] = krow[i] * kstride + kch[i];
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) vfo[i] = vrow[i] * vstride + vch[i];
+  // First key held by the LDS copy of block kb: its own start, except for a
+  // block that would run past the last key, which is loaded as the last BK
+  // keys instead (its keys before kb*BK, already processed, are masked).  So
+  // every load is a whole block at a scalar base with fixed lane offsets.
+  // With fewer than BK keys in all (one block) the rows past the end re-read
+  // the last key and are masked.
+  const bool whole_tail = Sk >= BK;
+  auto row0_of = [&](int kb) __attribute__((always_inline)) -> int {
+    return whole_tail ? min(kb * BK, Sk - BK) : kb * BK;
+  };
+  auto fill_k = [&](int j, uint32_t buf) __attribute__((always_inline)) {
+    const int kb = kb0 + j;
+    const uint32_t l = lds0 + buf + wis * K_INSTR * 1024;
+    if (whole_tail) {
+      const char* base = kg + (size_t)row0_of(kb) * kstride;
 #pragma unroll
       for (int i = 0; i < K_INSTR; ++i) global_to_lds_16_sbase(base, kfo[i], l + i * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < K_INSTR; ++i) {
-        const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
-        const int key = min(kb * BK + r, last_key);
-        global_to_lds_16(kg + (size_t)key * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16),
-                         l + i * 1024);
-      }
+      for (int i = 0; i < K_INSTR; ++i)
+        global_to_lds_16_sbase(kg, (uint32_t)(min(kb * BK + krow[i], last_key) * kstride) + kch[i], l + i * 1024);
     }
   };
-  auto fill_v = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
-    const uint32_t l = lds0 + buf + wave * V_INSTR * 1024;
-    if ((kb + 1) * BK <= Sk) {
-      const char* base = vg + (size_t)kb * BK * vstride;
+  auto fill_v = [&](int j, uint32_t buf) __attribute__((always_inline)) {
+    const int kb = kb0 + j;
+    const uint32_t l = lds0 + buf + wis * V_INSTR * 1024;
+    if (whole_tail) {
+      const char* base = vg + (size_t)row0_of(kb) * vstride;
 #pragma unroll
       for (int i = 0; i < V_INSTR; ++i) global_to_lds_16_sbase(base, vfo[i], l + i * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < V_INSTR; ++i) {
-        const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
-        const int key = min(kb * BK + r, last_key);
-        global_to_lds_16(vg + (size_t)key * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16),
-                         l + i * 1024);
-      }
+      for (int i = 0; i < V_INSTR; ++i)
+        global_to_lds_16_sbase(vg, (uint32_t)(min(kb * BK + vrow[i], last_key) * vstride) + vch[i], l + i * 1024);
     }
   };
+
+  // first K block, then Q (registers), then the first V block and the next K
+  // block: one wait covers K(0) and Q
+  fill_k(0, KBUF0);
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once ---------------
+  u32x4_t qf[KSTEPS];
+  {
+    const elem_t* qptr = (const elem_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4_t*)(qptr + 16 * s);
+  }
+  fill_v(0, VBUF0);
+  if (cnt > 1) fill_k(1, KBUF1);
 
   // ---- per-lane LDS read offsets -----------------------------------------
   // K fragment (A operand): key row l%32 (+32 for the second score tile),
   // head-dim slot 2*s + l/32.
-  uint32_t koff[D / 16];
+  uint32_t koff[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
+  for (int s = 0; s < KSTEPS; ++s)
     koff[s] = lds0 + l32 * KROW + ((((2 * s + hl)) ^ (int)swz_prefill<KCPR>(l32)) << 4);
   // V^T fragment (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16: lane
   // (group gq = l/16, s = l%16) addresses key row 4*(gq/2) + s/4 (+8 for the
@@ -208,7 +246,8 @@ void prefill_kernel(const PrefillArgs a) {
   const float s2 = a.s2;
   f32x16_t sa[2], sb[2];    // score tiles of two consecutive blocks
 
-  // GEMM 1: S^T[key][query] of the block in K buffer KB
+  // GEMM 1: S^T[key][query] of the block in K buffer KB: two 32-key tiles,
+  // KSTEPS MFMAs each
   auto qk = [&](auto kb_tag, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
     constexpr uint32_t KB = decltype(kb_tag)::value;
 #pragma unroll
@@ -217,7 +256,7 @@ void prefill_kernel(const PrefillArgs a) {
       sc[1][r] = 0.f;
     }
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int s = 0; s < KSTEPS; ++s) {
       const u32x4_t k0 = lds_read_b128(koff[s] + KB);
       const u32x4_t k1 = lds_read_b128(koff[s] + KB + 32 * KROW);
       sc[0] = mfma32x32x16<T>(k0, qf[s], sc[0]);
@@ -225,43 +264,60 @@ void prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // Softmax part 1: mask (tail blocks only), block row max, lazy rescale.
-  // Returns the subtrahend m of P = 2^(s2*S - m).
-  auto softmax_max = [&](int kb, f32x16_t (&sc)[2], auto masked_tag) __attribute__((always_inline)) -> float {
+  // Visible positions of block kb for this lane: register r of score tile t
+  // holds key row0 + 4*hl + 32t + 8(r/4) + r%4, visible iff it is at least
+  // kb*BK (not processed before) and at most the row's last visible key; the
+  // position 32t + 8(r/4) + r%4 must lie in [lo, hi].
+  struct Window {
+    int lo, hi;
+  };
+  auto window = [&](int kb) __attribute__((always_inline)) -> Window {
+    const int base = row0_of(kb) + 4 * hl;
+    return Window{kb * BK - base, (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - base};
+  };
+
+  // Block row max (log2 domain, scale folded in).  In a masked block the
+  // scores are replaced in place by s2*S or -inf.
+  auto block_max = [&](int j, f32x16_t (&sc)[2], auto masked_tag) __attribute__((always_inline)) -> float {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    float bmax;
     if constexpr (MASKED) {
-      // register r of tile t holds key kb*BK + 4*hl + 32t + 8(r/4) + r%4; it is
-      // visible iff that key <= the row's last visible key
-      const int lim = (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl);
-      bmax = -INFINITY;
+      const Window w = window(kb0 + j);
+      float bmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = (32 * t + 8 * (r >> 2) + (r & 3)) <= lim ? sc[t][r] * s2 : -INFINITY;
+          const int pos = 32 * t + 8 * (r >> 2) + (r & 3);
+          const float x = (pos >= w.lo && pos <= w.hi) ? sc[t][r] * s2 : -INFINITY;
           sc[t][r] = x;
           bmax = fmaxf(bmax, x);
         }
+      return bmax;
     } else {
-      float mx = sc[0][0];
+      float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
-      bmax = mx * s2;
+        for (int r = (t == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+      return mx * s2;
     }
+  };
+
+  // Row max across the lane pair and lazy rescale: the running max only moves
+  // (and O, l are rescaled by 2^(m_old - m_new)) when some row's block max
+  // exceeds it by more than kSlack; otherwise the stale max is kept, so
+  // P <= 2^kSlack.  The final O / l is unchanged because l accumulates the
+  // same P values.  Returns the subtrahend m of P = 2^(s2*S - m).
+  auto update_max = [&](float bmax, auto masked_tag) __attribute__((always_inline)) -> float {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     bmax = pair_max(bmax);
-    // Lazy rescale: the running max only moves (and O, l are rescaled by
-    // 2^(m_old - m_new)) when some row's block max exceeds it by more than
-    // kSlack; otherwise the stale max is kept, so P <= 2^kSlack.  The final
-    // O / l is unchanged because l accumulates the same P values.
     const float m_new = fmaxf(m_run, bmax);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kSlack)) {
       // rows that have seen no visible key keep m = -inf (masked blocks only)
       const float m_tgt = MASKED ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
       const float alpha = fast_exp2(m_run - m_tgt);
       l_run *= alpha;
+      mfma_acc_drain(acc);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -271,48 +327,35 @@ void prefill_kernel(const PrefillArgs a) {
     return MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
   };
 
-  // Softmax part 2: P = 2^(s2*S - m) packed to 16 bits as the PV B operand;
-  // the row sum is taken over the packed values.
-  auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0, p1;
-        if constexpr (MASKED) {
-          p0 = fast_exp2(sc[t][r] - m_sub);
-          p1 = fast_exp2(sc[t][r + 1] - m_sub);
-        } else {
-          p0 = fast_exp2(fmaf(sc[t][r], s2, -m_sub));
-          p1 = fast_exp2(fmaf(sc[t][r + 1], s2, -m_sub));
-        }
-        const uint32_t pk = pack2<T>(p0, p1);
-        pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
-        l_run = add_pair<T>(pk, l_run);
-      }
-  };
+  // ---- one pipeline iteration, as a fixed sequence of MFMA slots ----------
+  // Iteration j (PAR = j & 1): on entry the scores of block j are in
+  // registers with their subtrahend m_sub, K(j+1) sits in K buffer 1-PAR and
+  // V(j) in V buffer PAR, and every wave is past the reads of the previous
+  // iteration.  It runs 2*KSTEPS QK slots (the scores
+  // of block j+1, two 32-key tiles) followed by 4*NT PV slots (O^T += V^T P^T
+  // of block j, four 16-key chunks).  Every slot issues one MFMA, the LDS
+  // fragment reads of the slot kPD places ahead, one share of the vector work
+  // and, every few slots, one of the direct loads of V(j+1) / K(j+2) into the
+  // buffers the previous iteration freed.  The vector work is spread so that
+  // it runs under the matrix core:
+  //   QK slots:       exponentials of score tile 0 of block j
+  //   PV slots of chunks 0, 1: exponentials of score tile 1 (chunks 2, 3)
+  //   last PV slots:  row max of block j+1
+  // A scheduling fence closes each slot, so the order is the one written.
+  constexpr int NQK = 2 * KSTEPS;               // QK slots
+  constexpr int NPV = 4 * NT;                   // PV slots
+  constexpr int NSLOT = NQK + NPV;
+  constexpr int kPD = 4;                        // read-ahead distance (slots)
+  constexpr int NDMA = K_INSTR + V_INSTR;
+  constexpr int DSTRIDE = NSLOT / NDMA > 0 ? NSLOT / NDMA : 1;
+  constexpr int EXP1_SLOTS = 2 * NT;            // PV slots of chunks 0, 1
+  static_assert(16 % EXP1_SLOTS == 0 && (16 / EXP1_SLOTS) % 2 == 0, "tile-1 exponentials in pairs");
+  static_assert(NPV - EXP1_SLOTS > 0, "room for the row max");
 
-  // GEMM 2: O^T[dv][query] += V^T P^T from V buffer VB, 16 keys per MFMA
-  auto pv = [&](auto vb_tag, const u32x4_t (&pf)[4]) __attribute__((always_inline)) {
-    constexpr uint32_t VB = decltype(vb_tag)::value;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x2_t lo = lds_read_tr16(voff[0][t] + VB + (16 * c) * VROW);
-        const u32x2_t hi = lds_read_tr16(voff[1][t] + VB + (16 * c) * VROW);
-        const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
-        acc[t] = mfma32x32x16<T>(vf, pf[c], acc[t]);
-      }
-  };
-
-  // One pipeline iteration j (PAR = j & 1): the scores of block j are in
-  // registers, K(j+1) sits in K buffer 1-PAR and V(j) in V buffer PAR.  It
-  // starts the loads of V(j+1) and K(j+2) into the buffers freed by the
-  // previous iteration, computes the scores of block j+1, then the softmax
-  // and P V of block j.
-  auto iteration = [&](int j, auto masked_tag, auto next_tag, auto par_tag) __attribute__((always_inline)) {
+  auto iteration = [&](int j, float m_sub, auto mcur_tag, auto mnext_tag, auto next_tag, auto par_tag)
+      __attribute__((always_inline)) -> float {
+    constexpr bool MCUR = decltype(mcur_tag)::value;
+    constexpr bool MNEXT = decltype(mnext_tag)::value;
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
     constexpr uint32_t KB_NEXT = PAR ? KBUF0 : KBUF1;   // holds K(j+1)
@@ -321,80 +364,239 @@ void prefill_kernel(const PrefillArgs a) {
     constexpr uint32_t VB_FREE = PAR ? VBUF0 : VBUF1;   // receives V(j+1)
     f32x16_t(&s_cur)[2] = PAR ? sb : sa;
     f32x16_t(&s_nxt)[2] = PAR ? sa : sb;
-    if constexpr (NEXT) {
-      fill_v(j + 1, VB_FREE);
-      if (j + 2 < n_blocks) {
-        fill_k(j + 2, KB_FREE);
-        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) have landed
+
+    // Direct loads of this iteration, V(j+1) then K(j+2), without branches:
+    // an iteration with a next block implies more than BK keys, so every
+    // load is a whole block (the tail block shifted, see row0_of); when there
+    // is no block j+2 the K loads re-read block j+1 into the free buffer,
+    // which nothing reads afterwards.
+    const int kbv = kb0 + j + 1;
+    const int kbk = kb0 + min(j + 2, cnt - 1);
+    const char* vsrc = vg + (size_t)row0_of(kbv) * vstride;
+    const char* ksrc = kg + (size_t)row0_of(kbk) * kstride;
+    const uint32_t vl = lds0 + VB_FREE + wis * V_INSTR * 1024;
+    const uint32_t kl = lds0 + KB_FREE + wis * K_INSTR * 1024;
+    auto dma = [&](auto i_tag) __attribute__((always_inline)) {
+      constexpr int I = decltype(i_tag)::value;
+      if constexpr (I < V_INSTR)
+        global_to_lds_16_sbase(vsrc, vfo[I], vl + I * 1024);
+      else
+        global_to_lds_16_sbase(ksrc, kfo[I - V_INSTR], kl + (I - V_INSTR) * 1024);
+    };
+
+    // visible window of block j+1 (masked flavour only)
+    const Window w_next = window(kb0 + j + 1);
+
+    u32x4_t kfr[NQK];    // K fragments, one per QK slot
+    u32x4_t vfr[NPV];    // V^T fragments, one per PV slot
+    u32x4_t pf[4];       // packed P of block j, one per 16-key chunk
+    float pend = 0.f;    // first value of a pair awaiting its partner
+    float bmax = -INFINITY;
+    // LDS reads of slot N (issued kPD slots ahead of its MFMA)
+    auto read = [&](auto n_tag) __attribute__((always_inline)) {
+      constexpr int N = decltype(n_tag)::value;
+      if constexpr (N < NQK) {
+        if constexpr (NEXT) kfr[N] = ds_read_b128_at<KB_NEXT + (N % 2) * 32 * KROW>(koff[N / 2]);
+      } else if constexpr (N < NSLOT) {
+        constexpr int m = N - NQK, c = m / NT, t = m % NT;
+        const u32x2_t lo = ds_read_tr16_at<VB_CUR + 16 * c * VROW>(voff[0][t]);
+        const u32x2_t hi = ds_read_tr16_at<VB_CUR + 16 * c * VROW>(voff[1][t]);
+        vfr[m] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      }
+    };
+    auto expv = [&](float x) __attribute__((always_inline)) -> float {
+      return MCUR ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, s2, -m_sub));
+    };
+    auto maxv = [&](int t, int r) __attribute__((always_inline)) {
+      if constexpr (MNEXT) {
+        const int pos = 32 * t + 8 * (r >> 2) + (r & 3);
+        const float x = (pos >= w_next.lo && pos <= w_next.hi) ? s_nxt[t][r] * s2 : -INFINITY;
+        s_nxt[t][r] = x;
+        bmax = fmaxf(bmax, x);
       } else {
-        wait_vmcnt<V_INSTR>();
+        bmax = fmaxf(bmax, s_nxt[t][r]);
       }
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();
-    const float m_sub = softmax_max(j, s_cur, masked_tag);
-    u32x4_t pf[4];
-    // Phase fence, then the QK MFMAs of block j+1 interleaved with the
-    // exponentials of block j: after each K fragment read and MFMA the wave
-    // issues a few independent VALU instructions, which execute while the
-    // matrix core works on that MFMA.
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) qk(std::integral_constant<uint32_t, KB_NEXT>{}, s_nxt);
-    softmax_exp(s_cur, m_sub, pf, masked_tag);
-    if constexpr (NEXT) {
+    };
+    auto slot = [&](auto n_tag) __attribute__((always_inline)) {
+      constexpr int N = decltype(n_tag)::value;
+      constexpr int LGKM = reads_ahead<NQK, NSLOT, kPD, NEXT>(N);
+      read(std::integral_constant<int, N + kPD>{});
+      if constexpr (N < NQK) {
+        if constexpr (NEXT) {
+          if constexpr (N < 2)
+            mfma_s_first<T, LGKM>(s_nxt[N % 2], kfr[N], qf[N / 2]);
+          else
+            mfma_s_acc<T, LGKM>(s_nxt[N % 2], kfr[N], qf[N / 2]);
+        }
+        // exponentials of tile 0: 16 values over the QK slots
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+        for (int r = N * 16 / NQK; r < (N + 1) * 16 / NQK; ++r) {
+          float x = s_cur[0][r];
+          pin(x);
+          const float p = expv(x);
+          if (r & 1) {
+            uint32_t pk = pack2<T>(pend, p);
+            l_run = add_pair<T>(pk, l_run);
+            pin(pk);
+            pf[r >> 3][(r & 7) >> 1] = pk;
+          } else {
+            pend = p;
+            pin(pend);
+          }
+        }
+        pin(l_run);
+        if constexpr (NEXT && N == NQK - 1) mfma_s_drain(s_nxt);
+      } else {
+        constexpr int m = N - NQK, c = m / NT, t = m % NT;
+        mfma_o_acc<T, LGKM>(acc[t], vfr[m], pf[c]);
+        if constexpr (m < EXP1_SLOTS) {
+          // exponentials of tile 1, 16 / EXP1_SLOTS values per slot
+#pragma unroll
+          for (int r = m * 16 / EXP1_SLOTS; r < (m + 1) * 16 / EXP1_SLOTS; r += 2) {
+            float x0 = s_cur[1][r], x1 = s_cur[1][r + 1];
+            pin(x0);
+            pin(x1);
+            uint32_t pk = pack2<T>(expv(x0), expv(x1));
+            l_run = add_pair<T>(pk, l_run);
+            pin(pk);
+            pf[2 + (r >> 3)][(r & 7) >> 1] = pk;
+          }
+          pin(l_run);
+        } else if constexpr (NEXT) {
+          // row max of block j+1, spread over the remaining slots
+          constexpr int q = m - EXP1_SLOTS, NQ = NPV - EXP1_SLOTS;
+          pin(bmax);
+#pragma unroll
+          for (int e = q * 32 / NQ; e < (q + 1) * 32 / NQ; ++e) maxv(e / 16, e % 16);
+          pin(bmax);
+        }
       }
-    }
+      if constexpr (NEXT && N % DSTRIDE == 0 && N / DSTRIDE < NDMA)
+        dma(std::integral_constant<int, N / DSTRIDE>{});
+    };
+
     __builtin_amdgcn_sched_barrier(0);
-    pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
+    static_for<kPD>([&](auto n) __attribute__((always_inline)) { read(n); });
+    static_for<NSLOT>([&](auto n) __attribute__((always_inline)) { slot(n); });
+    // the accumulators may be copied between registers at block boundaries:
+    // let the last P V MFMAs finish first
+    mfma_acc_drain(acc);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) __syncthreads();  // this iteration's buffers are refilled next
-  };
-  using Par0 = std::integral_constant<int, 0>;
-  using Par1 = std::integral_constant<int, 1>;
-  // Iterations [j0, j1) of one flavour, unrolled by two so that the score
-  // tiles visibly alternate (block j in sa for even j, in sb for odd j).
-  auto run = [&](int j0, int j1, auto masked_tag, auto next_tag) __attribute__((always_inline)) {
-    int j = j0;
-    if (j < j1 && (j & 1)) iteration(j++, masked_tag, next_tag, Par1{});
-    for (; j + 1 < j1; j += 2) {
-      iteration(j, masked_tag, next_tag, Par0{});
-      iteration(j + 1, masked_tag, next_tag, Par1{});
+
+    float m_next = 0.f;
+    if constexpr (NEXT) {
+      m_next = update_max(MNEXT ? bmax : bmax * s2, mnext_tag);
+      wait_vmcnt<0>();  // V(j+1), K(j+2) have landed
+      __syncthreads();  // ... for every wave, which are all past this iteration
     }
-    if (j < j1) iteration(j, masked_tag, next_tag, Par0{});
+    return m_next;
   };
 
-  // ---- K-block pipeline ---------------------------------------------------
   using Unmasked = std::false_type;
   using Masked = std::true_type;
   using Next = std::true_type;
   using Last = std::false_type;
-  fill_k(0, KBUF0);
-  fill_v(0, VBUF0);
-  if (n_blocks > 1) {
-    fill_k(1, KBUF1);
-    wait_vmcnt<K_INSTR + V_INSTR>();  // K(0) has landed
-  } else {
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  float m_sub = 0.f;  // subtrahend of the block whose scores are in registers
+  // Iterations [j0, j1) of one flavour, unrolled by two so that the score
+  // tiles visibly alternate (block j in sa for even j, in sb for odd j).
+  auto run = [&](int j0, int j1, auto mcur_tag, auto mnext_tag) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) {
+      m_sub = iteration(j, m_sub, mcur_tag, mnext_tag, Next{}, Par1{});
+      ++j;
+    }
+    for (; j + 1 < j1; j += 2) {
+      m_sub = iteration(j, m_sub, mcur_tag, mnext_tag, Next{}, Par0{});
+      m_sub = iteration(j + 1, m_sub, mcur_tag, mnext_tag, Next{}, Par1{});
+    }
+    if (j < j1) m_sub = iteration(j, m_sub, mcur_tag, mnext_tag, Next{}, Par0{});
+  };
+
+  // ---- K-block pipeline ---------------------------------------------------
+  // prologue: K(0) (and Q) have landed; scores and max of block 0
+  if (cnt > 1)
+    wait_vmcnt<K_INSTR + V_INSTR>();
+  else
     wait_vmcnt<V_INSTR>();
-  }
+  qf[0] = row_ok ? qf[0] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int s = 1; s < KSTEPS; ++s) qf[s] = row_ok ? qf[s] : u32x4_t{0, 0, 0, 0};
   __syncthreads();
   qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
-  __syncthreads();  // K buffer 0 is refilled by the first iteration
-  const int n_next = n_blocks - 1;  // iterations that have a next block
-  const int j_mask = min(n_full, n_next);
-  run(0, j_mask, Unmasked{}, Next{});
-  run(j_mask, n_next, Masked{}, Next{});
-  // the last block (peeled): masked unless every key of it is visible to
-  // every row, in which case the mask is a no-op
-  if (n_next & 1)
-    iteration(n_next, Masked{}, Last{}, Par1{});
-  else
-    iteration(n_next, Masked{}, Last{}, Par0{});
+  // first block: O and l are still zero, so the running max is simply set
+  if (n_unmasked > 0) {
+    m_run = pair_max(block_max(0, sa, Unmasked{}));
+    m_sub = m_run;
+  } else {
+    m_run = pair_max(block_max(0, sa, Masked{}));
+    m_sub = m_run == -INFINITY ? 0.f : m_run;
+  }
+  wait_vmcnt<0>();  // V(0), K(1)
+  __syncthreads();  // and every wave is past its reads of K buffer 0
+
+  // iterations with a next block: [0, cnt-1); block j is masked iff j >= u
+  const int n_next = cnt - 1;
+  const int u = n_unmasked;
+  const int ju = min(max(u - 1, 0), n_next);  // last iteration with both blocks unmasked, + 1
+  run(0, ju, Unmasked{}, Unmasked{});
+  if (ju < n_next && ju < u) {   // block ju unmasked, block ju+1 masked
+    if (ju & 1)
+      m_sub = iteration(ju, m_sub, Unmasked{}, Masked{}, Next{}, Par1{});
+    else
+      m_sub = iteration(ju, m_sub, Unmasked{}, Masked{}, Next{}, Par0{});
+    run(ju + 1, n_next, Masked{}, Masked{});
+  } else {
+    run(ju, n_next, Masked{}, Masked{});
+  }
+  // the last block (peeled)
+  if (n_next < u) {
+    if (n_next & 1)
+      iteration(n_next, m_sub, Unmasked{}, Unmasked{}, Last{}, Par1{});
+    else
+      iteration(n_next, m_sub, Unmasked{}, Unmasked{}, Last{}, Par0{});
+  } else {
+    if (n_next & 1)
+      iteration(n_next, m_sub, Masked{}, Masked{}, Last{}, Par1{});
+    else
+      iteration(n_next, m_sub, Masked{}, Masked{}, Last{}, Par0{});
+  }
+
+  mfma_acc_drain(acc);  // the last P V MFMAs have written the accumulators
+  // ---- merge of the two key ranges (range 1 -> LDS -> range 0) -------------
+  if constexpr (KS == 2) {
+    __syncthreads();  // every wave is past its last LDS read
+    // per wave of range 1: NT*16 accumulators + (m, l) per lane, stored as
+    // 16-byte lane-major rows (conflict-free)
+    constexpr int XROWS = NT * 4 + 1;
+    SDPA_LDS f32x4_t* xb = (SDPA_LDS f32x4_t*)((SDPA_LDS char*)smem) + wis * XROWS * 64 + lane;
+    if (kr_i == 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xb[(t * 4 + q4) * 64] = f32x4_t{acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]};
+      xb[NT * 4 * 64] = f32x4_t{m_run, l_run, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (kr_i == 1) return;
+    const f32x4_t ml = xb[NT * 4 * 64];
+    const float m1 = ml[0], l1 = ml[1];
+    const float mm = fmaxf(m_run, m1);
+    const float w0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
+    const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+    l_run = l_run * w0 + l1 * w1;
+    m_run = mm;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t o1 = xb[(t * 4 + q4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][4 * q4 + e] = acc[t][4 * q4 + e] * w0 + o1[e] * w1;
+      }
+  }
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------
   const float l_tot = pair_sum(l_run);
@@ -416,22 +618,27 @@ void prefill_kernel(const PrefillArgs a) {
   }
 }
 
-template <class T, int D>
-static int launch_one(const PrefillArgs& a, int causal, ihipStream_t* stream) {
+template <class T, int D, int KS>
+static int launch_ks(const PrefillArgs& a, int causal, ihipStream_t* stream) {
   dim3 grid(a.num_groups), block(64 * kPrefillWaves);
   if (causal)
-    hipLaunchKernelGGL((prefill_kernel<T, D, D, true>), grid, block, 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, true, KS>), grid, block, 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, D, false>), grid, block, 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, false, KS>), grid, block, 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
+}
+
+template <class T, int D>
+static int launch_one(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
+  return plan.num_splits == 2 ? launch_ks<T, D, 2>(a, causal, stream) : launch_ks<T, D, 1>(a, causal, stream);
 }
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
   switch (plan.kernel) {
-    case kPrefillF16D64: return launch_one<F16, 64>(a, causal, stream);
-    case kPrefillBf16D64: return launch_one<Bf16, 64>(a, causal, stream);
-    case kPrefillF16D128: return launch_one<F16, 128>(a, causal, stream);
-    case kPrefillBf16D128: return launch_one<Bf16, 128>(a, causal, stream);
+    case kPrefillF16D64: return launch_one<F16, 64>(a, plan, causal, stream);
+    case kPrefillBf16D64: return launch_one<Bf16, 64>(a, plan, causal, stream);
+    case kPrefillF16D128: return launch_one<F16, 128>(a, plan, causal, stream);
+    case kPrefillBf16D128: return launch_one<Bf16, 128>(a, plan, causal, stream);
     case kPrefillFp8D192: return launch_prefill_fp8(a, causal, stream);
     case kWideF16D64:
     case kWideBf16D64:

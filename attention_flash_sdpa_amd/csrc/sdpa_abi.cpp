@@ -37,7 +37,12 @@ int device_cus() {
 // choice (for tuning sweeps); unset or anything else keeps the planner's.
 int prefill_variant() {
   const char* e = getenv("SDPA_PREFILL_VARIANT");
-  return (e && !strcmp(e, "narrow")) ? 1 : (e && !strcmp(e, "wide")) ? 2 : 0;
+  if (e == nullptr) return 0;
+  if (!strcmp(e, "narrow")) return 1;
+  if (!strcmp(e, "wide")) return 2;
+  if (!strcmp(e, "narrow1")) return 3;
+  if (!strcmp(e, "narrow2")) return 4;
+  return 0;
 }
 
 sdpa_status_t hip_status(int err, const char* what) {

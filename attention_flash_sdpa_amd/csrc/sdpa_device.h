@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sdpa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -35,6 +37,16 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 
 #define SDPA_LDS __attribute__((address_space(3)))
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (compile-time
+// unrolled; every index is a constant expression inside f).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -69,6 +81,93 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// ---- hand-ordered building blocks of the prefill mainloop ----------------
+// The mainloop issues its LDS fragment reads and its MFMAs from inline
+// assembly so that their order, and with it the read-ahead distance, is the
+// one written; the compiler keeps register allocation and the vector math in
+// between.  Everything the compiler would otherwise insert for these
+// instructions is explicit here:
+//  * the LDS wait: each MFMA waits until at most LGKM LDS reads of this wave
+//    are in flight (LDS reads complete in order, so the reads issued after
+//    the one it needs may stay outstanding);
+//  * two wait states before an MFMA whose inputs a vector instruction may
+//    just have written (P V only; the Q K inputs come from LDS or registers
+//    written long before);
+//  * mfma_acc_drain(): >= 18 wait states after the last P V MFMA before any
+//    other instruction touches the accumulators.
+template <int OFF>
+__device__ __forceinline__ u32x4_t ds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// c = A B (C = 0) / c += A B, scores in VGPRs
+template <class T, int LGKM>
+__device__ __forceinline__ void mfma_s_first(f32x16_t& c, u32x4_t a, u32x4_t b) {
+  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
+  if constexpr (T::is_bf16)
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                 : "=&v"(c) : "v"(a), "v"(b), "i"(LGKM));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0"
+                 : "=&v"(c) : "v"(a), "v"(b), "i"(LGKM));
+}
+template <class T, int LGKM>
+__device__ __forceinline__ void mfma_s_acc(f32x16_t& c, u32x4_t a, u32x4_t b) {
+  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
+  if constexpr (T::is_bf16)
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+v"(c) : "v"(a), "v"(b), "i"(LGKM));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                 : "+v"(c) : "v"(a), "v"(b), "i"(LGKM));
+}
+
+// acc += A B with the accumulators in AGPRs (touched only by the matrix core
+// inside the loop, which leaves the VGPRs to scores, fragments and softmax)
+template <class T, int LGKM>
+__device__ __forceinline__ void mfma_o_acc(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
+  if constexpr (T::is_bf16)
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                 : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
+}
+
+template <int NT>
+__device__ __forceinline__ void mfma_acc_drain(f32x16_t (&acc)[NT]) {
+  if constexpr (NT == 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]));
+}
+
+// >= 18 wait states after the last Q K MFMA of a block before any other
+// instruction reads the two score tiles it wrote
+__device__ __forceinline__ void mfma_s_drain(f32x16_t (&sc)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc[0]), "+v"(sc[1]));
+}
+
+// Ties a value to this point of the instruction order: instructions that use
+// the pinned value come after it, and (pinned at the end of a step) its
+// producers come before it.  Emits nothing.
+template <class V>
+__device__ __forceinline__ void pin(V& v) {
+  asm volatile("" : "+v"(v));
 }
 
 template <class T>

@@ -40,7 +40,8 @@ constexpr int kDefaultCUs = 256;
 // Validates the problem; fills *plan.  Writes a detail message through
 // set_error() on failure.  Pure host code.
 // variant: 0 = planner's choice, 1 = force the 32-row prefill kernel,
-// 2 = force the wide (64-row) prefill kernel (tuning sweeps only).
+// 2 = force the wide (64-row) prefill kernel, 3 / 4 = the 32-row kernel with
+// one / two key ranges per workgroup (tuning sweeps and tests only).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan, int variant = 0);
 

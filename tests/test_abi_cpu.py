@@ -97,11 +97,14 @@ def _problem(w: inputs.Workload, **over):
 def test_plans_for_workloads():
     W = inputs.WORKLOADS
     p = sdpa.plan(_problem(W["gqa_causal_prefill_bf16"]))
-    assert (p.rows_per_wave, p.heads_per_group, p.block_q, p.block_k, p.q_tiles, p.kv_blocks) == (32, 4, 32, 64, 16, 16)
-    assert p.num_groups == 8 * 16 and p.workspace_bytes == 0 and p.lds_bytes == 65536
+    # 4 heads x 1 tile would give 128 workgroups (< 256 CUs): the key range of
+    # each workgroup is split in two, 2 heads x 2 ranges
+    assert (p.rows_per_wave, p.heads_per_group, p.block_q, p.block_k, p.q_tiles, p.kv_blocks) == (32, 2, 32, 64, 16, 16)
+    assert p.num_splits == 2 and p.num_groups == 8 * 2 * 16 and p.workspace_bytes == 0 and p.lds_bytes == 131072
+    assert sdpa.plan(_problem(W["gqa_causal_prefill_bf16"]), num_cus=128).num_splits == 1
     p = sdpa.plan(_problem(W["unaligned_full_bf16"]))
     assert (p.rows_per_wave, p.heads_per_group, p.qtiles_per_group, p.q_tiles, p.block_k) == (32, 1, 4, 8, 64)
-    assert p.num_groups == 2 * 4 * 7 * 8
+    assert p.num_groups == 2 * 4 * 7 * 8 and p.num_splits == 1
     p = sdpa.plan(_problem(W["tiny_causal_bf16"]))
     assert (p.heads_per_group, p.q_tiles, p.num_groups) == (4, 1, 2 * 4 * 2)
     d = sdpa.plan(_problem(W["splitkv_decode_bf16"]), decode=True, num_cus=256)
@@ -118,6 +121,12 @@ def test_prefill_variant_override(monkeypatch):
     assert (pw.rows_per_wave, pw.block_k, pw.block_q, pw.q_tiles) == (64, 32, 64, 8)
     monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow")
     assert sdpa.plan(_problem(inputs.WORKLOADS["unaligned_full_bf16"])).rows_per_wave == 32
+    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow1")
+    p1 = sdpa.plan(_problem(w))
+    assert (p1.num_splits, p1.heads_per_group, p1.num_groups, p1.lds_bytes) == (1, 4, 128, 65536)
+    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow2")
+    p2 = sdpa.plan(_problem(inputs.WORKLOADS["unaligned_full_bf16"]))
+    assert (p2.num_splits, p2.heads_per_group, p2.qtiles_per_group, p2.num_groups) == (2, 1, 2, 2 * 4 * 7 * 16)
     monkeypatch.delenv("SDPA_PREFILL_VARIANT")
     assert sdpa.plan(_problem(w)).rows_per_wave == 32
 

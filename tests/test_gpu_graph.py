@@ -46,7 +46,8 @@ def _replays_match(dev, call, out, n_calls, replays=3):
         g.replay()
         torch.cuda.synchronize()
         same = torch.equal(out, want)
-        _say(f"  replay {r}: bit-identical={same}")
+        diff = (out.float() - want.float()).abs()
+        _say(f"  replay {r}: bit-identical={same} differing={int((diff > 0).sum())} max_abs_diff={float(diff.max()):.3e}")
         assert same, f"replay {r} differs from the eager call"
 
 

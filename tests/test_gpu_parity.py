@@ -160,13 +160,17 @@ EDGE = [
     (1, 129, 1, 7, 7, 128, torch.bfloat16, False),
     (1, 40, 520, 12, 4, 128, torch.bfloat16, True),
     (1, 256, 777, 5, 5, 64, torch.bfloat16, True),
+    (1, 300, 130, 4, 2, 128, torch.bfloat16, True),   # 3 key blocks, many empty rows
+    (1, 64, 192, 2, 1, 64, torch.float16, False),     # 3 whole key blocks
+    (2, 96, 64, 2, 2, 128, torch.float16, True),      # one key block
 ]
 
 
-@pytest.mark.parametrize("variant", ["narrow", "wide"])
+@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "wide"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}_q{c[1]}_k{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_{str(c[6])[6:]}_{'c' if c[7] else 'f'}" for c in EDGE])
 def test_prefill_edge_shapes(dev, oracle_mod, case, variant, monkeypatch):
-    """Every edge shape through both prefill kernels (32-row and 64-row waves)."""
+    """Every edge shape through both prefill kernels (32-row waves with one or
+    two key ranges per workgroup, and 64-row waves)."""
     monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
     B, Sq, Sk, Hq, Hkv, D, dt, causal = case
     g = torch.Generator().manual_seed(Sq * 1000 + Sk)
