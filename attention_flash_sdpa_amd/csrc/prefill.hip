@@ -168,46 +168,34 @@ void prefill_kernel(const PrefillArgs a) {
   auto row0_of = [&](int kb) __attribute__((always_inline)) -> int {
     return whole_tail ? min(kb * BK, Sk - BK) : kb * BK;
   };
-  auto fill_k = [&](int j, uint32_t buf) __attribute__((always_inline)) {
+  // one fill instruction i of block j of this range into LDS buffer buf
+  auto fill_k1 = [&](int j, uint32_t buf, int i) __attribute__((always_inline)) {
     const int kb = kb0 + j;
-    const uint32_t l = lds0 + buf + wis * K_INSTR * 1024;
-    if (whole_tail) {
-      const char* base = kg + (size_t)row0_of(kb) * kstride;
-#pragma unroll
-      for (int i = 0; i < K_INSTR; ++i) global_to_lds_16_sbase(base, kfo[i], l + i * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < K_INSTR; ++i)
-        global_to_lds_16_sbase(kg, (uint32_t)(min(kb * BK + krow[i], last_key) * kstride) + kch[i], l + i * 1024);
-    }
+    const uint32_t l = lds0 + buf + (wis * K_INSTR + i) * 1024;
+    if (whole_tail)
+      global_to_lds_16_sbase(kg + (size_t)row0_of(kb) * kstride, kfo[i], l);
+    else
+      global_to_lds_16_sbase(kg, (uint32_t)(min(kb * BK + krow[i], last_key) * kstride) + kch[i], l);
   };
-  auto fill_v = [&](int j, uint32_t buf) __attribute__((always_inline)) {
+  auto fill_v1 = [&](int j, uint32_t buf, int i) __attribute__((always_inline)) {
     const int kb = kb0 + j;
-    const uint32_t l = lds0 + buf + wis * V_INSTR * 1024;
-    if (whole_tail) {
-      const char* base = vg + (size_t)row0_of(kb) * vstride;
-#pragma unroll
-      for (int i = 0; i < V_INSTR; ++i) global_to_lds_16_sbase(base, vfo[i], l + i * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < V_INSTR; ++i)
-        global_to_lds_16_sbase(vg, (uint32_t)(min(kb * BK + vrow[i], last_key) * vstride) + vch[i], l + i * 1024);
-    }
+    const uint32_t l = lds0 + buf + (wis * V_INSTR + i) * 1024;
+    if (whole_tail)
+      global_to_lds_16_sbase(vg + (size_t)row0_of(kb) * vstride, vfo[i], l);
+    else
+      global_to_lds_16_sbase(vg, (uint32_t)(min(kb * BK + vrow[i], last_key) * vstride) + vch[i], l);
   };
 
-  // first K block, then Q (registers), then the first V block and the next K
-  // block: one wait covers K(0) and Q
-  fill_k(0, KBUF0);
-
-  // ---- Q fragments (B operand of S^T = K Q^T), loaded once ---------------
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once, then K(0) ------
+  // (V(0) and K(1) are loaded during the first block's QK MFMAs)
   u32x4_t qf[KSTEPS];
   {
     const elem_t* qptr = (const elem_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * hl;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4_t*)(qptr + 16 * s);
   }
-  fill_v(0, VBUF0);
-  if (cnt > 1) fill_k(1, KBUF1);
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) fill_k1(0, KBUF0, i);
 
   // ---- per-lane LDS read offsets -----------------------------------------
   // K fragment (A operand): key row l%32 (+32 for the second score tile),
@@ -338,9 +326,11 @@ void prefill_kernel(const PrefillArgs a) {
   // and, every few slots, one of the direct loads of V(j+1) / K(j+2) into the
   // buffers the previous iteration freed.  The vector work is spread so that
   // it runs under the matrix core:
-  //   QK slots:       exponentials of score tile 0 of block j
-  //   PV slots of chunks 0, 1: exponentials of score tile 1 (chunks 2, 3)
-  //   last PV slots:  row max of block j+1
+  //   QK slots:          exponentials of score tile 0 of block j and of the
+  //                      first half of tile 1
+  //   first half of PV:  exponentials of the rest of tile 1 (chunk 3, used
+  //                      from the last quarter of the PV slots on)
+  //   second half of PV: row max of block j+1
   // A scheduling fence closes each slot, so the order is the one written.
   constexpr int NQK = 2 * KSTEPS;               // QK slots
   constexpr int NPV = 4 * NT;                   // PV slots
@@ -348,9 +338,7 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int kPD = 4;                        // read-ahead distance (slots)
   constexpr int NDMA = K_INSTR + V_INSTR;
   constexpr int DSTRIDE = NSLOT / NDMA > 0 ? NSLOT / NDMA : 1;
-  constexpr int EXP1_SLOTS = 2 * NT;            // PV slots of chunks 0, 1
-  static_assert(16 % EXP1_SLOTS == 0 && (16 / EXP1_SLOTS) % 2 == 0, "tile-1 exponentials in pairs");
-  static_assert(NPV - EXP1_SLOTS > 0, "room for the row max");
+  static_assert(NQK % 8 == 0 && NPV % 4 == 0, "slot counts");
 
   auto iteration = [&](int j, float m_sub, auto mcur_tag, auto mnext_tag, auto next_tag, auto par_tag)
       __attribute__((always_inline)) -> float {
@@ -390,7 +378,6 @@ void prefill_kernel(const PrefillArgs a) {
     u32x4_t kfr[NQK];    // K fragments, one per QK slot
     u32x4_t vfr[NPV];    // V^T fragments, one per PV slot
     u32x4_t pf[4];       // packed P of block j, one per 16-key chunk
-    float pend = 0.f;    // first value of a pair awaiting its partner
     float bmax = -INFINITY;
     // LDS reads of slot N (issued kPD slots ahead of its MFMA)
     auto read = [&](auto n_tag) __attribute__((always_inline)) {
@@ -417,6 +404,29 @@ void prefill_kernel(const PrefillArgs a) {
         bmax = fmaxf(bmax, s_nxt[t][r]);
       }
     };
+    // exponentials of score tile TL, values [R0, R1): pairs are packed into
+    // the PV operand of their 16-key chunk and added to the row sum
+    float pend[2] = {0.f, 0.f};  // even value of a pair awaiting its partner
+    auto exp_range = [&](auto tl_tag, auto r0_tag, auto r1_tag) __attribute__((always_inline)) {
+      constexpr int TL = decltype(tl_tag)::value;
+      constexpr int R0 = decltype(r0_tag)::value, R1 = decltype(r1_tag)::value;
+#pragma unroll
+      for (int r = R0; r < R1; ++r) {
+        float x = s_cur[TL][r];
+        pin(x);
+        const float p = expv(x);
+        if (r & 1) {
+          uint32_t pk = pack2<T>(pend[TL], p);
+          l_run = add_pair<T>(pk, l_run);
+          pin(pk);
+          pf[2 * TL + (r >> 3)][(r & 7) >> 1] = pk;
+        } else {
+          pend[TL] = p;
+          pin(pend[TL]);
+        }
+      }
+      if constexpr (R1 > R0) pin(l_run);
+    };
     auto slot = [&](auto n_tag) __attribute__((always_inline)) {
       constexpr int N = decltype(n_tag)::value;
       constexpr int LGKM = reads_ahead<NQK, NSLOT, kPD, NEXT>(N);
@@ -428,46 +438,26 @@ void prefill_kernel(const PrefillArgs a) {
           else
             mfma_s_acc<T, LGKM>(s_nxt[N % 2], kfr[N], qf[N / 2]);
         }
-        // exponentials of tile 0: 16 values over the QK slots
-#pragma unroll
-        for (int r = N * 16 / NQK; r < (N + 1) * 16 / NQK; ++r) {
-          float x = s_cur[0][r];
-          pin(x);
-          const float p = expv(x);
-          if (r & 1) {
-            uint32_t pk = pack2<T>(pend, p);
-            l_run = add_pair<T>(pk, l_run);
-            pin(pk);
-            pf[r >> 3][(r & 7) >> 1] = pk;
-          } else {
-            pend = p;
-            pin(pend);
-          }
-        }
-        pin(l_run);
+        // exponentials of tile 0 (all) and of the first half of tile 1
+        exp_range(std::integral_constant<int, 0>{}, std::integral_constant<int, N * 16 / NQK>{},
+                  std::integral_constant<int, (N + 1) * 16 / NQK>{});
+        exp_range(std::integral_constant<int, 1>{}, std::integral_constant<int, N * 8 / NQK>{},
+                  std::integral_constant<int, (N + 1) * 8 / NQK>{});
         if constexpr (NEXT && N == NQK - 1) mfma_s_drain(s_nxt);
       } else {
         constexpr int m = N - NQK, c = m / NT, t = m % NT;
         mfma_o_acc<T, LGKM>(acc[t], vfr[m], pf[c]);
-        if constexpr (m < EXP1_SLOTS) {
-          // exponentials of tile 1, 16 / EXP1_SLOTS values per slot
-#pragma unroll
-          for (int r = m * 16 / EXP1_SLOTS; r < (m + 1) * 16 / EXP1_SLOTS; r += 2) {
-            float x0 = s_cur[1][r], x1 = s_cur[1][r + 1];
-            pin(x0);
-            pin(x1);
-            uint32_t pk = pack2<T>(expv(x0), expv(x1));
-            l_run = add_pair<T>(pk, l_run);
-            pin(pk);
-            pf[2 + (r >> 3)][(r & 7) >> 1] = pk;
-          }
-          pin(l_run);
+        constexpr int H = NPV / 2;
+        if constexpr (m < H) {
+          // second half of tile 1 (chunk 3 is used from slot 3*NT on)
+          exp_range(std::integral_constant<int, 1>{}, std::integral_constant<int, 8 + m * 8 / H>{},
+                    std::integral_constant<int, 8 + (m + 1) * 8 / H>{});
         } else if constexpr (NEXT) {
-          // row max of block j+1, spread over the remaining slots
-          constexpr int q = m - EXP1_SLOTS, NQ = NPV - EXP1_SLOTS;
+          // row max of block j+1 over the remaining slots
+          constexpr int q = m - H;
           pin(bmax);
 #pragma unroll
-          for (int e = q * 32 / NQ; e < (q + 1) * 32 / NQ; ++e) maxv(e / 16, e % 16);
+          for (int e = q * 32 / H; e < (q + 1) * 32 / H; ++e) maxv(e / 16, e % 16);
           pin(bmax);
         }
       }
@@ -515,16 +505,42 @@ void prefill_kernel(const PrefillArgs a) {
   };
 
   // ---- K-block pipeline ---------------------------------------------------
-  // prologue: K(0) (and Q) have landed; scores and max of block 0
-  if (cnt > 1)
-    wait_vmcnt<K_INSTR + V_INSTR>();
-  else
-    wait_vmcnt<V_INSTR>();
+  // prologue: Q and K(0) have landed; scores and max of block 0, with the
+  // loads of V(0) and K(1) (block 0 again when there is no block 1, into a
+  // buffer nothing reads) issued between the QK MFMAs
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) fill_v1(0, VBUF0, i);
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) fill_k1(min(1, cnt - 1), KBUF1, i);
   qf[0] = row_ok ? qf[0] : u32x4_t{0, 0, 0, 0};
 #pragma unroll
   for (int s = 1; s < KSTEPS; ++s) qf[s] = row_ok ? qf[s] : u32x4_t{0, 0, 0, 0};
   __syncthreads();
-  qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
+  {
+    constexpr int NQK0 = 2 * KSTEPS, PD = 4;
+    constexpr int NF = V_INSTR + K_INSTR, FSTRIDE = NQK0 / NF > 0 ? NQK0 / NF : 1;
+    const int j1 = min(1, cnt - 1);
+    u32x4_t kfr0[NQK0];
+    auto rd = [&](auto n_tag) __attribute__((always_inline)) {
+      constexpr int N = decltype(n_tag)::value;
+      if constexpr (N < NQK0) kfr0[N] = ds_read_b128_at<KBUF0 + (N % 2) * 32 * KROW>(koff[N / 2]);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<PD>([&](auto n) __attribute__((always_inline)) { rd(n); });
+    static_for<NQK0>([&](auto n) __attribute__((always_inline)) {
+      constexpr int N = decltype(n)::value;
+      constexpr int LGKM = (NQK0 - 1 - N) < PD ? (NQK0 - 1 - N) : PD;
+      rd(std::integral_constant<int, N + PD>{});
+      if constexpr (N < 2)
+        mfma_s_first<T, LGKM>(sa[N % 2], kfr0[N], qf[N / 2]);
+      else
+        mfma_s_acc<T, LGKM>(sa[N % 2], kfr0[N], qf[N / 2]);
+      (void)FSTRIDE;
+    });
+    mfma_s_drain(sa);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // first block: O and l are still zero, so the running max is simply set
   if (n_unmasked > 0) {
     m_run = pair_max(block_max(0, sa, Unmasked{}));
