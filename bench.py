@@ -135,8 +135,10 @@ def _kernels_of(sdpa, w, num_cus=256):
                 (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 64)]
     if w.dtype == "fp8_e4m3":
         return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
-    fam = "prefill_wide_kernel" if p.rows_per_wave == 64 else "prefill_kernel"
-    return [(f"{fam}<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
+    if p.rows_per_wave == 64:
+        return [(f"prefill_wide_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
+    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}>",
+             p.num_groups * p.waves_per_group * 64)]
 
 
 # kernel-source files whose text decides each profiled kernel's code
