@@ -212,6 +212,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   }
 }
 
+// splits combined from registers in one pass (more use the looped path)
+constexpr int kCombineFast = 32;
+
 template <class T, int DV>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int PER = DV / 64;   // value columns per lane (contiguous)
@@ -223,7 +226,41 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   const float* ml = a.part_ml + (size_t)bh * S * 2;
   const float* po = a.part_o + (size_t)bh * S * DV + PER * lane;
 
-  // global max over splits (lane s covers splits s, s+64, ...)
+  if (S <= kCombineFast) {
+    // Every lane loads all (m, l) pairs (one cache line, broadcast) and its
+    // columns of every partial row at once, then combines in registers: no
+    // cross-lane reduction, one memory round trip.
+    f32x2_t mlv[kCombineFast];
+    vec_t vals[kCombineFast];
+#pragma unroll
+    for (int u = 0; u < kCombineFast; ++u) mlv[u] = u < S ? *(const f32x2_t*)(ml + 2 * u) : f32x2_t{-INFINITY, 0.f};
+#pragma unroll
+    for (int u = 0; u < kCombineFast; ++u) vals[u] = u < S ? *(const vec_t*)(po + (size_t)u * DV) : (vec_t)0.f;
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kCombineFast; ++u) M = fmaxf(M, mlv[u][0]);
+    const float m_sub = M == -INFINITY ? 0.f : M;
+    float den = 0.f;
+    vec_t num = (vec_t)0.f;
+#pragma unroll
+    for (int u = 0; u < kCombineFast; ++u) {
+      const float mu = mlv[u][0], lu = mlv[u][1];
+      const float w = u < S ? fast_exp2(mu - m_sub) : 0.f;  // 0 for an empty split (m = -inf)
+      den += w * lu;
+      num += w * vals[u];
+    }
+    const float inv = den > 0.f ? a.v_descale / den : 0.f;
+    uint16_t* o = (uint16_t*)a.o + (size_t)bh * DV + PER * lane;
+    if constexpr (PER == 2) {
+      *(uint32_t*)o = pack2<T>(num[0] * inv, num[1] * inv);
+    } else {
+      o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
+    }
+    if (a.lse != nullptr && lane == 0) a.lse[bh] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    return;
+  }
+
+  // many splits: global max over splits (lane s covers splits s, s+64, ...)
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
