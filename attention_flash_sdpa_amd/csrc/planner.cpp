@@ -108,7 +108,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
       // default until the wide one measures faster)
       bool wide = false;
       (void)wide_waves;
-      if (variant == 1 || variant == 3 || variant == 4) wide = false;
+      if (variant == 1 || variant == 3 || variant == 4 || variant == 5) wide = false;
       if (variant == 2) wide = true;
       if (wide) {
         rows = kWideRowsPerWave;
@@ -144,12 +144,18 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // workgroup in two halves, each streamed by half of its waves and merged
     // at the end, which doubles the workgroup count.
     bool split = rows == kRowsPerWave && kid != kPrefillFp8D192 && groups < num_cus && plan->kv_blocks >= 2;
-    if (variant == 3) split = false;
+    if (variant == 3 || variant == 5) split = false;
     if (variant == 4) split = rows == kRowsPerWave && kid != kPrefillFp8D192;
     if (split) {
       ks = 2;
       groups = shape(kPrefillWaves / 2, &hp, &qtiles);
     }
+    // More workgroups than CUs: the two-waves-per-SIMD form keeps two of them
+    // on every CU at once (the one-wave form would run in rounds).
+    bool occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
+    if (variant == 3 || variant == 4) occ2 = false;
+    if (variant == 5) occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
     plan->num_splits = ks;
     plan->heads_per_group = hp;
     plan->qtiles_per_group = qtiles;

@@ -660,6 +660,10 @@ int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ih
     case kWideBf16D64:
     case kWideF16D128:
     case kWideBf16D128: return launch_prefill_wide(a, plan, causal, stream);
+    case kOccF16D64:
+    case kOccBf16D64:
+    case kOccF16D128:
+    case kOccBf16D128: return launch_prefill_o2(a, plan, causal, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -42,6 +42,7 @@ int prefill_variant() {
   if (!strcmp(e, "wide")) return 2;
   if (!strcmp(e, "narrow1")) return 3;
   if (!strcmp(e, "narrow2")) return 4;
+  if (!strcmp(e, "occ2")) return 5;
   return 0;
 }
 

@@ -21,6 +21,10 @@ enum KernelId : int32_t {
   kWideBf16D64 = 9,
   kWideF16D128 = 10,
   kWideBf16D128 = 11,
+  kOccF16D64 = 12,  // 32-row kernel, two waves per SIMD (large grids)
+  kOccBf16D64 = 13,
+  kOccF16D128 = 14,
+  kOccBf16D128 = 15,
   kDecodeF16D64 = 16,
   kDecodeBf16D64 = 17,
   kDecodeF16D128 = 18,
@@ -39,9 +43,10 @@ constexpr int kDefaultCUs = 256;
 
 // Validates the problem; fills *plan.  Writes a detail message through
 // set_error() on failure.  Pure host code.
-// variant: 0 = planner's choice, 1 = force the 32-row prefill kernel,
-// 2 = force the wide (64-row) prefill kernel, 3 / 4 = the 32-row kernel with
-// one / two key ranges per workgroup (tuning sweeps and tests only).
+// variant: 0 = planner's choice, 1 = the 32-row kernels (planner picks the
+// form), 2 = the wide (64-row) kernel, 3 / 4 = the one-wave-per-SIMD 32-row
+// kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
+// 32-row kernel (tuning sweeps and tests only).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan, int variant = 0);
 
@@ -80,6 +85,7 @@ struct DecodeArgs {
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
 int launch_prefill_wide(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 }  // namespace sdpa

@@ -135,6 +135,8 @@ def _kernels_of(sdpa, w, num_cus=256):
                 (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 64)]
     if w.dtype == "fp8_e4m3":
         return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
+    if 12 <= p.kernel <= 15:   # the two-waves-per-SIMD 32-row kernel
+        return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
     if p.rows_per_wave == 64:
         return [(f"prefill_wide_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
     return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}>",
@@ -142,7 +144,8 @@ def _kernels_of(sdpa, w, num_cus=256):
 
 
 # kernel-source files whose text decides each profiled kernel's code
-_SOURCES = {"prefill": ["prefill.hip", "prefill_wide.hip", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
+_SOURCES = {"prefill": ["prefill.hip", "prefill_o2.hip", "prefill_wide.hip", "sdpa_device.h", "sdpa_internal.h",
+                        "sdpa_bounds.h"],
             "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"]}
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
 

@@ -105,6 +105,8 @@ def test_plans_for_workloads():
     p = sdpa.plan(_problem(W["unaligned_full_bf16"]))
     assert (p.rows_per_wave, p.heads_per_group, p.qtiles_per_group, p.q_tiles, p.block_k) == (32, 1, 4, 8, 64)
     assert p.num_groups == 2 * 4 * 7 * 8 and p.num_splits == 1
+    assert p.kernel == 15   # 448 workgroups > 256 CUs: the two-waves-per-SIMD form
+    assert sdpa.plan(_problem(W["gqa_causal_prefill_bf16"])).kernel == 3
     p = sdpa.plan(_problem(W["tiny_causal_bf16"]))
     assert (p.heads_per_group, p.q_tiles, p.num_groups) == (4, 1, 2 * 4 * 2)
     d = sdpa.plan(_problem(W["splitkv_decode_bf16"]), decode=True, num_cus=256)

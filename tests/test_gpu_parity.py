@@ -166,11 +166,12 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "wide"])
+@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "wide"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}_q{c[1]}_k{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_{str(c[6])[6:]}_{'c' if c[7] else 'f'}" for c in EDGE])
 def test_prefill_edge_shapes(dev, oracle_mod, case, variant, monkeypatch):
-    """Every edge shape through both prefill kernels (32-row waves with one or
-    two key ranges per workgroup, and 64-row waves)."""
+    """Every edge shape through every 16-bit prefill kernel: 32-row waves (one
+    wave per SIMD with one or two key ranges per workgroup, two waves per
+    SIMD) and 64-row waves."""
     monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
     B, Sq, Sk, Hq, Hkv, D, dt, causal = case
     g = torch.Generator().manual_seed(Sq * 1000 + Sk)
