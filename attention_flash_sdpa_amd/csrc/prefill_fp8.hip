@@ -21,6 +21,10 @@
 //    (dims 0..127) and a 64-byte part (dims 128..191), each with a
 //    power-of-two swizzle that keeps the fragment reads free of bank
 //    conflicts.
+//  * Software pipeline as in the two-waves-per-SIMD 16-bit kernel: iteration
+//    j loads V(j+1) and K(j+2) into separate double buffers, issues the QK
+//    MFMAs of block j+1 interleaved with the exponentials of block j, then
+//    the P V MFMAs of block j; two waves per SIMD hide the rest.
 #include <math.h>
 
 #include <type_traits>
@@ -39,16 +43,20 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   constexpr int NW = kPrefillWaves;
   constexpr int KAROW = 128, KBROW = 64, VROW = 128;         // LDS bytes per key row
   constexpr int KABYTES = BK * KAROW, KBBYTES = BK * KBROW, VBYTES = BK * VROW;
-  constexpr int STAGE = KABYTES + KBBYTES + VBYTES;          // 20 KiB
+  constexpr int KBYTES = KABYTES + KBBYTES;                  // 12 KiB per K block
   constexpr int KA_INSTR = KABYTES / 1024 / NW;              // 2 per wave
   constexpr int KB_INSTR = KBBYTES / 1024 / NW;              // 1 per wave
+  constexpr int K_INSTR = KA_INSTR + KB_INSTR;
   constexpr int V_INSTR = VBYTES / 1024 / NW;                // 2 per wave
   constexpr int NT = DV / 32;                                // O^T accumulator tiles
   static_assert(KA_INSTR * NW * 1024 == KABYTES && KB_INSTR * NW * 1024 == KBBYTES &&
                     V_INSTR * NW * 1024 == VBYTES,
                 "block split into whole 1 KiB loads per wave");
+  // LDS: K buffers 0/1 (part A then part B), then V buffers 0/1
+  constexpr uint32_t KBUF0 = 0, KBUF1 = KBYTES;
+  constexpr uint32_t VBUF0 = 2 * KBYTES, VBUF1 = 2 * KBYTES + VBYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem;
 
   const int lane = __lane_id();
@@ -103,7 +111,7 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     }
   }
 
-  // ---- direct global -> LDS fill ------------------------------------------
+  // ---- direct global -> LDS fills (rows past the last key re-read it) -----
   const char* kg = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * D;
   const char* vg = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * DV;
   const int kstride = a.head_kv * D, vstride = a.head_kv * DV;  // bytes between keys
@@ -127,8 +135,8 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     v_col[i] = ((slot % 8) ^ (int)swz_prefill<8>(r)) * 16;
   }
   const int last_key = Sk - 1;
-  auto issue_fill = [&](int kb, int stage) __attribute__((always_inline)) {
-    const uint32_t base = lds0 + stage * STAGE;
+  auto fill_k = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + buf;
 #pragma unroll
     for (int i = 0; i < KA_INSTR; ++i)
       global_to_lds_16(kg + (size_t)min(kb * BK + ka_row[i], last_key) * kstride + ka_col[i],
@@ -137,10 +145,13 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     for (int i = 0; i < KB_INSTR; ++i)
       global_to_lds_16(kg + (size_t)min(kb * BK + kb_row[i], last_key) * kstride + kb_col[i],
                        base + KABYTES + (wave * KB_INSTR + i) * 1024);
+  };
+  auto fill_v = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + buf;
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i)
       global_to_lds_16(vg + (size_t)min(kb * BK + v_row[i], last_key) * vstride + v_col[i],
-                       base + KABYTES + KBBYTES + (wave * V_INSTR + i) * 1024);
+                       base + (wave * V_INSTR + i) * 1024);
   };
 
   // ---- per-lane LDS read offsets -----------------------------------------
@@ -152,9 +163,10 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      ka_off[s][c] = l32 * KAROW + (((4 * s + 2 * hl + c) ^ (int)swz_prefill<8>(l32)) << 4);
+      ka_off[s][c] = lds0 + l32 * KAROW + (((4 * s + 2 * hl + c) ^ (int)swz_prefill<8>(l32)) << 4);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) kb_off[c] = KABYTES + l32 * KBROW + (((2 * hl + c) ^ (int)swz_quarter(l32)) << 4);
+  for (int c = 0; c < 2; ++c)
+    kb_off[c] = lds0 + KABYTES + l32 * KBROW + (((2 * hl + c) ^ (int)swz_quarter(l32)) << 4);
   // V^T fragment (A operand of the bf16 32x32x16 MFMA) via ds_read_b64_tr_b8:
   // lane (group gq = l/16, s = l%16) addresses key row 8*(r/4) + 4*(gq/2) +
   // r%4 with r = s/2 (+16 per key chunk) and value bytes 32t + 16*(gq%2) +
@@ -167,7 +179,7 @@ void prefill_fp8_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int col = 32 * t + 16 * (gq & 1) + 8 * (s & 1);
-      v_off[t] = KABYTES + KBBYTES + row * VROW + ((((col >> 4) ^ (int)swz_prefill<8>(row))) << 4) + (col & 15);
+      v_off[t] = lds0 + row * VROW + ((((col >> 4) ^ (int)swz_prefill<8>(row))) << 4) + (col & 15);
     }
   }
 
@@ -179,37 +191,42 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float s2 = a.s2;
+  f32x16_t sa[2], sb[2];  // score tiles of two consecutive blocks
 
-  auto block = [&](int kb, int stage, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const uint32_t base = lds0 + stage * STAGE;
-
-    // GEMM 1 (fp8): S^T[key][query], three k-steps of 64 head dims
-    f32x16_t sc[2];
+  // GEMM 1 (fp8): S^T[key][query] of the block in K buffer KB, three k-steps
+  // of 64 head dims per 32-key score tile
+  auto qk = [&](auto kb_tag, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
+    constexpr uint32_t KB = decltype(kb_tag)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sc[0][r] = 0.f;
       sc[1][r] = 0.f;
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int s = 0; s < 3; ++s)
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
+      for (int t = 0; t < 2; ++t) {
         u32x4_t x0, x1;
         if (s < 2) {
-          x0 = lds_read_b128(base + ka_off[s][0] + 32 * t * KAROW);
-          x1 = lds_read_b128(base + ka_off[s][1] + 32 * t * KAROW);
+          x0 = lds_read_b128(ka_off[s][0] + KB + 32 * t * KAROW);
+          x1 = lds_read_b128(ka_off[s][1] + KB + 32 * t * KAROW);
         } else {
-          x0 = lds_read_b128(base + kb_off[0] + 32 * t * KBROW);
-          x1 = lds_read_b128(base + kb_off[1] + 32 * t * KBROW);
+          x0 = lds_read_b128(kb_off[0] + KB + 32 * t * KBROW);
+          x1 = lds_read_b128(kb_off[1] + KB + 32 * t * KBROW);
         }
         const i32x8_t kf = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         sc[t] = mfma32x32x64_fp8(kf, qf[s], sc[t]);
       }
-    }
+  };
 
+  // Softmax part 1: mask (tail blocks only), block row max, lazy rescale
+  // (the running max only moves when it grows by more than kSlack, so
+  // P <= 2^kSlack; O / l is unchanged because l sums the same P values).
+  auto softmax_max = [&](int kb, f32x16_t (&sc)[2], auto masked_tag) __attribute__((always_inline)) -> float {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     float bmax;
     if constexpr (MASKED) {
+      // register r of tile t holds key kb*BK + 4*hl + 32t + 8(r/4) + r%4
       const int lim = (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl);
       bmax = -INFINITY;
 #pragma unroll
@@ -240,9 +257,14 @@ void prefill_fp8_kernel(const PrefillArgs a) {
         for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
       m_run = m_new;
     }
-    const float m_sub = MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+    return MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+  };
 
-    u32x4_t pf[4];
+  // Softmax part 2: P = 2^(s2*S - m), rounded to bf16 as the PV B operand;
+  // the row sum is taken over the rounded values.
+  auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], auto masked_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -259,43 +281,107 @@ void prefill_fp8_kernel(const PrefillArgs a) {
         pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
         l_run = add_pair<Bf16>(pk, l_run);
       }
+  };
 
-    // GEMM 2 (bf16): O^T += V^T P^T, V widened from fp8 after the transposed read
+  // GEMM 2 (bf16): O^T += V^T P^T from V buffer VB, V widened from fp8 after
+  // the transposed read
+  auto pv = [&](auto vb_tag, const u32x4_t (&pf)[4]) __attribute__((always_inline)) {
+    constexpr uint32_t VB = decltype(vb_tag)::value;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x2_t v8 = lds_read_tr8(base + v_off[t] + (16 * c) * VROW);
+        const u32x2_t v8 = lds_read_tr8(v_off[t] + VB + (16 * c) * VROW);
         const u32x2_t lo = fp8x4_to_bf16x4(v8.x), hi = fp8x4_to_bf16x4(v8.y);
         const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
         acc[t] = mfma32x32x16<Bf16>(vf, pf[c], acc[t]);
       }
   };
 
+  // One pipeline iteration j (PAR = j & 1): the scores of block j are in
+  // registers, K(j+1) sits in K buffer 1-PAR and V(j) in V buffer PAR.  It
+  // starts the loads of V(j+1) and K(j+2) into the buffers freed by the
+  // previous iteration, computes the scores of block j+1 interleaved with the
+  // exponentials of block j, then the P V of block j.
+  auto iteration = [&](int j, auto masked_tag, auto next_tag, auto par_tag) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr uint32_t KB_NEXT = PAR ? KBUF0 : KBUF1;   // holds K(j+1)
+    constexpr uint32_t KB_FREE = PAR ? KBUF1 : KBUF0;   // receives K(j+2)
+    constexpr uint32_t VB_CUR = PAR ? VBUF1 : VBUF0;    // holds V(j)
+    constexpr uint32_t VB_FREE = PAR ? VBUF0 : VBUF1;   // receives V(j+1)
+    f32x16_t(&s_cur)[2] = PAR ? sb : sa;
+    f32x16_t(&s_nxt)[2] = PAR ? sa : sb;
+    if constexpr (NEXT) {
+      fill_v(j + 1, VB_FREE);
+      if (j + 2 < n_blocks) {
+        fill_k(j + 2, KB_FREE);
+        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) have landed
+      } else {
+        wait_vmcnt<V_INSTR>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const float m_sub = softmax_max(j, s_cur, masked_tag);
+    u32x4_t pf[4];
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) qk(std::integral_constant<uint32_t, KB_NEXT>{}, s_nxt);
+    softmax_exp(s_cur, m_sub, pf, masked_tag);
+    if constexpr (NEXT) {
+      // per QK MFMA (64 cycles on the matrix core): its two K reads and a
+      // share of the exponentials
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // fourteen VALU
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) __syncthreads();  // this iteration's buffers are refilled next
+  };
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  auto run = [&](int j0, int j1, auto masked_tag, auto next_tag) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) iteration(j++, masked_tag, next_tag, Par1{});
+    for (; j + 1 < j1; j += 2) {
+      iteration(j, masked_tag, next_tag, Par0{});
+      iteration(j + 1, masked_tag, next_tag, Par1{});
+    }
+    if (j < j1) iteration(j, masked_tag, next_tag, Par0{});
+  };
+
+  // ---- K-block pipeline ---------------------------------------------------
   using Unmasked = std::false_type;
   using Masked = std::true_type;
-  constexpr int FILL = KA_INSTR + KB_INSTR + V_INSTR;
-
-  issue_fill(0, 0);
-  int kb = 0;
-  const int n_pref = n_blocks - 1;
-  for (; kb < min(n_full, n_pref); ++kb) {
-    issue_fill(kb + 1, (kb + 1) & 1);
-    wait_vmcnt<FILL>();
-    __syncthreads();
-    block(kb, kb & 1, Unmasked{});
-    __syncthreads();
+  using Next = std::true_type;
+  using Last = std::false_type;
+  fill_k(0, KBUF0);
+  fill_v(0, VBUF0);
+  if (n_blocks > 1) {
+    fill_k(1, KBUF1);
+    wait_vmcnt<K_INSTR + V_INSTR>();  // K(0) has landed
+  } else {
+    wait_vmcnt<V_INSTR>();
   }
-  for (; kb < n_pref; ++kb) {
-    issue_fill(kb + 1, (kb + 1) & 1);
-    wait_vmcnt<FILL>();
-    __syncthreads();
-    block(kb, kb & 1, Masked{});
-    __syncthreads();
-  }
-  wait_vmcnt<0>();
   __syncthreads();
-  block(kb, kb & 1, Masked{});
+  qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
+  __syncthreads();  // K buffer 0 is refilled by the first iteration
+  const int n_next = n_blocks - 1;  // iterations that have a next block
+  const int j_mask = min(n_full, n_next);
+  run(0, j_mask, Unmasked{}, Next{});
+  run(j_mask, n_next, Masked{}, Next{});
+  // the last block (peeled): masked unless every key of it is visible to
+  // every row, in which case the mask is a no-op
+  if (n_next & 1)
+    iteration(n_next, Masked{}, Last{}, Par1{});
+  else
+    iteration(n_next, Masked{}, Last{}, Par0{});
 
   // ---- epilogue ------------------------------------------------------------
   const float l_tot = pair_sum(l_run);
