@@ -156,6 +156,19 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     if (variant == 3 || variant == 4) occ2 = false;
     if (variant == 5) occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192;
     if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
+    // Four key ranges of 32-key blocks, two waves (heads or query tiles) per
+    // range, 8 waves per workgroup at two waves per SIMD: the same grid as the
+    // two-range split with twice the waves in flight.
+    bool split4 = false;
+    if (variant == 6) split4 = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (split4) {
+      ks = kSplitRanges;
+      groups = shape(kSplitWaves / kSplitRanges, &hp, &qtiles);
+      plan->kernel = kid - kPrefillF16D64 + kSplitF16D64;
+      plan->waves_per_group = kSplitWaves;
+      plan->block_k = kSplitBlockK;
+      plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);
+    }
     plan->num_splits = ks;
     plan->heads_per_group = hp;
     plan->qtiles_per_group = qtiles;

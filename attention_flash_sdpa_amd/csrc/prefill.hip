@@ -186,16 +186,24 @@ void prefill_kernel(const PrefillArgs a) {
       global_to_lds_16_sbase(vg, (uint32_t)(min(kb * BK + vrow[i], last_key) * vstride) + vch[i], l);
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T), loaded once, then K(0) ------
-  // (V(0) and K(1) are loaded during the first block's QK MFMAs)
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once, then K(0),
+  // V(0) and K(1) (block 0 again when there is no block 1, into a buffer
+  // nothing reads): all in flight at once, the first block's scores wait for
+  // Q and K(0) only
   u32x4_t qf[KSTEPS];
   {
     const elem_t* qptr = (const elem_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4_t*)(qptr + 16 * s);
+    static_for<KSTEPS>([&](auto s) __attribute__((always_inline)) {
+      constexpr int S = decltype(s)::value;
+      global_load_16_untracked<32 * S>(qf[S], qptr);
+    });
   }
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) fill_k1(0, KBUF0, i);
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) fill_v1(0, VBUF0, i);
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) fill_k1(min(1, cnt - 1), KBUF1, i);
 
   // ---- per-lane LDS read offsets -----------------------------------------
   // K fragment (A operand): key row l%32 (+32 for the second score tile),
@@ -505,14 +513,9 @@ void prefill_kernel(const PrefillArgs a) {
   };
 
   // ---- K-block pipeline ---------------------------------------------------
-  // prologue: Q and K(0) have landed; scores and max of block 0, with the
-  // loads of V(0) and K(1) (block 0 again when there is no block 1, into a
-  // buffer nothing reads) issued between the QK MFMAs
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int i = 0; i < V_INSTR; ++i) fill_v1(0, VBUF0, i);
-#pragma unroll
-  for (int i = 0; i < K_INSTR; ++i) fill_k1(min(1, cnt - 1), KBUF1, i);
+  // prologue: once Q and K(0) have landed (V(0) and K(1) may still be in
+  // flight), the scores and max of block 0
+  wait_vmcnt_pin<V_INSTR + K_INSTR>(qf);
   qf[0] = row_ok ? qf[0] : u32x4_t{0, 0, 0, 0};
 #pragma unroll
   for (int s = 1; s < KSTEPS; ++s) qf[s] = row_ok ? qf[s] : u32x4_t{0, 0, 0, 0};
@@ -663,7 +666,11 @@ int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ih
     case kOccF16D64:
     case kOccBf16D64:
     case kOccF16D128:
-    case kOccBf16D128: return launch_prefill_o2(a, plan, causal, stream);
+    case kOccBf16D128:
+    case kSplitF16D64:
+    case kSplitBf16D64:
+    case kSplitF16D128:
+    case kSplitBf16D128: return launch_prefill_o2(a, plan, causal, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

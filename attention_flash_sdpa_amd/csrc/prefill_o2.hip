@@ -1,22 +1,29 @@
 // prefill_o2.hip -- the 32-row prefill mainloop in its two-waves-per-SIMD
-// form, for grids with more than one workgroup per CU.
+// form (at most 256 registers per wave, so two waves share each SIMD and hide
+// each other's LDS, memory and barrier latencies).
 //
 // Same method and data layout as prefill.hip ("Xe SDPA Forward Mainloop --
 // Key Loops + Shapes", sections "mainloop_body(K)", "softmax() helper" and
 // "Outer K-block loop"): S^T = K Q^T on the matrix cores, the blocked online
 // softmax with exp2 and the scale folded with log2(e), O^T += V^T P^T with P
-// kept in registers, K/V blocks of 64 keys streamed into double-buffered,
-// swizzled LDS by direct 16-byte loads, a branch-free unmasked loop and a
-// peeled masked tail.  Here the kernel keeps within 256 registers so two
-// workgroups share a CU: the second wave on each SIMD hides the LDS, memory
-// and barrier latencies that the one-wave form hides by ordering its
-// instructions, which pays off when the grid is large enough to fill both.
+// kept in registers, K/V blocks streamed into double-buffered, swizzled LDS
+// by direct 16-byte loads, a branch-free unmasked loop and a peeled masked
+// tail.  Two shapes are instantiated:
 //
-//  * Software pipeline: iteration j issues the QK MFMAs of block j+1 before
-//    the softmax of block j is finished, then runs the PV MFMAs of block j.
-//    K(j+2) and V(j+1) are loaded during iteration j.
-//  * Buffer parity is a compile-time parameter (the loop is unrolled by two),
-//    so every LDS read uses an immediate offset.
+//  * NW = 4 waves, one key range, 64-key blocks: for grids with more
+//    workgroups than CUs, where two workgroups share a CU;
+//  * NW = 8 waves, KS = 4 key ranges, 32-key blocks: for small grids.  Two
+//    query heads (or tiles) share each range's K/V stream, the four ranges
+//    of the workgroup's key span run side by side and are merged through LDS
+//    at the end with the split-softmax algebra of the two-phase decode
+//    ("xe2-sdp-kernels", section "Assets", two-phase decode), which gives
+//    every SIMD two waves where the one-range grid would give it one.
+//
+// Software pipeline: iteration j issues the QK MFMAs of block j+1 before the
+// softmax of block j is finished, then runs the PV MFMAs of block j; K(j+2)
+// and V(j+1) are loaded during iteration j.  Buffer parity is a compile-time
+// parameter (the loop is unrolled by two), so every LDS read uses an
+// immediate offset.
 #include <math.h>
 
 #include <type_traits>
@@ -27,27 +34,33 @@
 
 namespace sdpa {
 
-template <class T, int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <class T, int D, int DV, bool CAUSAL, int NW, int KS, int BKT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_o2_kernel(const PrefillArgs a) {
-  constexpr int BK = kPrefillBlockK;
-  constexpr int NW = kPrefillWaves;
+  constexpr int BK = BKT;                     // keys per block
+  constexpr int NWS = NW / KS;                // waves sharing one K/V stream
+  constexpr int NTL = BK / 32;                // 32-key score tiles per block
+  constexpr int NCH = BK / 16;                // 16-key PV chunks per block
   constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
   constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte slots per row
   constexpr int KBYTES = BK * KROW, VBYTES = BK * VROW;
-  constexpr int K_INSTR = BK * KCPR / 64 / NW;  // 1 KiB direct loads per wave per block
-  constexpr int V_INSTR = BK * VCPR / 64 / NW;
-  constexpr int NT = DV / 32;                   // O^T accumulator tiles
+  constexpr int K_INSTR = BK * KCPR / 64 / NWS;  // 1 KiB direct loads per wave per block
+  constexpr int V_INSTR = BK * VCPR / 64 / NWS;
+  constexpr int NT = DV / 32;                    // O^T accumulator tiles
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "block too small for the fill");
-  // LDS: K buffers 0/1, then V buffers 0/1
+  static_assert(NW % KS == 0 && (BK == 32 || BK == 64), "shape");
+  // LDS per key range: K buffers 0/1, then V buffers 0/1
   constexpr uint32_t KBUF0 = 0, KBUF1 = KBYTES;
   constexpr uint32_t VBUF0 = 2 * KBYTES, VBUF1 = 2 * KBYTES + VBYTES;
+  constexpr uint32_t RANGE_BYTES = 2 * KBYTES + 2 * VBYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem;
+  __shared__ __attribute__((aligned(1024))) char smem[KS * RANGE_BYTES];
 
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kr_i = KS == 1 ? 0 : wave / NWS;     // key range of this wave
+  const int wis = KS == 1 ? wave : wave % NWS;  // wave index within its key range
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem + kr_i * RANGE_BYTES;
   const int hl = lane >> 5;  // lane half
   const int l32 = lane & 31;
 
@@ -60,8 +73,8 @@ void prefill_o2_kernel(const PrefillArgs a) {
   const int g = rest % a.head_kv;
   const int b = rest / a.head_kv;
   if (CAUSAL) qt = a.q_tiles - 1 - qt;  // heaviest causal tiles first
-  const int hp_i = wave % a.heads_per_group;
-  const int qp_i = wave / a.heads_per_group;
+  const int hp_i = wis % a.heads_per_group;
+  const int qp_i = wis / a.heads_per_group;
   // heads_per_group need not divide the group size: waves past the group's
   // last head run the loop (uniform barriers) but store nothing
   const bool head_ok = hg * a.heads_per_group + hp_i < a.group;
@@ -82,7 +95,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
   elem_t* __restrict__ optr = (elem_t*)a.o;
 
   if (n_blocks == 0) {  // no visible key for any row of this workgroup
-    if (row_ok) {
+    if (row_ok && kr_i == 0) {
       elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
       for (int c = hl * (DV / 2); c < (hl + 1) * (DV / 2); c += 8) *(u32x4_t*)(orow + c) = u32x4_t{0, 0, 0, 0};
       if (a.lse != nullptr && hl == 0) a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = -INFINITY;
@@ -90,20 +103,27 @@ void prefill_o2_kernel(const PrefillArgs a) {
     return;
   }
 
-  // ---- Q fragments (B operand of S^T = K Q^T), loaded once ---------------
+  // Key range of this wave: range r takes blocks [r*cnt, (r+1)*cnt); blocks
+  // past n_blocks (the end of the last ranges) are masked entirely, so every
+  // range runs the same number of iterations.
+  const int cnt = (n_blocks + KS - 1) / KS;
+  const int kb0 = kr_i * cnt;
+  const int n_unmasked = min(max(n_full - kb0, 0), cnt);
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once; the prologue
+  // waits for them together with K(0) ----------------------------------------
   u32x4_t qf[D / 16];
   {
     const elem_t* qptr = (const elem_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4_t v = *(const u32x4_t*)(qptr + 16 * s);
-      qf[s] = row_ok ? v : u32x4_t{0, 0, 0, 0};
-    }
+    static_for<D / 16>([&](auto s) __attribute__((always_inline)) {
+      constexpr int S = decltype(s)::value;
+      global_load_16_untracked<32 * S>(qf[S], qptr);
+    });
   }
 
   // ---- direct global -> LDS fills ------------------------------------------
   // Instruction i of this wave covers the 64 16-byte slots starting at slot
-  // (wave*INSTR + i)*64; lane p holds slot P: row P / CPR, position P % CPR,
+  // (wis*INSTR + i)*64; lane p holds slot P: row P / CPR, position P % CPR,
   // which receives chunk (P % CPR) ^ swizzle(row) of that key row.
   const char* kg = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * (D * 2);
   const char* vg = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * (DV * 2);
@@ -112,19 +132,19 @@ void prefill_o2_kernel(const PrefillArgs a) {
   uint32_t kfo[K_INSTR], vfo[V_INSTR];    // byte offsets within a whole block
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
-    const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
+    const int slot = (wis * K_INSTR + i) * 64 + lane, r = slot / KCPR;
     kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
-    const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
+    const int slot = (wis * V_INSTR + i) * 64 + lane, r = slot / VCPR;
     vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
   }
   const int last_key = Sk - 1;
-  // A block is whole if all its BK keys exist; in the last block of a ragged
-  // key range the rows past the end re-read the last key (they are masked).
+  // A block is whole if all its BK keys exist; in a ragged block (the last
+  // one, or one past the end) rows past the last key re-read it (masked).
   auto fill_k = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
-    const uint32_t l = lds0 + buf + wave * K_INSTR * 1024;
+    const uint32_t l = lds0 + buf + wis * K_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = kg + (size_t)kb * BK * kstride;
 #pragma unroll
@@ -132,7 +152,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < K_INSTR; ++i) {
-        const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
+        const int slot = (wis * K_INSTR + i) * 64 + lane, r = slot / KCPR;
         const int key = min(kb * BK + r, last_key);
         global_to_lds_16(kg + (size_t)key * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16),
                          l + i * 1024);
@@ -140,7 +160,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
     }
   };
   auto fill_v = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
-    const uint32_t l = lds0 + buf + wave * V_INSTR * 1024;
+    const uint32_t l = lds0 + buf + wis * V_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = vg + (size_t)kb * BK * vstride;
 #pragma unroll
@@ -148,7 +168,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < V_INSTR; ++i) {
-        const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
+        const int slot = (wis * V_INSTR + i) * 64 + lane, r = slot / VCPR;
         const int key = min(kb * BK + r, last_key);
         global_to_lds_16(vg + (size_t)key * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16),
                          l + i * 1024);
@@ -157,8 +177,8 @@ void prefill_o2_kernel(const PrefillArgs a) {
   };
 
   // ---- per-lane LDS read offsets -----------------------------------------
-  // K fragment (A operand): key row l%32 (+32 for the second score tile),
-  // head-dim slot 2*s + l/32.
+  // K fragment (A operand): key row l%32 (+32 per score tile), head-dim slot
+  // 2*s + l/32.
   uint32_t koff[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
@@ -191,28 +211,27 @@ void prefill_o2_kernel(const PrefillArgs a) {
   float m_run = -INFINITY;  // running max of s2*S for query l%32 (log2 domain)
   float l_run = 0.f;        // this lane's share of the running sum
   const float s2 = a.s2;
-  f32x16_t sa[2], sb[2];    // score tiles of two consecutive blocks
+  f32x16_t sa[NTL], sb[NTL];  // score tiles of two consecutive blocks
 
   // GEMM 1: S^T[key][query] of the block in K buffer KB
-  auto qk = [&](auto kb_tag, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
+  auto qk = [&](auto kb_tag, f32x16_t (&sc)[NTL]) __attribute__((always_inline)) {
     constexpr uint32_t KB = decltype(kb_tag)::value;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[0][r] = 0.f;
-      sc[1][r] = 0.f;
-    }
+    for (int t = 0; t < NTL; ++t)
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const u32x4_t k0 = lds_read_b128(koff[s] + KB);
-      const u32x4_t k1 = lds_read_b128(koff[s] + KB + 32 * KROW);
-      sc[0] = mfma32x32x16<T>(k0, qf[s], sc[0]);
-      sc[1] = mfma32x32x16<T>(k1, qf[s], sc[1]);
-    }
+      for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const u32x4_t kf = lds_read_b128(koff[s] + KB + 32 * t * KROW);
+        sc[t] = mfma32x32x16<T>(kf, qf[s], sc[t]);
+      }
   };
 
   // Softmax part 1: mask (tail blocks only), block row max, lazy rescale.
   // Returns the subtrahend m of P = 2^(s2*S - m).
-  auto softmax_max = [&](int kb, f32x16_t (&sc)[2], auto masked_tag) __attribute__((always_inline)) -> float {
+  auto softmax_max = [&](int kb, f32x16_t (&sc)[NTL], auto masked_tag) __attribute__((always_inline)) -> float {
     constexpr bool MASKED = decltype(masked_tag)::value;
     float bmax;
     if constexpr (MASKED) {
@@ -221,7 +240,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
       const int lim = (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl);
       bmax = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = (32 * t + 8 * (r >> 2) + (r & 3)) <= lim ? sc[t][r] * s2 : -INFINITY;
@@ -231,7 +250,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
     } else {
       float mx = sc[0][0];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
       bmax = mx * s2;
@@ -258,10 +277,11 @@ void prefill_o2_kernel(const PrefillArgs a) {
 
   // Softmax part 2: P = 2^(s2*S - m) packed to 16 bits as the PV B operand;
   // the row sum is taken over the packed values.
-  auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], auto masked_tag) __attribute__((always_inline)) {
+  auto softmax_exp = [&](const f32x16_t (&sc)[NTL], float m_sub, u32x4_t (&pf)[NCH], auto masked_tag)
+      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NTL; ++t)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0, p1;
@@ -279,10 +299,10 @@ void prefill_o2_kernel(const PrefillArgs a) {
   };
 
   // GEMM 2: O^T[dv][query] += V^T P^T from V buffer VB, 16 keys per MFMA
-  auto pv = [&](auto vb_tag, const u32x4_t (&pf)[4]) __attribute__((always_inline)) {
+  auto pv = [&](auto vb_tag, const u32x4_t (&pf)[NCH]) __attribute__((always_inline)) {
     constexpr uint32_t VB = decltype(vb_tag)::value;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const u32x2_t lo = lds_read_tr16(voff[0][t] + VB + (16 * c) * VROW);
@@ -292,11 +312,11 @@ void prefill_o2_kernel(const PrefillArgs a) {
       }
   };
 
-  // One pipeline iteration j (PAR = j & 1): the scores of block j are in
-  // registers, K(j+1) sits in K buffer 1-PAR and V(j) in V buffer PAR.  It
-  // starts the loads of V(j+1) and K(j+2) into the buffers freed by the
-  // previous iteration, computes the scores of block j+1, then the softmax
-  // and P V of block j.
+  // One pipeline iteration j (PAR = j & 1, block kb0 + j): the scores of
+  // block j are in registers, K(j+1) sits in K buffer 1-PAR and V(j) in V
+  // buffer PAR.  It starts the loads of V(j+1) and K(j+2) into the buffers
+  // freed by the previous iteration, computes the scores of block j+1, then
+  // the softmax and P V of block j.
   auto iteration = [&](int j, auto masked_tag, auto next_tag, auto par_tag) __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
@@ -304,12 +324,12 @@ void prefill_o2_kernel(const PrefillArgs a) {
     constexpr uint32_t KB_FREE = PAR ? KBUF1 : KBUF0;   // receives K(j+2)
     constexpr uint32_t VB_CUR = PAR ? VBUF1 : VBUF0;    // holds V(j)
     constexpr uint32_t VB_FREE = PAR ? VBUF0 : VBUF1;   // receives V(j+1)
-    f32x16_t(&s_cur)[2] = PAR ? sb : sa;
-    f32x16_t(&s_nxt)[2] = PAR ? sa : sb;
+    f32x16_t(&s_cur)[NTL] = PAR ? sb : sa;
+    f32x16_t(&s_nxt)[NTL] = PAR ? sa : sb;
     if constexpr (NEXT) {
-      fill_v(j + 1, VB_FREE);
-      if (j + 2 < n_blocks) {
-        fill_k(j + 2, KB_FREE);
+      fill_v(kb0 + j + 1, VB_FREE);
+      if (j + 2 < cnt) {
+        fill_k(kb0 + j + 2, KB_FREE);
         wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) have landed
       } else {
         wait_vmcnt<V_INSTR>();
@@ -318,8 +338,8 @@ void prefill_o2_kernel(const PrefillArgs a) {
       wait_vmcnt<0>();
     }
     __syncthreads();
-    const float m_sub = softmax_max(j, s_cur, masked_tag);
-    u32x4_t pf[4];
+    const float m_sub = softmax_max(kb0 + j, s_cur, masked_tag);
+    u32x4_t pf[NCH];
     // Phase fence, then the QK MFMAs of block j+1 interleaved with the
     // exponentials of block j: after each K fragment read and MFMA the wave
     // issues a few independent VALU instructions, which execute while the
@@ -329,7 +349,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
     softmax_exp(s_cur, m_sub, pf, masked_tag);
     if constexpr (NEXT) {
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
+      for (int i = 0; i < NTL * D / 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
@@ -359,19 +379,20 @@ void prefill_o2_kernel(const PrefillArgs a) {
   using Masked = std::true_type;
   using Next = std::true_type;
   using Last = std::false_type;
-  fill_k(0, KBUF0);
-  fill_v(0, VBUF0);
-  if (n_blocks > 1) {
-    fill_k(1, KBUF1);
-    wait_vmcnt<K_INSTR + V_INSTR>();  // K(0) has landed
-  } else {
-    wait_vmcnt<V_INSTR>();
-  }
+  // Q, K(0), V(0) and K(1) in flight at once (block 0 again when there is no
+  // block 1, into a buffer nothing reads); the first scores wait for Q and
+  // K(0) only
+  fill_k(kb0, KBUF0);
+  fill_v(kb0, VBUF0);
+  fill_k(kb0 + min(1, cnt - 1), KBUF1);
+  wait_vmcnt_pin<K_INSTR + V_INSTR>(qf);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = row_ok ? qf[s] : u32x4_t{0, 0, 0, 0};
   __syncthreads();
   qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
   __syncthreads();  // K buffer 0 is refilled by the first iteration
-  const int n_next = n_blocks - 1;  // iterations that have a next block
-  const int j_mask = min(n_full, n_next);
+  const int n_next = cnt - 1;  // iterations that have a next block
+  const int j_mask = min(n_unmasked, n_next);
   run(0, j_mask, Unmasked{}, Next{});
   run(j_mask, n_next, Masked{}, Next{});
   // the last block (peeled): masked unless every key of it is visible to
@@ -380,6 +401,59 @@ void prefill_o2_kernel(const PrefillArgs a) {
     iteration(n_next, Masked{}, Last{}, Par1{});
   else
     iteration(n_next, Masked{}, Last{}, Par0{});
+
+  // ---- merge of the key ranges (ranges 1.. -> LDS -> range 0) -------------
+  if constexpr (KS > 1) {
+    __syncthreads();  // every wave is past its last LDS read
+    // per wave of ranges 1..KS-1: NT*16 accumulators + (m, l) per lane, as
+    // 16-byte lane-major rows (conflict-free)
+    constexpr int XROWS = NT * 4 + 1;
+    static_assert((KS - 1) * NWS * XROWS * 1024 <= KS * RANGE_BYTES, "merge area");
+    SDPA_LDS f32x4_t* xbase = (SDPA_LDS f32x4_t*)((SDPA_LDS char*)smem) + lane;
+    if (kr_i > 0) {
+      SDPA_LDS f32x4_t* xb = xbase + ((kr_i - 1) * NWS + wis) * XROWS * 64;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xb[(t * 4 + q4) * 64] = f32x4_t{acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]};
+      xb[NT * 4 * 64] = f32x4_t{m_run, l_run, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (kr_i > 0) return;
+    float mr[KS], lr[KS];
+    mr[0] = m_run;
+    lr[0] = l_run;
+    float mm = m_run;
+#pragma unroll
+    for (int r = 1; r < KS; ++r) {
+      const f32x4_t ml = xbase[((r - 1) * NWS + wis) * XROWS * 64 + NT * 4 * 64];
+      mr[r] = ml[0];
+      lr[r] = ml[1];
+      mm = fmaxf(mm, mr[r]);
+    }
+    float w[KS];
+    l_run = 0.f;
+#pragma unroll
+    for (int r = 0; r < KS; ++r) {
+      w[r] = mr[r] == -INFINITY ? 0.f : fast_exp2(mr[r] - mm);  // empty range: weight 0
+      l_run += w[r] * lr[r];
+    }
+    m_run = mm;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][4 * q4 + e] *= w[0];
+#pragma unroll
+        for (int r = 1; r < KS; ++r) {
+          const f32x4_t o = xbase[((r - 1) * NWS + wis) * XROWS * 64 + (t * 4 + q4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][4 * q4 + e] += w[r] * o[e];
+        }
+      }
+  }
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------
   const float l_tot = pair_sum(l_run);
@@ -391,32 +465,36 @@ void prefill_o2_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int col = 32 * t + 8 * q4 + 4 * hl;
-        u32x2_t w;
-        w.x = pack2<T>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
-        w.y = pack2<T>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
-        *(u32x2_t*)(orow + col) = w;
+        u32x2_t wv;
+        wv.x = pack2<T>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
+        wv.y = pack2<T>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
+        *(u32x2_t*)(orow + col) = wv;
       }
     if (a.lse != nullptr && hl == 0)
       a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <class T, int D>
+template <class T, int D, int NW, int KS, int BK>
 static int launch_o2_t(const PrefillArgs& a, int causal, ihipStream_t* stream) {
-  dim3 grid(a.num_groups), block(64 * kPrefillWaves);
+  dim3 grid(a.num_groups), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, true>), grid, block, 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, true, NW, KS, BK>), grid, block, 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, false>), grid, block, 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, false, NW, KS, BK>), grid, block, 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
   switch (plan.kernel) {
-    case kOccF16D64: return launch_o2_t<F16, 64>(a, causal, stream);
-    case kOccBf16D64: return launch_o2_t<Bf16, 64>(a, causal, stream);
-    case kOccF16D128: return launch_o2_t<F16, 128>(a, causal, stream);
-    case kOccBf16D128: return launch_o2_t<Bf16, 128>(a, causal, stream);
+    case kOccF16D64: return launch_o2_t<F16, 64, 4, 1, 64>(a, causal, stream);
+    case kOccBf16D64: return launch_o2_t<Bf16, 64, 4, 1, 64>(a, causal, stream);
+    case kOccF16D128: return launch_o2_t<F16, 128, 4, 1, 64>(a, causal, stream);
+    case kOccBf16D128: return launch_o2_t<Bf16, 128, 4, 1, 64>(a, causal, stream);
+    case kSplitF16D64: return launch_o2_t<F16, 64, 8, 4, 32>(a, causal, stream);
+    case kSplitBf16D64: return launch_o2_t<Bf16, 64, 8, 4, 32>(a, causal, stream);
+    case kSplitF16D128: return launch_o2_t<F16, 128, 8, 4, 32>(a, causal, stream);
+    case kSplitBf16D128: return launch_o2_t<Bf16, 128, 8, 4, 32>(a, causal, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

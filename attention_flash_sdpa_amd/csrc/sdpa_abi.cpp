@@ -43,6 +43,7 @@ int prefill_variant() {
   if (!strcmp(e, "narrow1")) return 3;
   if (!strcmp(e, "narrow2")) return 4;
   if (!strcmp(e, "occ2")) return 5;
+  if (!strcmp(e, "split4")) return 6;
   return 0;
 }
 

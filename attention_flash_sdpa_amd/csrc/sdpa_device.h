@@ -283,6 +283,27 @@ __device__ __forceinline__ void global_to_lds_16_sbase(const void* sbase, uint32
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(u), "{m0}"(lds_base) : "memory");
 }
 
+// 16-byte global load into a VGPR quad, issued from asm so that the
+// compiler's wait-count tracking does not see it: it can then be issued
+// ahead of direct-to-LDS loads and waited for with a vmcnt that leaves those
+// in flight (the compiler would otherwise wait for all of them before the
+// first use).  Its result is read only after wait_vmcnt_pin<N>().
+template <int OFF>
+__device__ __forceinline__ void global_load_16_untracked(u32x4_t& d, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=&v"(d) : "v"(p), "i"(OFF) : "memory");
+}
+
+// Waits until at most N vector-memory operations of this wave are in flight,
+// then marks the registers of d as written here, so no use of them can be
+// scheduled before the wait.
+template <int N, int K>
+__device__ __forceinline__ void wait_vmcnt_pin(u32x4_t (&d)[K]) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+#pragma unroll
+  for (int k = 0; k < K; ++k) asm volatile("" : "+v"(d[k]));
+}
+
 // Waits until at most n vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

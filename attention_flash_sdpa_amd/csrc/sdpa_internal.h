@@ -29,6 +29,10 @@ enum KernelId : int32_t {
   kDecodeBf16D64 = 17,
   kDecodeF16D128 = 18,
   kDecodeBf16D128 = 19,
+  kSplitF16D64 = 24,  // 32-row kernel, 8 waves: 2 heads x 4 key ranges (small grids)
+  kSplitBf16D64 = 25,
+  kSplitF16D128 = 26,
+  kSplitBf16D128 = 27,
 };
 
 constexpr int kRowsPerWave = 32;   // prefill: query rows per wave (MFMA N)
@@ -36,6 +40,9 @@ constexpr int kWideRowsPerWave = 64;  // wide prefill: two 32-row tiles per wave
 constexpr int kWideBlockK = 32;       // wide prefill: keys per K/V block
 constexpr int kPrefillWaves = 4;   // prefill: waves per workgroup
 constexpr int kPrefillBlockK = 64; // prefill: keys per K/V block
+constexpr int kSplitWaves = 8;     // 4-range prefill: waves per workgroup
+constexpr int kSplitRanges = 4;    // 4-range prefill: key ranges per workgroup
+constexpr int kSplitBlockK = 32;   // 4-range prefill: keys per K/V block
 constexpr int kDecodeBlockK = 32;  // decode: keys per K/V block
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
@@ -46,7 +53,8 @@ constexpr int kDefaultCUs = 256;
 // variant: 0 = planner's choice, 1 = the 32-row kernels (planner picks the
 // form), 2 = the wide (64-row) kernel, 3 / 4 = the one-wave-per-SIMD 32-row
 // kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
-// 32-row kernel (tuning sweeps and tests only).
+// 32-row kernel, 6 = its 8-wave, four-key-range form (tuning sweeps and tests
+// only).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan, int variant = 0);
 

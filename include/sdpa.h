@@ -108,7 +108,7 @@ typedef struct sdpa_plan {
   int32_t kv_blocks;        /* ceil(kv_len / block_k)                           */
   int32_t num_groups;       /* workgroups of the main kernel                    */
   int32_t num_splits;       /* decode: key-range splits per (batch, KV head);
-                               prefill: key ranges per workgroup (1 or 2), each
+                               prefill: key ranges per workgroup (1, 2 or 4), each
                                streamed by its own waves, merged at the end    */
   int32_t blocks_per_split; /* decode: K/V blocks per split                     */
   int32_t combine_groups;   /* decode: workgroups of the combine kernel         */

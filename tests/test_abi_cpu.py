@@ -129,6 +129,10 @@ def test_prefill_variant_override(monkeypatch):
     monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow2")
     p2 = sdpa.plan(_problem(inputs.WORKLOADS["unaligned_full_bf16"]))
     assert (p2.num_splits, p2.heads_per_group, p2.qtiles_per_group, p2.num_groups) == (2, 1, 2, 2 * 4 * 7 * 16)
+    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "split4")
+    p4 = sdpa.plan(_problem(w))
+    assert (p4.kernel, p4.num_splits, p4.waves_per_group, p4.block_k, p4.kv_blocks) == (27, 4, 8, 32, 32)
+    assert (p4.heads_per_group, p4.qtiles_per_group, p4.num_groups, p4.lds_bytes) == (2, 1, 8 * 2 * 16, 131072)
     monkeypatch.delenv("SDPA_PREFILL_VARIANT")
     assert sdpa.plan(_problem(w)).rows_per_wave == 32
 

@@ -102,6 +102,15 @@ def test_gqa_causal_prefill_bf16(dev, oracle_mod):
     _prefill_case(dev, oracle_mod, q, k, v, causal=w.causal, scale=w.scale, what=w.name)
 
 
+@pytest.mark.parametrize("variant", ["narrow1", "occ2", "split4"])
+def test_gqa_causal_prefill_bf16_forms(dev, oracle_mod, variant, monkeypatch):
+    """The full-size causal GQA workload through the other 32-row forms."""
+    monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    q, k, v, _ = inputs.make_qkv(w)
+    _prefill_case(dev, oracle_mod, q, k, v, causal=w.causal, scale=w.scale, what=f"{w.name} {variant}")
+
+
 def test_unaligned_full_bf16_reduced(dev, oracle_mod):
     """Same head layout and dtypes, lengths cut to 301 x 323 (several tiles and
     ragged tails in both dimensions) so every row is checked."""
@@ -163,15 +172,16 @@ EDGE = [
     (1, 300, 130, 4, 2, 128, torch.bfloat16, True),   # 3 key blocks, many empty rows
     (1, 64, 192, 2, 1, 64, torch.float16, False),     # 3 whole key blocks
     (2, 96, 64, 2, 2, 128, torch.float16, True),      # one key block
+    (1, 20, 150, 4, 2, 128, torch.bfloat16, True),    # key ranges past the last key
 ]
 
 
-@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "wide"])
+@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "split4", "wide"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}_q{c[1]}_k{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_{str(c[6])[6:]}_{'c' if c[7] else 'f'}" for c in EDGE])
 def test_prefill_edge_shapes(dev, oracle_mod, case, variant, monkeypatch):
     """Every edge shape through every 16-bit prefill kernel: 32-row waves (one
     wave per SIMD with one or two key ranges per workgroup, two waves per
-    SIMD) and 64-row waves."""
+    SIMD with one or four key ranges) and 64-row waves."""
     monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
     B, Sq, Sk, Hq, Hkv, D, dt, causal = case
     g = torch.Generator().manual_seed(Sq * 1000 + Sk)
