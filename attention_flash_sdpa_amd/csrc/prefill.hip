@@ -399,9 +399,6 @@ void prefill_kernel(const PrefillArgs a) {
         vfr[m] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
       }
     };
-    auto expv = [&](float x) __attribute__((always_inline)) -> float {
-      return MCUR ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, s2, -m_sub));
-    };
     auto maxv = [&](int t, int r) __attribute__((always_inline)) {
       if constexpr (MNEXT) {
         const int pos = 32 * t + 8 * (r >> 2) + (r & 3);
@@ -420,13 +417,20 @@ void prefill_kernel(const PrefillArgs a) {
       constexpr int R0 = decltype(r0_tag)::value, R1 = decltype(r1_tag)::value;
 #pragma unroll
       for (int r = R0; r < R1; ++r) {
-        float x = s_cur[TL][r];
-        pin(x);
-        const float p = expv(x);
+        // the exponent is formed by an asm instruction that reads the score
+        // where the MFMA left it (anchoring the work to this slot without
+        // copying the score out of its tile first)
+        float y;
+        if constexpr (MCUR)
+          asm volatile("v_sub_f32 %0, %1, %2" : "=v"(y) : "v"(s_cur[TL][r]), "v"(m_sub));
+        else
+          asm volatile("v_fma_f32 %0, %1, %2, -%3" : "=v"(y) : "v"(s_cur[TL][r]), "s"(s2), "v"(m_sub));
+        const float p = fast_exp2(y);
         if (r & 1) {
           uint32_t pk = pack2<T>(pend[TL], p);
           l_run = add_pair<T>(pk, l_run);
-          pin(pk);
+          asm volatile("" ::"v"(pk));  // computed in this slot; not tied, so it
+                                        // can be formed in its operand register
           pf[2 * TL + (r >> 3)][(r & 7) >> 1] = pk;
         } else {
           pend[TL] = p;
