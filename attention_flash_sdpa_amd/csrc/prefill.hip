@@ -374,10 +374,15 @@ void prefill_kernel(const PrefillArgs a) {
     const uint32_t kl = lds0 + KB_FREE + wis * K_INSTR * 1024;
     auto dma = [&](auto i_tag) __attribute__((always_inline)) {
       constexpr int I = decltype(i_tag)::value;
-      if constexpr (I < V_INSTR)
+      // the first load from each base waits for its SGPRs, the rest do not
+      if constexpr (I == 0)
         global_to_lds_16_sbase(vsrc, vfo[I], vl + I * 1024);
-      else
+      else if constexpr (I < V_INSTR)
+        global_to_lds_16_sbase_next(vsrc, vfo[I], vl + I * 1024);
+      else if constexpr (I == V_INSTR)
         global_to_lds_16_sbase(ksrc, kfo[I - V_INSTR], kl + (I - V_INSTR) * 1024);
+      else
+        global_to_lds_16_sbase_next(ksrc, kfo[I - V_INSTR], kl + (I - V_INSTR) * 1024);
     };
 
     // visible window of block j+1 (masked flavour only)

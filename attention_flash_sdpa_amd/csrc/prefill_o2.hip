@@ -147,8 +147,9 @@ void prefill_o2_kernel(const PrefillArgs a) {
     const uint32_t l = lds0 + buf + wis * K_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = kg + (size_t)kb * BK * kstride;
+      global_to_lds_16_sbase(base, kfo[0], l);
 #pragma unroll
-      for (int i = 0; i < K_INSTR; ++i) global_to_lds_16_sbase(base, kfo[i], l + i * 1024);
+      for (int i = 1; i < K_INSTR; ++i) global_to_lds_16_sbase_next(base, kfo[i], l + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < K_INSTR; ++i) {
@@ -163,8 +164,9 @@ void prefill_o2_kernel(const PrefillArgs a) {
     const uint32_t l = lds0 + buf + wis * V_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = vg + (size_t)kb * BK * vstride;
+      global_to_lds_16_sbase(base, vfo[0], l);
 #pragma unroll
-      for (int i = 0; i < V_INSTR; ++i) global_to_lds_16_sbase(base, vfo[i], l + i * 1024);
+      for (int i = 1; i < V_INSTR; ++i) global_to_lds_16_sbase_next(base, vfo[i], l + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < V_INSTR; ++i) {

@@ -293,6 +293,16 @@ __device__ __forceinline__ void global_load_16_untracked(u32x4_t& d, const void*
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=&v"(d) : "v"(p), "i"(OFF) : "memory");
 }
 
+// As global_to_lds_16_sbase, for a later load from the same base: the base
+// SGPRs were written (by the first load's v_readfirstlane) at least five
+// instructions earlier, so only the M0 write needs its wait state.
+__device__ __forceinline__ void global_to_lds_16_sbase_next(const void* sbase, uint32_t voffset, uint32_t lds_base) {
+  const uint64_t p = (uint64_t)(uintptr_t)sbase;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(u), "{m0}"(lds_base) : "memory");
+}
+
 // Waits until at most N vector-memory operations of this wave are in flight,
 // then marks the registers of d as written here, so no use of them can be
 // scheduled before the wait.
