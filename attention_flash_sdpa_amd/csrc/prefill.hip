@@ -592,57 +592,85 @@ void prefill_kernel(const PrefillArgs a) {
   }
 
   mfma_acc_drain(acc);  // the last P V MFMAs have written the accumulators
-  // ---- merge of the two key ranges (range 1 -> LDS -> range 0) -------------
-  if constexpr (KS == 2) {
-    __syncthreads();  // every wave is past its last LDS read
-    // per wave of range 1: NT*16 accumulators + (m, l) per lane, stored as
-    // 16-byte lane-major rows (conflict-free)
-    constexpr int XROWS = NT * 4 + 1;
-    SDPA_LDS f32x4_t* xb = (SDPA_LDS f32x4_t*)((SDPA_LDS char*)smem) + wis * XROWS * 64 + lane;
-    if (kr_i == 1) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          xb[(t * 4 + q4) * 64] = f32x4_t{acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]};
-      xb[NT * 4 * 64] = f32x4_t{m_run, l_run, 0.f, 0.f};
-    }
-    __syncthreads();
-    if (kr_i == 1) return;
-    const f32x4_t ml = xb[NT * 4 * 64];
-    const float m1 = ml[0], l1 = ml[1];
-    const float mm = fmaxf(m_run, m1);
-    const float w0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
-    const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
-    l_run = l_run * w0 + l1 * w1;
-    m_run = mm;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t o1 = xb[(t * 4 + q4) * 64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t][4 * q4 + e] = acc[t][4 * q4 + e] * w0 + o1[e] * w1;
-      }
-  }
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
-  if (row_ok) {
-    elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
+  // Value tiles [T0, T1) of this wave's rows.
+  auto store = [&](auto t0_tag, auto t1_tag) __attribute__((always_inline)) {
+    constexpr int T0 = decltype(t0_tag)::value, T1 = decltype(t1_tag)::value;
+    const float l_tot = pair_sum(l_run);
+    const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
+    if (row_ok) {
+      elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = T0; t < T1; ++t)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int col = 32 * t + 8 * q4 + 4 * hl;
-        u32x2_t w;
-        w.x = pack2<T>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
-        w.y = pack2<T>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
-        *(u32x2_t*)(orow + col) = w;
-      }
-    if (a.lse != nullptr && hl == 0)
-      a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int col = 32 * t + 8 * q4 + 4 * hl;
+          u32x2_t w;
+          w.x = pack2<T>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
+          w.y = pack2<T>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
+          *(u32x2_t*)(orow + col) = w;
+        }
+      if (a.lse != nullptr && hl == 0 && T0 == 0)
+        a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  };
+
+  if constexpr (KS == 1) {
+    store(std::integral_constant<int, 0>{}, std::integral_constant<int, NT>{});
+  } else {
+    // ---- merge of the two key ranges through LDS ---------------------------
+    // Each range finalizes half of the value tiles of its rows: range 0 tiles
+    // [0, NT/2), range 1 [NT/2, NT).  A wave hands the other half of its
+    // accumulators and its (m, l) to its partner wave (same rows, other range)
+    // as 16-byte lane-major rows (conflict-free), then merges its own half.
+    constexpr int H = NT / 2;
+    constexpr int XROWS = H * 4 + 1;
+    static_assert(2 * NWS * XROWS * 1024 <= sizeof(smem), "merge area");
+    __syncthreads();  // every wave is past its last LDS read
+    SDPA_LDS f32x4_t* xout = (SDPA_LDS f32x4_t*)((SDPA_LDS char*)smem) + (kr_i * NWS + wis) * XROWS * 64 + lane;
+    SDPA_LDS f32x4_t* xin = (SDPA_LDS f32x4_t*)((SDPA_LDS char*)smem) + ((1 - kr_i) * NWS + wis) * XROWS * 64 + lane;
+    auto hand_over = [&](auto t0_tag) __attribute__((always_inline)) {
+      constexpr int T0 = decltype(t0_tag)::value;
+#pragma unroll
+      for (int t = 0; t < H; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xout[(t * 4 + q4) * 64] = f32x4_t{acc[T0 + t][4 * q4], acc[T0 + t][4 * q4 + 1], acc[T0 + t][4 * q4 + 2],
+                                            acc[T0 + t][4 * q4 + 3]};
+      xout[H * 4 * 64] = f32x4_t{m_run, l_run, 0.f, 0.f};
+    };
+    auto merge = [&](auto t0_tag) __attribute__((always_inline)) {
+      constexpr int T0 = decltype(t0_tag)::value;
+      const f32x4_t ml = xin[H * 4 * 64];
+      const float m1 = ml[0], l1 = ml[1];
+      const float mm = fmaxf(m_run, m1);
+      const float w0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
+      const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+      l_run = l_run * w0 + l1 * w1;
+      m_run = mm;
+#pragma unroll
+      for (int t = 0; t < H; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t o1 = xin[(t * 4 + q4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[T0 + t][4 * q4 + e] = acc[T0 + t][4 * q4 + e] * w0 + o1[e] * w1;
+        }
+    };
+    using Lo = std::integral_constant<int, 0>;
+    using Hi = std::integral_constant<int, H>;
+    using End = std::integral_constant<int, NT>;
+    if (kr_i == 0) hand_over(Hi{});
+    else hand_over(Lo{});
+    __syncthreads();
+    if (kr_i == 0) {
+      merge(Lo{});
+      store(Lo{}, Hi{});
+    } else {
+      merge(Hi{});
+      store(Hi{}, End{});
+    }
   }
 }
 
