@@ -220,10 +220,16 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     S = num_splits;
     plan->blocks_per_split = (int32_t)(plan->kv_blocks > 0 ? ceil_div(plan->kv_blocks, S) : 1);
   } else {
-    // Enough wavefronts to keep every CU streaming (8 per CU), but no split
-    // shorter than two blocks, so the per-split overhead (Q load, partial
-    // write, combine) stays a few percent of the K/V bytes.
-    const int64_t target = (int64_t)num_cus * 8;
+    // One round of workgroups, as many as fit on a CU at once (LDS-bound: the
+    // double-buffered K/V blocks of its 4 waves), keeps every CU streaming; a
+    // second round would start only as the first drains.  No split is shorter
+    // than two blocks, so the per-split overhead (Q load, partial write,
+    // combine) stays a few percent of the K/V bytes.
+    const int64_t lds = (int64_t)kDecodeWaves * 2 * kDecodeBlockK * (p.d_qk + p.d_v) * 2;
+    int64_t per_cu = kLdsPerCu / lds;
+    if (per_cu < 1) per_cu = 1;
+    if (per_cu > 2) per_cu = 2;  // at most two waves per SIMD
+    const int64_t target = (int64_t)num_cus * kDecodeWaves * per_cu;
     S = pairs > 0 ? ceil_div(target, pairs) : 1;
     const int64_t max_s = plan->kv_blocks / 2 > 0 ? plan->kv_blocks / 2 : 1;
     if (S > max_s) S = max_s;

@@ -242,23 +242,6 @@ void prefill_kernel(const PrefillArgs a) {
   const float s2 = a.s2;
   f32x16_t sa[2], sb[2];    // score tiles of two consecutive blocks
 
-  // GEMM 1: S^T[key][query] of the block in K buffer KB: two 32-key tiles,
-  // KSTEPS MFMAs each
-  auto qk = [&](auto kb_tag, f32x16_t (&sc)[2]) __attribute__((always_inline)) {
-    constexpr uint32_t KB = decltype(kb_tag)::value;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[0][r] = 0.f;
-      sc[1][r] = 0.f;
-    }
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const u32x4_t k0 = lds_read_b128(koff[s] + KB);
-      const u32x4_t k1 = lds_read_b128(koff[s] + KB + 32 * KROW);
-      sc[0] = mfma32x32x16<T>(k0, qf[s], sc[0]);
-      sc[1] = mfma32x32x16<T>(k1, qf[s], sc[1]);
-    }
-  };
 
   // Visible positions of block kb for this lane: register r of score tile t
   // holds key row0 + 4*hl + 32t + 8(r/4) + r%4, visible iff it is at least
@@ -531,8 +514,6 @@ void prefill_kernel(const PrefillArgs a) {
   __syncthreads();
   {
     constexpr int NQK0 = 2 * KSTEPS, PD = 4;
-    constexpr int NF = V_INSTR + K_INSTR, FSTRIDE = NQK0 / NF > 0 ? NQK0 / NF : 1;
-    const int j1 = min(1, cnt - 1);
     u32x4_t kfr0[NQK0];
     auto rd = [&](auto n_tag) __attribute__((always_inline)) {
       constexpr int N = decltype(n_tag)::value;
@@ -548,7 +529,6 @@ void prefill_kernel(const PrefillArgs a) {
         mfma_s_first<T, LGKM>(sa[N % 2], kfr0[N], qf[N / 2]);
       else
         mfma_s_acc<T, LGKM>(sa[N % 2], kfr0[N], qf[N / 2]);
-      (void)FSTRIDE;
     });
     mfma_s_drain(sa);
     __builtin_amdgcn_sched_barrier(0);

@@ -110,10 +110,15 @@ def test_plans_for_workloads():
     p = sdpa.plan(_problem(W["tiny_causal_bf16"]))
     assert (p.heads_per_group, p.q_tiles, p.num_groups) == (4, 1, 2 * 4 * 2)
     d = sdpa.plan(_problem(W["splitkv_decode_bf16"]), decode=True, num_cus=256)
-    assert (d.num_splits, d.blocks_per_split, d.block_k) == (16, 16, 32)
-    assert d.num_groups * d.waves_per_group == 16 * 8 * 16
+    # 128 KiB of LDS per workgroup: one per CU, so one round of 256 workgroups
+    assert (d.num_splits, d.blocks_per_split, d.block_k) == (8, 32, 32)
+    assert d.num_groups * d.waves_per_group == 16 * 8 * 8 and d.num_groups == 256
     assert d.combine_groups == 16 * 32
-    assert d.workspace_bytes == 16 * 32 * 16 * 128 * 4 + 16 * 32 * 16 * 2 * 4
+    assert d.workspace_bytes == 16 * 32 * 8 * 128 * 4 + 16 * 32 * 8 * 2 * 4
+    # d = 64 blocks take 64 KiB: two workgroups per CU
+    import dataclasses
+    d64 = sdpa.plan(_problem(dataclasses.replace(W["splitkv_decode_bf16"], d_qk=64, d_v=64)), decode=True, num_cus=256)
+    assert d64.num_splits == 16 and d64.num_groups == 512
 
 
 def test_prefill_variant_override(monkeypatch):
