@@ -135,8 +135,10 @@ def _kernels_of(sdpa, w, num_cus=256):
                 (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 64)]
     if w.dtype == "fp8_e4m3":
         return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
-    if 12 <= p.kernel <= 15:   # the two-waves-per-SIMD 32-row kernel
-        return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
+    if 12 <= p.kernel <= 15 or 24 <= p.kernel <= 27:   # the two-waves-per-SIMD 32-row kernel
+        shape = "4, 1, 64" if p.kernel <= 15 else "8, 4, 32"   # waves, key ranges, keys per block
+        return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {shape}>",
+                 p.num_groups * p.waves_per_group * 64)]
     if p.rows_per_wave == 64:
         return [(f"prefill_wide_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
     return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}>",
