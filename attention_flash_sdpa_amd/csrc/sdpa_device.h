@@ -92,9 +92,12 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
 //  * the LDS wait: each MFMA waits until at most LGKM LDS reads of this wave
 //    are in flight (LDS reads complete in order, so the reads issued after
 //    the one it needs may stay outstanding);
-//  * two wait states before an MFMA whose inputs a vector instruction may
-//    just have written (P V only; the Q K inputs come from LDS or registers
-//    written long before);
+//  * no wait states before an MFMA for its A/B inputs: the Q K inputs come
+//    from LDS or from registers written long before, and the slot schedule
+//    packs each 16-key chunk of P at least a slot ahead of its P V MFMAs
+//    (a vector write followed within two wait states by an MFMA read of the
+//    same register would need them; an ISA scan of every built MFMA checks
+//    that none occurs);
 //  * mfma_acc_drain(): >= 18 wait states after the last P V MFMA before any
 //    other instruction touches the accumulators.
 template <int OFF>
@@ -141,10 +144,10 @@ template <class T, int LGKM>
 __device__ __forceinline__ void mfma_o_acc(f32x16_t& acc, u32x4_t a, u32x4_t b) {
   static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
   if constexpr (T::is_bf16)
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                  : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
   else
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\ts_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
                  : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
 }
 
