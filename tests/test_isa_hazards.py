@@ -1,0 +1,64 @@
+"""The hand-ordered parts of the kernels (asm MFMAs, asm loads into LDS and
+registers) rely on wait states and wait counts the compiler cannot see.  These
+tests build the device assembly with the package's own flags and scan it
+(`tests/isa_scan.py`).  CPU only: hipcc cross-compiles for gfx950."""
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from attention_flash_sdpa_amd import build as B
+
+import isa_scan  # tests/ is on sys.path (pytest prepends the test file's folder)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
+                                reason="hipcc not available")
+
+SOURCES = ["prefill.hip", "prefill_o2.hip", "prefill_wide.hip", "prefill_fp8.hip", "decode.hip"]
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    d = tmp_path_factory.mktemp("isa")
+
+    def compile_one(src):
+        out = d / (src + ".s")
+        cmd = [B.HIPCC, "-x", "hip", *B.COMMON, *B.DEVICE, *B.EXTRA.get(src, []), "--cuda-device-only", "-S",
+               os.path.join(B.CSRC, src), "-o", str(out)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return src, out.read_text()
+
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        return dict(ex.map(compile_one, SOURCES))
+
+
+def test_hand_ordered_mfma_results_drained(asm):
+    bad, n = isa_scan.mfma_result_waits(asm["prefill.hip"])
+    assert n > 1000 and not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_vector_writes_before_mfma_inputs(asm, src):
+    bad, n = isa_scan.valu_to_mfma_inputs(asm[src])
+    assert n > 0 and not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", ["prefill.hip", "prefill_o2.hip", "prefill_wide.hip"])
+def test_lds_dma_scalar_base_wait_states(asm, src):
+    bad, n = isa_scan.lds_dma_scalar_base(asm[src])
+    assert n > 0 and not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", ["prefill_fp8.hip", "decode.hip"])
+def test_lds_dma_m0_wait_state(asm, src):
+    bad, _ = isa_scan.lds_dma_scalar_base(asm[src])
+    assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", ["prefill.hip", "prefill_o2.hip"])
+def test_untracked_q_loads_waited_for(asm, src):
+    bad, n = isa_scan.untracked_loads_waited(asm[src])
+    assert n > 0 and not bad, bad[:5]
