@@ -216,12 +216,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 constexpr int kCombineFast = 32;
 
 template <class T, int DV>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int PER = DV / 64;   // value columns per lane (contiguous)
   constexpr int CH = 16;         // splits whose partials are loaded together
   typedef float vec_t __attribute__((ext_vector_type(PER)));
-  const int bh = blockIdx.x;     // b * head_q + h
-  const int lane = threadIdx.x;
+  // one wave per (batch, query head) row, kCombineRows rows per workgroup
+  const int bh = blockIdx.x * kCombineRows + (threadIdx.x >> 6);  // b * head_q + h
+  const int lane = threadIdx.x & 63;
+  if (bh >= a.batch * a.head_q) return;  // no barriers in this kernel
   const int S = a.num_splits;
   const float* ml = a.part_ml + (size_t)bh * S * 2;
   const float* po = a.part_o + (size_t)bh * S * DV + PER * lane;
@@ -309,7 +311,7 @@ static int launch_decode_t(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStr
                      (hipStream_t)stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(plan.combine_groups), dim3(64), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(plan.combine_groups), dim3(64 * kCombineRows), 0, (hipStream_t)stream,
                      a);
   return (int)hipGetLastError();
 }

@@ -245,7 +245,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
   }
   // one workgroup per (batch, split, 4 adjacent KV heads)
   plan->num_groups = (int32_t)(p.batch * S * ceil_div(p.head_kv, kDecodeWaves));
-  plan->combine_groups = (int32_t)((int64_t)p.batch * p.head_q);
+  plan->combine_groups = (int32_t)ceil_div((int64_t)p.batch * p.head_q, kCombineRows);
   plan->lds_bytes = (uint64_t)kDecodeWaves * 2 * kDecodeBlockK * (p.d_qk + p.d_v) * 2;
   const uint64_t po = (uint64_t)p.batch * p.head_q * S * p.d_v * 4;
   const uint64_t pml = (uint64_t)p.batch * p.head_q * S * 2 * 4;

@@ -45,6 +45,7 @@ constexpr int kSplitRanges = 4;    // 4-range prefill: key ranges per workgroup
 constexpr int kSplitBlockK = 32;   // 4-range prefill: keys per K/V block
 constexpr int kDecodeBlockK = 32;  // decode: keys per K/V block
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per CU (gfx950)
+constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows per workgroup
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
 constexpr int kDefaultCUs = 256;

@@ -132,7 +132,7 @@ def _kernels_of(sdpa, w, num_cus=256):
     c = "true" if w.causal else "false"
     if w.decode:
         return [(f"decode_split_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}>", p.num_groups * p.waves_per_group * 64),
-                (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 64)]
+                (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 256)]
     if w.dtype == "fp8_e4m3":
         return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
     if 12 <= p.kernel <= 15 or 24 <= p.kernel <= 27:   # the two-waves-per-SIMD 32-row kernel

@@ -187,9 +187,10 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
  * Phase 1: one workgroup per (batch, KV head, split) streams its key range
  * once for all head_q/head_kv query heads of the group and writes unnormalised
  * partial outputs with their running max and sum into the workspace.
- * Phase 2: one workgroup per (batch, query head) rescales and merges the
- * splits (the same rescale the online softmax applies between K blocks) and
- * writes O (and lse).  Both kernels run on `stream`; nothing synchronises.
+ * Phase 2: one wavefront per (batch, query head), four per workgroup,
+ * rescales and merges the splits (the same rescale the online softmax applies
+ * between K blocks) and writes O (and lse).  Both kernels run on `stream`;
+ * nothing synchronises.
  *   q : [batch, head_q, d_qk]; k, v : [batch, kv_len, head_kv, d_qk|d_v]
  *   o : [batch, head_q, d_v]; lse : [batch, head_q] fp32 or NULL
  *   num_splits : 0 = planner's choice, otherwise the split count to use

@@ -113,7 +113,7 @@ def test_plans_for_workloads():
     # 128 KiB of LDS per workgroup: one per CU, so one round of 256 workgroups
     assert (d.num_splits, d.blocks_per_split, d.block_k) == (8, 32, 32)
     assert d.num_groups * d.waves_per_group == 16 * 8 * 8 and d.num_groups == 256
-    assert d.combine_groups == 16 * 32
+    assert d.combine_groups == 16 * 32 // 4   # four (batch, head) rows per workgroup
     assert d.workspace_bytes == 16 * 32 * 8 * 128 * 4 + 16 * 32 * 8 * 2 * 4
     # d = 64 blocks take 64 KiB: two workgroups per CU
     import dataclasses
