@@ -262,6 +262,8 @@ DECODE_EDGE = [
     (2, 1000, 32, 8, 128, torch.bfloat16, 3),
     (1, 4097, 2, 1, 128, torch.bfloat16, 0),
     (4, 333, 12, 4, 64, torch.float16, 0),
+    (3, 70, 6, 2, 128, torch.bfloat16, 0),     # 18 (batch, head) rows: a partly filled combine workgroup
+    (1, 2000, 6, 3, 64, torch.float16, 40),    # more than 32 splits (looped combine), 6 rows
 ]
 
 
