@@ -42,13 +42,12 @@
 
 namespace sdpa {
 
-// LDS reads issued after those of slot n when its MFMA runs: the reads of
-// slots n+1 .. n+pd (one K fragment per QK slot when there is a next block,
-// two transposed V reads per PV slot).
-template <int NQK, int NSLOT, int PD, bool NEXT>
-__host__ __device__ constexpr int reads_ahead(int n) {
+// LDS reads of slots [a, b]: one K fragment per Q K slot when there is a
+// next block, two transposed V^T halves per P V slot.
+template <int NQK, int NSLOT, bool NEXT>
+__host__ __device__ constexpr int reads_in(int a, int b) {
   int c = 0;
-  for (int m = n + 1; m <= n + PD; ++m) c += m < NQK ? (NEXT ? 1 : 0) : (m < NSLOT ? 2 : 0);
+  for (int m = a; m <= b; ++m) c += m < NQK ? (NEXT ? 1 : 0) : (m < NSLOT ? 2 : 0);
   return c;
 }
 
@@ -429,7 +428,10 @@ void prefill_kernel(const PrefillArgs a) {
     };
     auto slot = [&](auto n_tag) __attribute__((always_inline)) {
       constexpr int N = decltype(n_tag)::value;
-      constexpr int LGKM = reads_ahead<NQK, NSLOT, kPD, NEXT>(N);
+      // one LDS wait per pair of slots: the even slot waits for its own and
+      // the next slot's fragments (the reads of slots N+2 .. N+kPD may stay
+      // in flight; slot N+1+kPD's read is issued later), the odd slot none
+      constexpr int LGKM = N % 2 == 0 ? reads_in<NQK, NSLOT, NEXT>(N + 2, N + kPD) : -1;
       read(std::integral_constant<int, N + kPD>{});
       if constexpr (N < NQK) {
         if constexpr (NEXT) {

@@ -119,36 +119,54 @@ __device__ __forceinline__ u32x2_t ds_read_tr16_at(uint32_t addr) {
 // c = A B (C = 0) / c += A B, scores in VGPRs
 template <class T, int LGKM>
 __device__ __forceinline__ void mfma_s_first(f32x16_t& c, u32x4_t a, u32x4_t b) {
-  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
+  static_assert(LGKM >= -1 && LGKM <= 15, "lgkmcnt range (-1: no wait)");
   if constexpr (T::is_bf16)
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                 : "=&v"(c) : "v"(a), "v"(b), "i"(LGKM));
+    if constexpr (LGKM < 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                   : "=&v"(c) : "v"(a), "v"(b), "i"(LGKM));
   else
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0"
-                 : "=&v"(c) : "v"(a), "v"(b), "i"(LGKM));
+    if constexpr (LGKM < 0)
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0"
+                   : "=&v"(c) : "v"(a), "v"(b), "i"(LGKM));
 }
 template <class T, int LGKM>
 __device__ __forceinline__ void mfma_s_acc(f32x16_t& c, u32x4_t a, u32x4_t b) {
-  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
+  static_assert(LGKM >= -1 && LGKM <= 15, "lgkmcnt range (-1: no wait)");
   if constexpr (T::is_bf16)
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                 : "+v"(c) : "v"(a), "v"(b), "i"(LGKM));
+    if constexpr (LGKM < 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+v"(c) : "v"(a), "v"(b), "i"(LGKM));
   else
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
-                 : "+v"(c) : "v"(a), "v"(b), "i"(LGKM));
+    if constexpr (LGKM < 0)
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                   : "+v"(c) : "v"(a), "v"(b), "i"(LGKM));
 }
 
 // acc += A B with the accumulators in AGPRs (touched only by the matrix core
 // inside the loop, which leaves the VGPRs to scores, fragments and softmax)
 template <class T, int LGKM>
 __device__ __forceinline__ void mfma_o_acc(f32x16_t& acc, u32x4_t a, u32x4_t b) {
-  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt range");
+  static_assert(LGKM >= -1 && LGKM <= 15, "lgkmcnt range (-1: no wait)");
   if constexpr (T::is_bf16)
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                 : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
+    if constexpr (LGKM < 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
   else
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
-                 : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
+    if constexpr (LGKM < 0)
+      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                   : "+a"(acc) : "v"(a), "v"(b), "i"(LGKM));
 }
 
 template <int NT>
