@@ -152,11 +152,14 @@ void prefill_kernel(const PrefillArgs a) {
     vch[i] = ((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16;
   }
   const int last_key = Sk - 1;
-  uint32_t kfo[K_INSTR], vfo[V_INSTR];    // lane byte offsets within a whole block
+  // lane byte offsets within a whole block, less the instruction offset
+  // (i % 4) KiB that load i adds to both of its addresses (four loads share
+  // one M0 value)
+  uint32_t kfo[K_INSTR], vfo[V_INSTR];
 #pragma unroll
-  for (int i = 0; i < K_INSTR; ++i) kfo[i] = krow[i] * kstride + kch[i];
+  for (int i = 0; i < K_INSTR; ++i) kfo[i] = krow[i] * kstride + kch[i] - (i % 4) * 1024;
 #pragma unroll
-  for (int i = 0; i < V_INSTR; ++i) vfo[i] = vrow[i] * vstride + vch[i];
+  for (int i = 0; i < V_INSTR; ++i) vfo[i] = vrow[i] * vstride + vch[i] - (i % 4) * 1024;
   // First key held by the LDS copy of block kb: its own start, except for a
   // block that would run past the last key, which is loaded as the last BK
   // keys instead (its keys before kb*BK, already processed, are masked).  So
@@ -172,7 +175,7 @@ void prefill_kernel(const PrefillArgs a) {
     const int kb = kb0 + j;
     const uint32_t l = lds0 + buf + (wis * K_INSTR + i) * 1024;
     if (whole_tail)
-      global_to_lds_16_sbase(kg + (size_t)row0_of(kb) * kstride, kfo[i], l);
+      global_to_lds_16_sbase(kg + (size_t)row0_of(kb) * kstride, kfo[i] + (i % 4) * 1024, l);
     else
       global_to_lds_16_sbase(kg, (uint32_t)(min(kb * BK + krow[i], last_key) * kstride) + kch[i], l);
   };
@@ -180,7 +183,7 @@ void prefill_kernel(const PrefillArgs a) {
     const int kb = kb0 + j;
     const uint32_t l = lds0 + buf + (wis * V_INSTR + i) * 1024;
     if (whole_tail)
-      global_to_lds_16_sbase(vg + (size_t)row0_of(kb) * vstride, vfo[i], l);
+      global_to_lds_16_sbase(vg + (size_t)row0_of(kb) * vstride, vfo[i] + (i % 4) * 1024, l);
     else
       global_to_lds_16_sbase(vg, (uint32_t)(min(kb * BK + vrow[i], last_key) * vstride) + vch[i], l);
   };
@@ -356,15 +359,16 @@ void prefill_kernel(const PrefillArgs a) {
     const uint32_t kl = lds0 + KB_FREE + wis * K_INSTR * 1024;
     auto dma = [&](auto i_tag) __attribute__((always_inline)) {
       constexpr int I = decltype(i_tag)::value;
-      // the first load from each base waits for its SGPRs, the rest do not
-      if constexpr (I == 0)
-        global_to_lds_16_sbase(vsrc, vfo[I], vl + I * 1024);
-      else if constexpr (I < V_INSTR)
-        global_to_lds_16_sbase_next(vsrc, vfo[I], vl + I * 1024);
-      else if constexpr (I == V_INSTR)
-        global_to_lds_16_sbase(ksrc, kfo[I - V_INSTR], kl + (I - V_INSTR) * 1024);
+      constexpr bool IS_V = I < V_INSTR;
+      constexpr int i = IS_V ? I : I - V_INSTR;
+      // load i goes to LDS (group base) + (i / 4) * 4 KiB + (i % 4) KiB; the
+      // first load from each base waits for its SGPRs, the first of each
+      // group of four for its M0 write, the rest for nothing
+      constexpr int WAITS = i == 0 ? 5 : (i % 4 == 0 ? 1 : 0);
+      if constexpr (IS_V)
+        global_to_lds_16_off<(i % 4) * 1024, WAITS>(vsrc, vfo[i], vl + (i / 4) * 4096);
       else
-        global_to_lds_16_sbase_next(ksrc, kfo[I - V_INSTR], kl + (I - V_INSTR) * 1024);
+        global_to_lds_16_off<(i % 4) * 1024, WAITS>(ksrc, kfo[i], kl + (i / 4) * 4096);
     };
 
     // visible window of block j+1 (masked flavour only)

@@ -324,6 +324,28 @@ __device__ __forceinline__ void global_to_lds_16_sbase_next(const void* sbase, u
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(u), "{m0}"(lds_base) : "memory");
 }
 
+// Direct 16-byte load from base + voffset + OFF into LDS at m0_base + OFF
+// (+16 per lane): the instruction's offset field applies to both addresses,
+// so up to four consecutive 1 KiB loads share one M0 value.  WAITS is the
+// wait states issued first: 5 after the v_readfirstlane that writes a new
+// base, 1 after an M0 write, 0 when neither changed since the previous load.
+template <int OFF, int WAITS>
+__device__ __forceinline__ void global_to_lds_16_off(const void* sbase, uint32_t voffset, uint32_t m0_base) {
+  static_assert(OFF >= 0 && OFF < 4096 && (WAITS == 0 || WAITS == 1 || WAITS == 5), "offset / wait states");
+  const uint64_t p = (uint64_t)(uintptr_t)sbase;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  if constexpr (WAITS == 5)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voffset), "s"(u), "{m0}"(m0_base),
+                 "i"(OFF) : "memory");
+  else if constexpr (WAITS == 1)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voffset), "s"(u), "{m0}"(m0_base),
+                 "i"(OFF) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voffset), "s"(u), "{m0}"(m0_base), "i"(OFF)
+                 : "memory");
+}
+
 // Waits until at most N vector-memory operations of this wave are in flight,
 // then marks the registers of d as written here, so no use of them can be
 // scheduled before the wait.

@@ -39,8 +39,11 @@ def _sregs(tok):
 
 
 def _operands(ins):
+    """Operands of an instruction, without trailing modifiers (offset:, sc0 ...)."""
     parts = ins.split(None, 1)
-    return [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
+    if len(parts) < 2:
+        return []
+    return [o.split()[0] for o in parts[1].split(",") if o.strip()]
 
 
 def _waits(ins):
