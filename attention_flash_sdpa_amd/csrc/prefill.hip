@@ -408,15 +408,17 @@ void prefill_kernel(const PrefillArgs a) {
       constexpr int R0 = decltype(r0_tag)::value, R1 = decltype(r1_tag)::value;
 #pragma unroll
       for (int r = R0; r < R1; ++r) {
-        // the exponent is formed by an asm instruction that reads the score
+        // exponent and exponential in one asm block that reads the score
         // where the MFMA left it (anchoring the work to this slot without
-        // copying the score out of its tile first)
-        float y;
+        // copying the score out of its tile first); the compiler keeps a wait
+        // state between the block and the first use of its result, which the
+        // exponential needs
+        float p;
         if constexpr (MCUR)
-          asm volatile("v_sub_f32 %0, %1, %2" : "=v"(y) : "v"(s_cur[TL][r]), "v"(m_sub));
+          asm volatile("v_sub_f32 %0, %1, %2\n\tv_exp_f32 %0, %0" : "=&v"(p) : "v"(s_cur[TL][r]), "v"(m_sub));
         else
-          asm volatile("v_fma_f32 %0, %1, %2, -%3" : "=v"(y) : "v"(s_cur[TL][r]), "s"(s2), "v"(m_sub));
-        const float p = fast_exp2(y);
+          asm volatile("v_fma_f32 %0, %1, %2, -%3\n\tv_exp_f32 %0, %0"
+                       : "=&v"(p) : "v"(s_cur[TL][r]), "s"(s2), "v"(m_sub));
         if (r & 1) {
           uint32_t pk = pack2<T>(pend[TL], p);
           l_run = add_pair<T>(pk, l_run);

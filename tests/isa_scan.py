@@ -102,6 +102,36 @@ def valu_to_mfma_inputs(text, need=2):
     return bad, n
 
 
+_TRANS = ("v_exp_", "v_log_", "v_rcp_", "v_rsq_", "v_sqrt_", "v_sin_", "v_cos_")
+
+
+def trans_result_use(text, need=1):
+    """A vector instruction reading the result of a transcendental one (v_exp
+    and the like) needs `need` wait states after it."""
+    ins = _instructions(text)
+    bad, n = [], 0
+    for i, t in enumerate(ins):
+        if not t.startswith(_TRANS):
+            continue
+        n += 1
+        dst = _vregs(_operands(t)[0])
+        ws = 0
+        for u in ins[i + 1:i + 4]:
+            if ws >= need:
+                break
+            if u.startswith("s_nop"):
+                ws += _waits(u)
+                continue
+            if u.startswith("v_"):
+                srcs = set()
+                for o in _operands(u)[1:]:
+                    srcs |= _vregs(o)
+                if srcs & dst:
+                    bad.append(f"{t} -> {u} after {ws} wait states")
+            ws += 1
+    return bad, n
+
+
 def lds_dma_scalar_base(text):
     """A direct global->LDS load with an SGPR base needs five wait states after
     a vector instruction (v_readfirstlane) writes that base, and one after the

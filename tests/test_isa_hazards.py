@@ -46,6 +46,12 @@ def test_vector_writes_before_mfma_inputs(asm, src):
     assert n > 0 and not bad, bad[:5]
 
 
+@pytest.mark.parametrize("src", SOURCES)
+def test_transcendental_results_waited_for(asm, src):
+    bad, n = isa_scan.trans_result_use(asm[src])
+    assert n > 0 and not bad, bad[:5]
+
+
 @pytest.mark.parametrize("src", ["prefill.hip", "prefill_o2.hip", "prefill_wide.hip"])
 def test_lds_dma_scalar_base_wait_states(asm, src):
     bad, n = isa_scan.lds_dma_scalar_base(asm[src])
