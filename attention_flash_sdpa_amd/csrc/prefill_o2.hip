@@ -129,16 +129,16 @@ void prefill_o2_kernel(const PrefillArgs a) {
   const char* vg = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * (DV * 2);
   const int kstride = a.head_kv * D * 2;  // bytes between consecutive keys
   const int vstride = a.head_kv * DV * 2;
-  uint32_t kfo[K_INSTR], vfo[V_INSTR];    // byte offsets within a whole block
+  uint32_t kfo[K_INSTR], vfo[V_INSTR];    // byte offsets within a whole block, less (i % 4) KiB
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
     const int slot = (wis * K_INSTR + i) * 64 + lane, r = slot / KCPR;
-    kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
+    kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16) - (i % 4) * 1024;
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int slot = (wis * V_INSTR + i) * 64 + lane, r = slot / VCPR;
-    vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
+    vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16) - (i % 4) * 1024;
   }
   const int last_key = Sk - 1;
   // A block is whole if all its BK keys exist; in a ragged block (the last
@@ -147,9 +147,12 @@ void prefill_o2_kernel(const PrefillArgs a) {
     const uint32_t l = lds0 + buf + wis * K_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = kg + (size_t)kb * BK * kstride;
-      global_to_lds_16_sbase(base, kfo[0], l);
-#pragma unroll
-      for (int i = 1; i < K_INSTR; ++i) global_to_lds_16_sbase_next(base, kfo[i], l + i * 1024);
+      // four 1 KiB loads per M0 value, the instruction offset moving both
+      // addresses (the lane offsets are stored less it)
+      static_for<K_INSTR>([&](auto i_tag) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_tag)::value;
+        global_to_lds_16_off<(i % 4) * 1024, i == 0 ? 5 : (i % 4 == 0 ? 1 : 0)>(base, kfo[i], l + (i / 4) * 4096);
+      });
     } else {
 #pragma unroll
       for (int i = 0; i < K_INSTR; ++i) {
@@ -164,9 +167,12 @@ void prefill_o2_kernel(const PrefillArgs a) {
     const uint32_t l = lds0 + buf + wis * V_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = vg + (size_t)kb * BK * vstride;
-      global_to_lds_16_sbase(base, vfo[0], l);
-#pragma unroll
-      for (int i = 1; i < V_INSTR; ++i) global_to_lds_16_sbase_next(base, vfo[i], l + i * 1024);
+      // four 1 KiB loads per M0 value, the instruction offset moving both
+      // addresses (the lane offsets are stored less it)
+      static_for<V_INSTR>([&](auto i_tag) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_tag)::value;
+        global_to_lds_16_off<(i % 4) * 1024, i == 0 ? 5 : (i % 4 == 0 ? 1 : 0)>(base, vfo[i], l + (i / 4) * 4096);
+      });
     } else {
 #pragma unroll
       for (int i = 0; i < V_INSTR; ++i) {

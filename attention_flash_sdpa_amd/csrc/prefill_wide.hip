@@ -111,21 +111,24 @@ void prefill_wide_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
     const int slot = (wave * K_INSTR + i) * 64 + lane, r = slot / KCPR;
-    kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16);
+    kfo[i] = r * kstride + (((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16) - (i % 4) * 1024;
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / VCPR;
-    vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16);
+    vfo[i] = r * vstride + (((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16) - (i % 4) * 1024;
   }
   const int last_key = Sk - 1;
   auto fill_k = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
     const uint32_t l = lds0 + buf + wave * K_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = kg + (size_t)kb * BK * kstride;
-      global_to_lds_16_sbase(base, kfo[0], l);
-#pragma unroll
-      for (int i = 1; i < K_INSTR; ++i) global_to_lds_16_sbase_next(base, kfo[i], l + i * 1024);
+      // four 1 KiB loads per M0 value, the instruction offset moving both
+      // addresses (the lane offsets are stored less it)
+      static_for<K_INSTR>([&](auto i_tag) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_tag)::value;
+        global_to_lds_16_off<(i % 4) * 1024, i == 0 ? 5 : (i % 4 == 0 ? 1 : 0)>(base, kfo[i], l + (i / 4) * 4096);
+      });
     } else {
 #pragma unroll
       for (int i = 0; i < K_INSTR; ++i) {
@@ -140,9 +143,12 @@ void prefill_wide_kernel(const PrefillArgs a) {
     const uint32_t l = lds0 + buf + wave * V_INSTR * 1024;
     if ((kb + 1) * BK <= Sk) {
       const char* base = vg + (size_t)kb * BK * vstride;
-      global_to_lds_16_sbase(base, vfo[0], l);
-#pragma unroll
-      for (int i = 1; i < V_INSTR; ++i) global_to_lds_16_sbase_next(base, vfo[i], l + i * 1024);
+      // four 1 KiB loads per M0 value, the instruction offset moving both
+      // addresses (the lane offsets are stored less it)
+      static_for<V_INSTR>([&](auto i_tag) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_tag)::value;
+        global_to_lds_16_off<(i % 4) * 1024, i == 0 ? 5 : (i % 4 == 0 ? 1 : 0)>(base, vfo[i], l + (i / 4) * 4096);
+      });
     } else {
 #pragma unroll
       for (int i = 0; i < V_INSTR; ++i) {
