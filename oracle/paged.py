@@ -39,13 +39,15 @@ def gather_sequence(cache, page_table, page_size: int, seq_len: int, b: int):
     return cache[pages, slots]
 
 
-def decode_paged(q, k_cache, v_cache, *, page_table, page_size: int, seq_lens, scale: float):
+def decode_paged(q, k_cache, v_cache, *, page_table, page_size: int, seq_lens, scale: float, kv_len=None):
     """fp64 decode (one query token per sequence) over paged and/or
     variable-length keys.
 
     q: [B, Hq, D]; k_cache/v_cache: [num_pages, page_size, Hkv, D|Dv] when
     page_table ([B, pages_per_seq] ints) is given, else [B, kv_len, Hkv, ...];
-    seq_lens: [B] ints, or None for the full kv_len.
+    seq_lens: [B] ints, or None for kv_len keys in every sequence, kv_len
+    defaulting to what a sequence can hold: the dense cache's length, or a
+    full table row (pages_per_seq * page_size).
     Returns {"out": [B, Hq, Dv] float64, "lse": [B, Hq]} with O = 0 and
     lse = -inf for a sequence without keys.
     """
@@ -54,7 +56,10 @@ def decode_paged(q, k_cache, v_cache, *, page_table, page_size: int, seq_lens, s
     B, Hq, D = (int(s) for s in q.shape)
     Dv = int(v_cache.shape[-1])
     if seq_lens is None:
-        seq_lens = [int(k_cache.shape[1])] * B
+        if kv_len is None:
+            kv_len = (int(k_cache.shape[1]) if page_table is None
+                      else int(np.asarray(page_table).shape[1]) * page_size)
+        seq_lens = [int(kv_len)] * B
     out = np.zeros((B, Hq, Dv), dtype=np.float64)
     lse = np.full((B, Hq), -np.inf, dtype=np.float64)
     for b in range(B):

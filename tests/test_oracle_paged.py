@@ -43,6 +43,22 @@ def test_identity_table_equals_contiguous_definition():
     assert np.array_equal(got["lse"], want["lse"][:, :, 0])
 
 
+def test_without_lengths_every_sequence_is_full():
+    """No seq_lens: a paged sequence holds its whole table row (not one page),
+    or kv_len keys when kv_len is given."""
+    q, k, v = _contiguous(Sk=192)
+    kp, table = _paginate(k, 32, 6, perm_seed=2)
+    vp, _ = _paginate(v, 32, 6, perm_seed=2)
+    want = oracle.sdpa(q[:, None], k, v, scale=0.125, causal=False)
+    got = paged.decode_paged(q, kp, vp, page_table=table, page_size=32, seq_lens=None, scale=0.125)
+    assert np.array_equal(got["out"], want["out"][:, 0])
+    short = oracle.sdpa(q[:, None], k[:, :100], v[:, :100], scale=0.125, causal=False)
+    got = paged.decode_paged(q, kp, vp, page_table=table, page_size=32, seq_lens=None, scale=0.125, kv_len=100)
+    assert np.array_equal(got["out"], short["out"][:, 0])
+    got = paged.decode_paged(q, k, v, page_table=None, page_size=0, seq_lens=None, scale=0.125)
+    assert np.array_equal(got["out"], want["out"][:, 0])
+
+
 def test_shuffled_physical_pages_do_not_change_the_result():
     q, k, v = _contiguous(seed=1)
     kp, table = _paginate(k, 64, 4, perm_seed=5)
