@@ -1,9 +1,10 @@
 """MI355X-native fused scaled-dot-product-attention forward.
 
 Python front end of the C-ABI library ``libsdpa_mi355x.so`` (see
-``include/sdpa.h``): ``prefill`` (causal or full, GQA) and ``decode`` (two-phase
-split-KV), plus the host planner ``plan``.  The compute runs in hand-written
-HIP kernels for gfx950; PyTorch only provides device memory and streams.
+``include/sdpa.h``): ``prefill`` (causal or full, GQA), ``decode`` (two-phase
+split-KV), ``decode_paged`` (variable-length and paged caches) and the host
+planner ``plan``.  The compute runs in hand-written HIP kernels for gfx950;
+PyTorch only provides device memory and streams.
 """
 from .binding import (  # noqa: F401
     BF16,
@@ -13,6 +14,7 @@ from .binding import (  # noqa: F401
     Problem,
     SdpaError,
     decode,
+    decode_paged,
     decode_workspace,
     load,
     loop_counts,
@@ -21,5 +23,5 @@ from .binding import (  # noqa: F401
     prefill,
 )
 
-__all__ = ["prefill", "decode", "decode_workspace", "plan", "loop_counts", "make_problem", "load", "Problem", "Plan",
-           "SdpaError", "F16", "BF16", "FP8_E4M3"]
+__all__ = ["prefill", "decode", "decode_paged", "decode_workspace", "plan", "loop_counts", "make_problem", "load",
+           "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]

@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
-    "sdpa_loop_counts",
+    "sdpa_decode_paged_fwd", "sdpa_loop_counts",
 )
 
 
@@ -92,6 +92,9 @@ def load(path: str = LIB_PATH):
     lib.sdpa_prefill_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
     lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    i32 = ctypes.c_int32
+    lib.sdpa_decode_paged_fwd.restype = ctypes.c_int
+    lib.sdpa_decode_paged_fwd.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -179,24 +182,37 @@ class DecodeWorkspace:
     nbytes: int
 
 
-def decode_workspace(q, k, v, *, num_splits=0, descale=(1.0, 1.0, 1.0)):
-    """Allocates the decode workspace for these shapes (reusable across calls)."""
+def decode_workspace(q, k, v, *, num_splits=0, descale=(1.0, 1.0, 1.0), kv_len=None):
+    """Allocates the decode workspace for these shapes (reusable across calls);
+    ``kv_len`` overrides the key count read from ``k`` (paged caches)."""
     import torch
 
-    pr = _decode_problem(q, k, v, 1.0, descale, None)
+    pr = _decode_problem(q, k, v, 1.0, descale, None, kv_len)
+    plan(pr, decode=True, num_splits=num_splits)  # raises for an invalid problem
     n = load().sdpa_decode_workspace_bytes(ctypes.byref(pr), int(num_splits))
-    if n == 0:
-        raise SdpaError(2, "invalid decode problem")
-    return DecodeWorkspace(torch.empty(n, dtype=torch.uint8, device=q.device), n)
+    # an empty batch needs none; keep a valid aligned pointer all the same
+    return DecodeWorkspace(torch.empty(max(n, 256), dtype=torch.uint8, device=q.device), n)
 
 
-def _decode_problem(q, k, v, scale, descale, out):
+def _decode_problem(q, k, v, scale, descale, out, kv_len=None):
     B, Hq, D = q.shape
     _, Sk, Hkv, _ = k.shape
+    if kv_len is not None:
+        Sk = kv_len
     Dv = v.shape[-1]
     od = _dtype_code(out) if out is not None else _dtype_code(q)
     return make_problem(batch=B, q_len=1, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=Dv,
                         in_dtype=_dtype_code(q), out_dtype=od, causal=False, scale=scale, descale=descale)
+
+
+def _check_caches(q, k, v, *, dense):
+    """The kernels index K and V with one row geometry and read d_qk from q."""
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches 4-D")
+    if k.shape[:3] != v.shape[:3] or k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"cache shapes disagree: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if dense and k.shape[0] != q.shape[0]:
+        raise ValueError("dense caches need one row of keys per sequence")
 
 
 def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=None, descale=(1.0, 1.0, 1.0),
@@ -210,6 +226,7 @@ def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=N
     for t in (q, k, v):
         if not t.is_contiguous() or not t.is_cuda:
             raise ValueError("q, k, v must be contiguous device tensors")
+    _check_caches(q, k, v, dense=True)
     if out is None:
         out = torch.empty(B, Hq, Dv, dtype=q.dtype, device=q.device)
     if scale is None:
@@ -220,4 +237,51 @@ def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=N
         workspace = decode_workspace(q, k, v, num_splits=num_splits, descale=descale)
     _check(lib.sdpa_decode_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(num_splits),
                                _ptr(workspace.tensor), workspace.nbytes, _stream_handle(stream)))
+    return out
+
+
+def decode_paged(q, k_cache, v_cache, *, page_table=None, seq_lens=None, kv_len=None, scale=None, out=None,
+                 lse=None, num_splits=0, workspace=None, descale=(1.0, 1.0, 1.0), stream=None):
+    """Decode over variable-length and/or paged caches (``sdpa_decode_paged_fwd``).
+
+    q [B, Hq, D].  With ``page_table`` (int32 [B, pages_per_seq] on the
+    device) the caches are pools [num_pages, page_size, Hkv, D|Dv] and
+    ``kv_len`` (default pages_per_seq * page_size) bounds every sequence;
+    without it they are dense [B, kv_len, Hkv, D|Dv].  ``seq_lens`` (int32
+    [B] on the device, or None) gives each sequence's key count."""
+    import torch
+
+    B, Hq, D = q.shape
+    Dv = v_cache.shape[-1]
+    for t in (q, k_cache, v_cache, page_table, seq_lens):
+        if t is not None and (not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("q, caches, page_table and seq_lens must be contiguous device tensors")
+    for t in (page_table, seq_lens):
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError("page_table and seq_lens must be int32")
+    _check_caches(q, k_cache, v_cache, dense=page_table is None)
+    if page_table is not None:
+        num_pages, page_size = int(k_cache.shape[0]), int(k_cache.shape[1])
+        pages_per_seq = int(page_table.shape[1])
+        if page_table.shape[0] != B:
+            raise ValueError("page_table must have one row per sequence")
+        if kv_len is None:
+            kv_len = pages_per_seq * page_size
+    else:
+        num_pages = page_size = pages_per_seq = 0
+        kv_len = int(k_cache.shape[1]) if kv_len is None else kv_len
+    if seq_lens is not None and seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be [B]")
+    if out is None:
+        out = torch.empty(B, Hq, Dv, dtype=q.dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    pr = _decode_problem(q, k_cache, v_cache, scale, descale, out, kv_len)
+    lib = load()
+    if workspace is None:
+        workspace = decode_workspace(q, k_cache, v_cache, num_splits=num_splits, descale=descale, kv_len=kv_len)
+    _check(lib.sdpa_decode_paged_fwd(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                     _ptr(page_table), num_pages, page_size, pages_per_seq, _ptr(out), _ptr(lse),
+                                     int(num_splits), _ptr(workspace.tensor), workspace.nbytes,
+                                     _stream_handle(stream)))
     return out

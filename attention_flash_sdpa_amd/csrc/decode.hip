@@ -20,6 +20,18 @@
 // Phase 2 (decode_combine_kernel): one wavefront per (batch, query head)
 // merges the splits: M = max_s m_s, w_s = 2^(m_s - M), O = sum w_s O_s /
 // sum w_s l_s (0 when nothing was visible), lse = ln2 * (M + log2 den).
+//
+// Variable-length and paged caches (the mainloop's optional paged-KV
+// arguments and its logical-to-physical K tile helper, "Xe SDPA Forward
+// Mainloop", sections "Runtime args / params" and "Helpers"; its variable-
+// length launch mode, section "Launcher -> kernel"): sequence b holds
+// seq_lens[b] keys, and with a page table its keys p*page_size ..
+// (p+1)*page_size - 1 sit in physical page page_table[b][p] of a
+// [num_pages, page_size, head_kv, d] pool.  page_size is a multiple of the
+// 32-key block, so every block lies in one page and costs one table entry,
+// read from a register that holds 64 of the split's entries (one per lane).
+// An entry outside [0, num_pages) is never dereferenced: page 0 is read in
+// its place and the affected rows come out NaN.
 #include <math.h>
 
 #include "sdpa_device.h"
@@ -27,7 +39,7 @@
 
 namespace sdpa {
 
-template <class T, int D, int DV>
+template <class T, int D, int DV, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   constexpr int BK = kDecodeBlockK;           // 32 keys per block (two 16-key tiles)
   constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
@@ -55,8 +67,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   if (g >= a.head_kv) return;  // no barriers in this kernel
   const int G = a.group;
   const int Sk = a.kv_len;
-  const int k_begin = min(split * a.blocks_per_split * BK, Sk);
-  const int k_end = min(k_begin + a.blocks_per_split * BK, Sk);
+  // this sequence's keys: kv_len, or its own length clamped to [0, kv_len]
+  const int seq_len = a.seq_lens == nullptr ? Sk : min(max(a.seq_lens[b], 0), Sk);
+  const int k_begin = min(split * a.blocks_per_split * BK, seq_len);
+  const int k_end = min(k_begin + a.blocks_per_split * BK, seq_len);
   const int nb = (k_end - k_begin + BK - 1) / BK;
 
   const int n16 = lane & 15;   // query head within the group (MFMA N index)
@@ -78,8 +92,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   // direct global -> LDS fill of one block: instruction i covers rows
   // [i*1024/ROW, ...), lane p the 16-byte slot p % CPR of its row, which holds
   // chunk slot ^ swizzle(row) -- so 16 (or 8) lanes read one whole key row
-  const char* kbase = (const char*)a.k + ((size_t)b * Sk * a.head_kv + g) * KROW;
-  const char* vbase = (const char*)a.v + ((size_t)b * Sk * a.head_kv + g) * VROW;
+  // (dense: row 0 of sequence b; paged: row 0 of the pool, page p starting at
+  // row p * page_size -- the rows of one page follow each other as in a
+  // dense sequence)
+  const size_t seq_rows = PAGED ? 0 : (size_t)b * Sk;
+  const char* kbase = (const char*)a.k + (seq_rows * a.head_kv + g) * KROW;
+  const char* vbase = (const char*)a.v + (seq_rows * a.head_kv + g) * VROW;
   const size_t kstride = (size_t)a.head_kv * KROW, vstride = (size_t)a.head_kv * VROW;
   int krow[K_INSTR], kcol[K_INSTR], vrow[V_INSTR], vcol[V_INSTR];
 #pragma unroll
@@ -94,15 +112,56 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     vrow[i] = r;
     vcol[i] = ((slot % VCPR) ^ (int)swz_decode<VCPR>(r)) * 16;
   }
-  const int last_key = Sk - 1;
+  const int last_key = seq_len - 1;
+
+  // paged: table entries of pages pt_first .. pt_first + 63 of this sequence
+  // (lane i holds entry pt_first + i, clamped to the table row), the page and
+  // row within it of the next block to fill, and whether any entry used was
+  // out of range.  Fills run in key order, so the cursor just advances.
+  int pt_first = 0, pt_page = 0, pt_row = 0;
+  int pt_vals = 0;
+  bool pt_bad = false;
+  const int32_t* pt = PAGED ? a.page_table + (size_t)b * a.pages_per_seq : nullptr;
+  if constexpr (PAGED) {
+    if (nb > 0) {
+      pt_page = k_begin / a.page_size;
+      pt_row = k_begin - pt_page * a.page_size;
+      pt_first = pt_page;
+      pt_vals = pt[min(pt_first + lane, a.pages_per_seq - 1)];
+    }
+  }
+
   auto issue_fill = [&](int key0, int stage) __attribute__((always_inline)) {
     const uint32_t kl = lds_w + stage * STAGE, vl = kl + KBYTES;
+    // rows past the sequence end repeat its last key (masked later); they stay
+    // in the block's page because blocks start at multiples of 32 keys
+    const int lim = last_key - key0;
+    size_t row0 = (size_t)key0;
+    if constexpr (PAGED) {
+      if (pt_page - pt_first >= 64) {  // next 64 entries (long splits only)
+        pt_first += 64;
+        pt_vals = (int)global_load_dword_sync(pt + min(pt_first + lane, a.pages_per_seq - 1));
+      }
+      int phys = __builtin_amdgcn_readlane(pt_vals, pt_page - pt_first);
+      if ((uint32_t)phys >= (uint32_t)a.num_pages) {
+        pt_bad = true;
+        phys = 0;
+      }
+      row0 = (size_t)phys * a.page_size + pt_row;
+      pt_row += BK;
+      if (pt_row == a.page_size) {
+        pt_row = 0;
+        ++pt_page;
+      }
+    }
+    const char* kb = kbase + row0 * kstride;
+    const char* vb = vbase + row0 * vstride;
 #pragma unroll
     for (int i = 0; i < K_INSTR; ++i)
-      global_to_lds_16(kbase + (size_t)min(key0 + krow[i], last_key) * kstride + kcol[i], kl + i * 1024);
+      global_to_lds_16(kb + (size_t)min(krow[i], lim) * kstride + kcol[i], kl + i * 1024);
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i)
-      global_to_lds_16(vbase + (size_t)min(key0 + vrow[i], last_key) * vstride + vcol[i], vl + i * 1024);
+      global_to_lds_16(vb + (size_t)min(vrow[i], lim) * vstride + vcol[i], vl + i * 1024);
   };
 
   // K fragment (A operand of 16x16x32): key row 16t + l%16, slot 4s + l/16
@@ -200,6 +259,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   // partial results: unnormalised O^T (lane holds head n16, values 16t + 4*gq + r)
   float l_tot = l_run + xor_lane(l_run, 16);
   l_tot += xor_lane(l_tot, 32);
+  if constexpr (PAGED) {
+    if (pt_bad) {  // a page-table entry was out of range: poison the rows
+      l_tot = __builtin_nanf("");
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{l_tot, l_tot, l_tot, l_tot};
+    }
+  }
   if (head_ok) {
     const size_t pidx = ((size_t)b * a.head_q + h) * S + split;
     float* po = a.part_o + pidx * DV + 4 * gq;
@@ -258,7 +324,7 @@ __global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const
     } else {
       o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
     }
-    if (a.lse != nullptr && lane == 0) a.lse[bh] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    if (a.lse != nullptr && lane == 0) a.lse[bh] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
     return;
   }
 
@@ -302,13 +368,17 @@ __global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const
   } else {
     o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
   }
-  if (a.lse != nullptr && lane == 0) a.lse[bh] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
 }
 
 template <class T, int D>
 static int launch_decode_t(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, D, D>), dim3(plan.num_groups), dim3(64 * kDecodeWaves), 0,
-                     (hipStream_t)stream, a);
+  if (a.page_table != nullptr)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, D, true>), dim3(plan.num_groups), dim3(64 * kDecodeWaves), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, D, false>), dim3(plan.num_groups), dim3(64 * kDecodeWaves), 0,
+                       (hipStream_t)stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(plan.combine_groups), dim3(64 * kCombineRows), 0, (hipStream_t)stream,

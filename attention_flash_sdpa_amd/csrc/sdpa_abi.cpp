@@ -156,14 +156,12 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
   return hip_status(launch_prefill(a, plan, p.causal != 0, (ihipStream_t*)stream), "prefill launch");
 }
 
-sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
-                              void* o, float* lse, int num_splits, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  clear_error();
-  if (problem == nullptr) {
-    set_error("problem must not be NULL");
-    return SDPA_ERR_NULL_PTR;
-  }
+// Shared by the dense and the paged decode entry points; cache rows per
+// page and the table are checked by the caller.
+static sdpa_status_t decode_common(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
+                                   void* o, float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                                   void* stream, const int32_t* seq_lens, const int32_t* page_table,
+                                   int32_t num_pages, int32_t page_size, int32_t pages_per_seq) {
   const sdpa_problem_t& p = *problem;
   sdpa_plan_t plan;
   sdpa_status_t st = make_plan(p, true, device_cus(), num_splits, &plan);
@@ -174,8 +172,8 @@ sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, cons
     return SDPA_ERR_NULL_PTR;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
-      ((uintptr_t)lse & 3u)) {
-    set_error("q, k, v, o, workspace must be 16-byte aligned and lse 4-byte aligned");
+      ((uintptr_t)lse & 3u) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)page_table & 3u)) {
+    set_error("q, k, v, o, workspace must be 16-byte aligned and lse, seq_lens, page_table 4-byte aligned");
     return SDPA_ERR_MISALIGNED;
   }
   if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
@@ -202,7 +200,55 @@ sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, cons
   a.split_waves = plan.num_splits;
   a.s2 = (float)((double)p.scale * 1.4426950408889634 * (double)p.q_descale * (double)p.k_descale);
   a.v_descale = p.v_descale;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
   return hip_status(launch_decode(a, plan, (ihipStream_t*)stream), "decode launch");
+}
+
+sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
+                              void* o, float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  return decode_common(problem, q, k, v, o, lse, num_splits, workspace, workspace_bytes, stream, nullptr, nullptr,
+                       0, 0, 0);
+}
+
+sdpa_status_t sdpa_decode_paged_fwd(const sdpa_problem_t* problem, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t num_pages, int32_t page_size, int32_t pages_per_seq, void* o,
+                                    float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  const sdpa_problem_t& p = *problem;
+  if (page_table != nullptr && p.batch > 0 && p.kv_len > 0) {
+    if (page_size <= 0 || page_size % kDecodeBlockK != 0) {
+      set_error("page_size must be a positive multiple of %d (got %d)", kDecodeBlockK, page_size);
+      return SDPA_ERR_BAD_SHAPE;
+    }
+    if (num_pages <= 0 || pages_per_seq <= 0 || (int64_t)pages_per_seq * page_size < p.kv_len) {
+      set_error("need num_pages > 0 and pages_per_seq * page_size >= kv_len (num_pages=%d, pages_per_seq=%d, "
+                "page_size=%d, kv_len=%d)", num_pages, pages_per_seq, page_size, p.kv_len);
+      return SDPA_ERR_BAD_SHAPE;
+    }
+    if ((int64_t)num_pages * page_size > INT32_MAX || (int64_t)p.batch * pages_per_seq > INT32_MAX) {
+      set_error("page pool or table too large (num_pages=%d, page_size=%d, pages_per_seq=%d)", num_pages,
+                page_size, pages_per_seq);
+      return SDPA_ERR_BAD_SHAPE;
+    }
+  }
+  return decode_common(problem, q, k_cache, v_cache, o, lse, num_splits, workspace, workspace_bytes, stream,
+                       seq_lens, page_table, num_pages, page_size, pages_per_seq);
 }
 
 }  // extern "C"

@@ -314,6 +314,17 @@ __device__ __forceinline__ void global_load_16_untracked(u32x4_t& d, const void*
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=&v"(d) : "v"(p), "i"(OFF) : "memory");
 }
 
+// One dword load that waits for every outstanding vector-memory load of the
+// wave (including untracked direct-to-LDS ones) before returning.  Meant for
+// rare loads inside an explicitly counted load pipeline: a compiler-tracked
+// load there would make the compiler wait on every path through the loop,
+// this waits only where it runs.
+__device__ __forceinline__ uint32_t global_load_dword_sync(const void* p) {
+  uint32_t d;
+  asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=&v"(d) : "v"(p) : "memory");
+  return d;
+}
+
 // As global_to_lds_16_sbase, for a later load from the same base: the base
 // SGPRs were written (by the first load's v_readfirstlane) at least five
 // instructions earlier, so only the M0 write needs its wait state.

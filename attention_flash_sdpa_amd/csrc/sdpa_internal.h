@@ -90,6 +90,11 @@ struct DecodeArgs {
   int32_t num_splits, blocks_per_split, split_waves;
   float s2;
   float v_descale;
+  // variable-length and paged key/value caches (both NULL: every sequence
+  // holds kv_len keys in a dense [batch, kv_len, head_kv, d] cache)
+  const int32_t* seq_lens;    // [batch] keys per sequence, or NULL
+  const int32_t* page_table;  // [batch, pages_per_seq] physical page ids, or NULL
+  int32_t num_pages, page_size, pages_per_seq;
 };
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);

@@ -134,3 +134,38 @@ def make_qkv(w: Workload, *, seed: int | None = None, kv_set: int = 0, q_len: in
     del k32
     v, sv_ = cast(v32, w.dtype)
     return q, k, v, (sq_, sk_, sv_)
+
+
+def paginate(k: torch.Tensor, v: torch.Tensor, page_size: int, *, seed: int, spare_pages: int = 0,
+             fill: float = float("nan")):
+    """Scatters dense caches k, v [B, Sk, Hkv, D|Dv] into page pools
+    [B * P + spare_pages, page_size, Hkv, D|Dv] (P = ceil(Sk / page_size)) in a
+    seeded random physical order.  Returns (k_pool, v_pool, page_table) with
+    page_table int32 [B, P]: logical page p of sequence b is pool page
+    page_table[b, p].  Slots past Sk and the spare pages hold ``fill`` (NaN by
+    default, so a read of a slot no sequence owns shows in the output)."""
+    B, Sk, Hkv, D = k.shape
+    Dv = v.shape[-1]
+    P = -(-Sk // page_size)
+    n = B * P + spare_pages
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(seed))[:B * P]
+    table = perm.reshape(B, P).to(torch.int32)
+    kp = torch.full((n, page_size, Hkv, D), fill, dtype=torch.float32).to(k.dtype)
+    vp = torch.full((n, page_size, Hkv, Dv), fill, dtype=torch.float32).to(v.dtype)
+    for b in range(B):
+        for p in range(P):
+            lo, hi = p * page_size, min(Sk, (p + 1) * page_size)
+            kp[table[b, p], :hi - lo] = k[b, lo:hi]
+            vp[table[b, p], :hi - lo] = v[b, lo:hi]
+    return kp, vp, table
+
+
+def length_mix(batch: int, kv_len: int, *, seed: int) -> torch.Tensor:
+    """Seeded per-sequence key counts in [0, kv_len] for variable-length
+    decode: the first sequences take the edge values 0, 1 and kv_len, the rest
+    are uniform draws (int32 [batch])."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(0, kv_len + 1, (batch,), generator=g)
+    edges = [0, 1, kv_len][:batch]
+    lens[:len(edges)] = torch.tensor(edges)
+    return lens.to(torch.int32)

@@ -200,6 +200,38 @@ sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, cons
                               const void* v, void* o, float* lse, int num_splits,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode over variable-length and/or paged key/value caches.  The mainloop
+ * page ("Xe SDPA Forward Mainloop", section "Runtime args / params") lists
+ * an optional page table, page size and per-sequence page counts among its
+ * runtime arguments, section "Helpers" a logical-to-physical K tile lookup,
+ * and section "Launcher -> kernel" a variable-length mode; the pages fix no
+ * layout, so this one is taken:
+ *   page_table == NULL : k_cache, v_cache are dense [batch, kv_len, head_kv,
+ *       d_qk|d_v] as for sdpa_decode_fwd (num_pages, page_size,
+ *       pages_per_seq ignored).
+ *   page_table != NULL : k_cache, v_cache are pools [num_pages, page_size,
+ *       head_kv, d_qk|d_v]; page_table is device int32 [batch, pages_per_seq]
+ *       and keys p*page_size .. (p+1)*page_size - 1 of sequence b sit in
+ *       physical page page_table[b * pages_per_seq + p].  page_size must be a
+ *       positive multiple of 32, pages_per_seq * page_size >= kv_len.
+ *   seq_lens : device int32 [batch], sequence b attends to its first
+ *       seq_lens[b] keys (clamped to [0, kv_len]; 0 gives O = 0 and
+ *       lse = -inf), or NULL for kv_len keys each.
+ * problem->kv_len is the longest sequence the call allows; split count and
+ * workspace follow it exactly as for sdpa_decode_fwd (the same
+ * sdpa_decode_workspace_bytes).  Only the table entries of pages holding a
+ * sequence's first seq_lens[b] keys are read.  The table lives on the device
+ * and is not checked on the host: an entry outside [0, num_pages) is never
+ * dereferenced (page 0 is read in its place) and turns that sequence's O and
+ * lse rows (all heads) into NaN.  Pointers 4-byte (tables) or 16-byte (data,
+ * workspace) aligned; other arguments and errors as for sdpa_decode_fwd. */
+sdpa_status_t sdpa_decode_paged_fwd(const sdpa_problem_t* problem, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t num_pages, int32_t page_size, int32_t pages_per_seq,
+                                    void* o, float* lse, int num_splits, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -190,3 +190,53 @@ def test_null_and_workspace_errors_before_any_launch():
     # empty problems are successful no-ops with no pointer checks
     empty = _problem(w, q_len=0)
     assert lib.sdpa_prefill_fwd(ctypes.byref(empty), null, null, null, null, null, null, 0, null) == 0
+
+
+def test_paged_decode_argument_errors_before_any_launch():
+    """sdpa_decode_paged_fwd checks the page geometry, alignment and workspace
+    on the host and returns before enqueuing anything (so this runs on the CPU)."""
+    import ctypes
+
+    lib = sdpa.load()
+    dw = inputs.WORKLOADS["splitkv_decode_bf16"]
+    dp = _problem(dw)
+    null = ctypes.c_void_p(0)
+    a = ctypes.c_void_p(0x1000)
+    need = lib.sdpa_decode_workspace_bytes(ctypes.byref(dp), 0)
+    pages = dw.kv_len // 64
+
+    def call(problem=dp, table=a, lens=null, num_pages=dw.batch * pages, page_size=64, per_seq=pages,
+             ws=a, ws_bytes=need):
+        return lib.sdpa_decode_paged_fwd(None if problem is None else ctypes.byref(problem), a, a, a, lens, table,
+                                         num_pages, page_size, per_seq, a, null, 0, ws, ws_bytes, null)
+
+    assert call(problem=None) == 1
+    assert call(page_size=48) == 2                      # not a multiple of the 32-key block
+    assert b"page_size" in lib.sdpa_last_error()
+    assert call(page_size=0) == 2
+    assert call(per_seq=pages - 1) == 2                 # table row shorter than kv_len
+    assert call(num_pages=0) == 2
+    assert call(num_pages=2 ** 30) == 2                 # pool rows overflow int32
+    assert call(table=ctypes.c_void_p(0x1002)) == 5     # table not 4-byte aligned
+    assert call(lens=ctypes.c_void_p(0x1001)) == 5
+    assert call(ws_bytes=need - 16) == 6
+    # geometry is ignored without a table (dense variable-length form)
+    assert call(table=null, page_size=48, ws_bytes=need - 16) == 6
+    # an empty batch is a successful no-op
+    assert call(problem=_problem(dw, batch=0), table=null, ws=null, ws_bytes=0) == 0
+
+
+def test_paged_binding_rejects_bad_tensors():
+    import torch
+
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    pool = torch.zeros(4, 64, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdpa.decode_paged(q, pool, pool, page_table=torch.zeros(2, 2, dtype=torch.int32))  # host tensors
+    with pytest.raises(ValueError):
+        binding._check_caches(q, pool, pool[:3], dense=False)          # V pool smaller than K pool
+    with pytest.raises(ValueError):
+        binding._check_caches(q, pool, pool, dense=True)               # 4 dense rows for 2 sequences
+    with pytest.raises(ValueError):
+        binding._check_caches(q, pool[..., :64], pool, dense=False)    # head dim differs from q
+    binding._check_caches(q, pool, pool, dense=False)
