@@ -124,14 +124,16 @@ def _problem(sdpa, w):
                              out_dtype=code[w.out_dtype], causal=w.causal, scale=w.scale)
 
 
-def _kernels_of(sdpa, w, num_cus=256):
+def _kernels_of(sdpa, w, num_cus=256, paged=False):
     """(kernel name, grid size in work-items) of each launch one call of
-    workload `w` makes, from the host planner."""
+    workload `w` makes, from the host planner (`paged`: decode through a page
+    table)."""
     p = sdpa.plan(_problem(sdpa, w), decode=w.decode, num_cus=num_cus)
     t = {"f16": "F16", "bf16": "Bf16"}.get(w.dtype)
     c = "true" if w.causal else "false"
     if w.decode:
-        return [(f"decode_split_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}>", p.num_groups * p.waves_per_group * 64),
+        return [(f"decode_split_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {'true' if paged else 'false'}>",
+                 p.num_groups * p.waves_per_group * 64),
                 (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 256)]
     if w.dtype == "fp8_e4m3":
         return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
@@ -206,8 +208,12 @@ def _summarize_trace(d):
     rows = _read_csv(os.path.join(d, "run_kernel_trace.csv"))
     cmd = open(os.path.join(d, "command.txt")).read().strip() if os.path.exists(os.path.join(d, "command.txt")) \
         else "(command not recorded)"
-    for wname, w in inputs.WORKLOADS.items():
-        for kname, grid in _kernels_of(sdpa, w):
+    todo = [(wname, w, False) for wname, w in inputs.WORKLOADS.items()]
+    todo.append(("splitkv_decode_bf16_paged64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
+    for wname, w, paged in todo:
+        for kname, grid in _kernels_of(sdpa, w, paged=paged):
+            if paged and "true>" not in kname:
+                continue  # the combine kernel is the dense one
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
                     if kname in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid]
             if not durs:
@@ -377,6 +383,36 @@ def main():
     decode_err = float(np.abs(dgot - dref).max())
     del sets
 
+    # ------- the same decode over a paged cache: 64-key pages, shuffled -------
+    from oracle import paged as opaged
+
+    PS = 64
+    P = dw.kv_len // PS
+    kp0, vp0, table0 = inputs.paginate(dk0, dv0, PS, seed=dw.seed + 1)
+    psets = [(kp0.to(dev), vp0.to(dev), table0.to(dev))]
+    for s in range(1, dw.kv_sets):
+        g = torch.Generator(device=dev).manual_seed(dw.seed + 100 * s)
+        pk, pv = (torch.randn(t.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                  for t in (kp0, vp0))
+        perm = torch.randperm(dw.batch * P, generator=torch.Generator().manual_seed(dw.seed + 100 * s + 1))
+        psets.append((pk, pv, perm.reshape(dw.batch, P).to(torch.int32).to(dev)))
+    full = torch.full((dw.batch,), dw.kv_len, dtype=torch.int32, device=dev)
+
+    def pstep(i):
+        pk, pv, pt = psets[i % len(psets)]
+        sdpa.decode_paged(dqd, pk, pv, page_table=pt, seq_lens=full, scale=dw.scale, out=dout, workspace=ws)
+
+    peager_ms = _time(pstep, args.decode_steps, args.warmup, stream)
+    pms = _graph_time(pstep, args.decode_steps, args.warmup, period=len(psets))
+    pbytes = dbytes + table0.numel() * 4 + dw.batch * 4
+    pgbs = pbytes / (pms * 1e-3) / 1e9
+    pstep(0)
+    torch.cuda.synchronize()
+    pref = opaged.decode_paged(dq.reshape(dw.batch, dw.head_q, dw.d_qk), kp0, vp0, page_table=table0,
+                               page_size=PS, seq_lens=None, scale=dw.scale)["out"]
+    paged_err = float(np.abs(dout.double().cpu().numpy() - pref).max())
+    del psets, kp0, vp0
+
     # ---------------- other prefill workloads (context lines) ----------------
     extra = {}
     for name in ("single_head_f16_128", "unaligned_full_bf16", "tiny_causal_bf16", "mla_fp8_causal_prefill"):
@@ -447,6 +483,15 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dgbs / PEAK_HBM_GBS, 5), "traffic": dtraffic},
             "parity": {"max_abs_err": decode_err},
+        },
+        "decode_paged": {
+            "workload": f"{dw.name} in {PS}-key pages (shuffled physical order, every sequence full)",
+            "value": round(pgbs, 2), "unit": "GB/s", "ms_per_call": round(pms, 6),
+            "eager_ms_per_call": round(peager_ms, 6), "steps": args.decode_steps, "kv_sets": dw.kv_sets,
+            "algorithmic_bytes": pbytes,
+            "roofline": {"bound": "hbm", "achieved": round(pgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
+            "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
         },
         "other_workloads": extra,
         "launch_floor_us": {"eager": round(floor_eager * 1e3, 3), "graph": round(floor_graph * 1e3, 3)},
