@@ -1,7 +1,8 @@
 """MI355X-native fused scaled-dot-product-attention forward.
 
 Python front end of the C-ABI library ``libsdpa_mi355x.so`` (see
-``include/sdpa.h``): ``prefill`` (causal or full, GQA), ``decode`` (two-phase
+``include/sdpa.h``): ``prefill`` (causal or full, GQA), ``prefill_cached``
+(a chunk over a cached prefix), ``decode`` (two-phase
 split-KV), ``decode_paged`` (variable-length and paged caches) and the host
 planner ``plan``.  The compute runs in hand-written HIP kernels for gfx950;
 PyTorch only provides device memory and streams.
@@ -21,7 +22,8 @@ from .binding import (  # noqa: F401
     make_problem,
     plan,
     prefill,
+    prefill_cached,
 )
 
-__all__ = ["prefill", "decode", "decode_paged", "decode_workspace", "plan", "loop_counts", "make_problem", "load",
+__all__ = ["prefill", "prefill_cached", "decode", "decode_paged", "decode_workspace", "plan", "loop_counts", "make_problem", "load",
            "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]

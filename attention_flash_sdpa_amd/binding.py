@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
-    "sdpa_decode_paged_fwd", "sdpa_loop_counts",
+    "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_loop_counts",
 )
 
 
@@ -90,6 +90,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_decode_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.sdpa_prefill_fwd.restype = ctypes.c_int
     lib.sdpa_prefill_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sdpa_prefill_cached_fwd.restype = ctypes.c_int
+    lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
     lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     i32 = ctypes.c_int32
@@ -173,6 +175,39 @@ def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     _check(lib.sdpa_prefill_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                                 ws_bytes, _stream_handle(stream)))
+    return out
+
+
+def prefill_cached(q, k_cache, v_cache, k, v, *, cache_len, scale=None, causal=False, out=None, lse=None,
+                   stream=None):
+    """Cached-KV (chunked) prefill (``sdpa_prefill_cached_fwd``): the chunk's
+    queries q [B, Sq, Hq, D] attend to cache keys 0 .. cache_len-1 of
+    k_cache / v_cache [B, cap, Hkv, D|Dv] followed by the chunk's own keys
+    k / v [B, Sk, Hkv, D|Dv]; with ``causal`` only the new keys are masked
+    (bottom-right, Sq <= Sk).  Returns O [B, Sq, Hq, Dv]."""
+    import torch
+
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    Dv = v.shape[-1]
+    for t in (q, k, v, k_cache, v_cache):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v, k_cache, v_cache must be contiguous device tensors")
+    if k_cache.shape[0] != B or k_cache.shape[2:] != k.shape[2:] or v_cache.shape[:3] != k_cache.shape[:3] \
+            or v_cache.shape[-1] != Dv or v.shape[:3] != k.shape[:3] or k.shape[0] != B or k.shape[-1] != D:
+        raise ValueError(f"shapes disagree: q {tuple(q.shape)}, k_cache {tuple(k_cache.shape)}, "
+                         f"v_cache {tuple(v_cache.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not 0 <= cache_len <= k_cache.shape[1]:
+        raise ValueError(f"cache_len {cache_len} outside [0, {k_cache.shape[1]}]")
+    if out is None:
+        out = torch.empty(B, Sq, Hq, Dv, dtype=q.dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    pr = make_problem(batch=B, q_len=Sq, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=Dv,
+                      in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=causal, scale=scale)
+    _check(load().sdpa_prefill_cached_fwd(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len),
+                                          int(k_cache.shape[1]), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                          _stream_handle(stream)))
     return out
 
 

@@ -57,7 +57,7 @@ void clear_error() { g_last_error[0] = 0; }
 const char* last_error_text() { return g_last_error; }
 
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
-                        sdpa_plan_t* plan, int variant) {
+                        sdpa_plan_t* plan, int variant, bool cached) {
   memset(plan, 0, sizeof *plan);
   if (num_cus <= 0) num_cus = kDefaultCUs;
   if (p.batch < 0 || p.q_len < 0 || p.kv_len < 0) {
@@ -93,6 +93,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
 
   if (!is_decode) {
     int kid = prefill_kernel_id(p);
+    if (cached && kid == kPrefillFp8D192) kid = -1;  // the fp8 kernel reads one K/V tensor
     if (kid < 0) {
       set_error("unsupported prefill (in_dtype=%d, out_dtype=%d, d_qk=%d, d_v=%d)", p.in_dtype, p.out_dtype,
                 p.d_qk, p.d_v);
@@ -110,6 +111,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
       (void)wide_waves;
       if (variant == 1 || variant == 3 || variant == 4 || variant == 5) wide = false;
       if (variant == 2) wide = true;
+      if (cached) wide = false;
       if (wide) {
         rows = kWideRowsPerWave;
         kid = kid - kPrefillF16D64 + kWideF16D64;
@@ -155,12 +157,14 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     bool occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
     if (variant == 3 || variant == 4) occ2 = false;
     if (variant == 5) occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (cached) occ2 = false;
     if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
     // Four key ranges of 32-key blocks, two waves (heads or query tiles) per
     // range, 8 waves per workgroup at two waves per SIMD: the same grid as the
     // two-range split with twice the waves in flight.
     bool split4 = false;
     if (variant == 6) split4 = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (cached) split4 = false;
     if (split4) {
       ks = kSplitRanges;
       groups = shape(kSplitWaves / kSplitRanges, &hp, &qtiles);

@@ -1,0 +1,37 @@
+// prefill_cached.hip -- cached-KV (chunked) prefill instantiations of the
+// one-wave prefill kernel (prefill_kernel.h with CACHED = true): the chunk's
+// queries over a cached prefix followed by the chunk's own keys, the mode
+// "Xe SDPA Forward Mainloop" runs with kblocks_cache > 0 (sections "Startup
+// prefetch + init" and "Outer K-block loop").  Compiled apart from
+// prefill.hip only so that the two sets of instantiations build in parallel.
+#include "prefill_kernel.h"
+
+namespace sdpa {
+
+template <class T, int D, int KS>
+static int launch_cached_ks(const PrefillArgs& a, int causal, ihipStream_t* stream) {
+  dim3 grid(a.num_groups), block(64 * kPrefillWaves);
+  if (causal)
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, true, KS, true>), grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, false, KS, true>), grid, block, 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+template <class T, int D>
+static int launch_cached_one(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
+  return plan.num_splits == 2 ? launch_cached_ks<T, D, 2>(a, causal, stream)
+                              : launch_cached_ks<T, D, 1>(a, causal, stream);
+}
+
+int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
+  switch (plan.kernel) {
+    case kPrefillF16D64: return launch_cached_one<F16, 64>(a, plan, causal, stream);
+    case kPrefillBf16D64: return launch_cached_one<Bf16, 64>(a, plan, causal, stream);
+    case kPrefillF16D128: return launch_cached_one<F16, 128>(a, plan, causal, stream);
+    case kPrefillBf16D128: return launch_cached_one<Bf16, 128>(a, plan, causal, stream);
+    default: return (int)hipErrorInvalidValue;  // the planner picks no other kernel for a cached prefill
+  }
+}
+
+}  // namespace sdpa

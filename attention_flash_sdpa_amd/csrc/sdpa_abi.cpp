@@ -109,6 +109,36 @@ size_t sdpa_decode_workspace_bytes(const sdpa_problem_t* problem, int num_splits
   return (size_t)plan.workspace_bytes;
 }
 
+// Fills the kernel arguments of a planned prefill and launches it.
+static sdpa_status_t prefill_launch(const sdpa_problem_t& p, const sdpa_plan_t& plan, const void* q, const void* k,
+                                    const void* v, void* o, float* lse, const void* k_cache, const void* v_cache,
+                                    int32_t cache_len, int32_t cache_cap, void* stream) {
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.batch = p.batch;
+  a.q_len = p.q_len;
+  a.kv_len = p.kv_len;
+  a.head_q = p.head_q;
+  a.head_kv = p.head_kv;
+  a.group = p.head_q / p.head_kv;
+  a.heads_per_group = plan.heads_per_group;
+  a.qtiles_per_group = plan.qtiles_per_group;
+  a.q_tiles = plan.q_tiles;
+  a.head_groups = (a.group + plan.heads_per_group - 1) / plan.heads_per_group;
+  a.num_groups = plan.num_groups;
+  a.s2 = (float)((double)p.scale * 1.4426950408889634 * (double)p.q_descale * (double)p.k_descale);
+  a.v_descale = p.v_descale;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_len = cache_len;
+  a.cache_cap = cache_cap;
+  return hip_status(launch_prefill(a, plan, p.causal != 0, (ihipStream_t*)stream), "prefill launch");
+}
+
 sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
                                void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
@@ -134,26 +164,67 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
               (unsigned long long)workspace_bytes);
     return SDPA_ERR_WORKSPACE;
   }
-  PrefillArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.batch = p.batch;
-  a.q_len = p.q_len;
-  a.kv_len = p.kv_len;
-  a.head_q = p.head_q;
-  a.head_kv = p.head_kv;
-  a.group = p.head_q / p.head_kv;
-  a.heads_per_group = plan.heads_per_group;
-  a.qtiles_per_group = plan.qtiles_per_group;
-  a.q_tiles = plan.q_tiles;
-  a.head_groups = (a.group + plan.heads_per_group - 1) / plan.heads_per_group;
-  a.num_groups = plan.num_groups;
-  a.s2 = (float)((double)p.scale * 1.4426950408889634 * (double)p.q_descale * (double)p.k_descale);
-  a.v_descale = p.v_descale;
-  return hip_status(launch_prefill(a, plan, p.causal != 0, (ihipStream_t*)stream), "prefill launch");
+  return prefill_launch(p, plan, q, k, v, o, lse, nullptr, nullptr, 0, 0, stream);
+}
+
+sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void* q, const void* k_cache,
+                                      const void* v_cache, int32_t cache_len, int32_t cache_cap, const void* k,
+                                      const void* v, void* o, float* lse, void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  const sdpa_problem_t& p = *problem;
+  if (cache_len < 0 || cache_cap < cache_len) {
+    set_error("need 0 <= cache_len <= cache_cap (cache_len=%d, cache_cap=%d)", cache_len, cache_cap);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (p.causal && p.q_len > p.kv_len) {
+    set_error("causal cached prefill needs q_len <= new keys (q_len=%d, kv_len=%d)", p.q_len, p.kv_len);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (p.kv_len < 0 || (int64_t)p.kv_len + cache_len > INT32_MAX) {
+    set_error("cache_len + kv_len out of range (%d + %d)", cache_len, p.kv_len);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (cache_len == 0) {  // nothing cached: the plain prefill
+    sdpa_plan_t plan;
+    sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan, prefill_variant());
+    if (st != SDPA_OK) return st;
+    if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
+    if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr))) {
+      set_error("q, k, v and o must not be NULL");
+      return SDPA_ERR_NULL_PTR;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u)) {
+      set_error("q, k, v, o must be 16-byte aligned and lse 4-byte aligned");
+      return SDPA_ERR_MISALIGNED;
+    }
+    return prefill_launch(p, plan, q, k, v, o, lse, nullptr, nullptr, 0, 0, stream);
+  }
+  // one sequence of cache_len + kv_len keys for the planner and the kernel
+  sdpa_problem_t vp = p;
+  vp.kv_len = cache_len + p.kv_len;
+  sdpa_plan_t plan;
+  sdpa_status_t st = make_plan(vp, false, device_cus(), 0, &plan, prefill_variant(), true);
+  if (st != SDPA_OK) return st;
+  if ((int64_t)cache_cap * p.head_kv * (p.d_qk > p.d_v ? p.d_qk : p.d_v) >= (int64_t)1 << 31) {
+    set_error("one batch entry of the cache exceeds 2^31 elements (cache_cap=%d)", cache_cap);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
+  if (o == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr ||
+      (p.kv_len > 0 && (k == nullptr || v == nullptr))) {
+    set_error("q, k_cache, v_cache, k, v and o must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || ((uintptr_t)lse & 3u)) {
+    set_error("q, k, v, o, k_cache, v_cache must be 16-byte aligned and lse 4-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  return prefill_launch(vp, plan, q, k, v, o, lse, k_cache, v_cache, cache_len, cache_cap, stream);
 }
 
 // Shared by the dense and the paged decode entry points; cache rows per

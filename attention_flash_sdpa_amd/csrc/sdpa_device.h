@@ -314,6 +314,20 @@ __device__ __forceinline__ void global_load_16_untracked(u32x4_t& d, const void*
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=&v"(d) : "v"(p), "i"(OFF) : "memory");
 }
 
+// As global_to_lds_16_off with a per-lane 64-bit address (the lane's address
+// less OFF) instead of a scalar base: used where the lanes of one load read
+// from different tensors.  A vector address carries no SGPR hazard, so only
+// an M0 write needs its wait state (WAITS 1), else none (WAITS 0).
+template <int OFF, int WAITS>
+__device__ __forceinline__ void global_to_lds_16_voff(const void* addr, uint32_t m0_base) {
+  static_assert(OFF >= 0 && OFF < 4096 && (WAITS == 0 || WAITS == 1), "offset / wait states");
+  if constexpr (WAITS == 1)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(addr), "{m0}"(m0_base), "i"(OFF)
+                 : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, off offset:%2" ::"v"(addr), "{m0}"(m0_base), "i"(OFF) : "memory");
+}
+
 // One dword load that waits for every outstanding vector-memory load of the
 // wave (including untracked direct-to-LDS ones) before returning.  Meant for
 // rare loads inside an explicitly counted load pipeline: a compiler-tracked

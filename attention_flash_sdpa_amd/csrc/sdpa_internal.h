@@ -56,9 +56,10 @@ constexpr int kDefaultCUs = 256;
 // form), 2 = the wide (64-row) kernel, 3 / 4 = the one-wave-per-SIMD 32-row
 // kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
 // 32-row kernel, 6 = its 8-wave, four-key-range form (tuning sweeps and tests
-// only).
+// only).  cached: a cached-KV prefill (kv_len counts cache and new keys),
+// which only the one-wave 32-row kernel implements.
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
-                        sdpa_plan_t* plan, int variant = 0);
+                        sdpa_plan_t* plan, int variant = 0, bool cached = false);
 
 sdpa_status_t loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k, int block_d,
                           int block_v, bool causal, sdpa_loop_counts_t* out);
@@ -76,6 +77,12 @@ struct PrefillArgs {
   int32_t heads_per_group, qtiles_per_group, q_tiles, head_groups, num_groups;
   float s2;         // scale * log2(e) * q_descale * k_descale
   float v_descale;  // applied to the output (fp8 inputs), else 1
+  // cached-KV prefill: keys 0 .. cache_len-1 come from k_cache / v_cache
+  // ([batch, cache_cap, head_kv, d]), keys cache_len .. kv_len-1 from k / v
+  // ([batch, kv_len - cache_len, head_kv, d]); unused otherwise
+  const void* k_cache;
+  const void* v_cache;
+  int32_t cache_len, cache_cap;
 };
 
 struct DecodeArgs {
@@ -101,6 +108,7 @@ int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ih
 int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
 int launch_prefill_wide(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 }  // namespace sdpa

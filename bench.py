@@ -148,8 +148,8 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False):
 
 
 # kernel-source files whose text decides each profiled kernel's code
-_SOURCES = {"prefill": ["prefill.hip", "prefill_o2.hip", "prefill_wide.hip", "sdpa_device.h", "sdpa_internal.h",
-                        "sdpa_bounds.h"],
+_SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_wide.hip", "sdpa_device.h",
+                        "sdpa_internal.h", "sdpa_bounds.h"],
             "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"]}
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
 

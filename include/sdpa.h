@@ -182,6 +182,31 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
                                const void* v, void* o, float* lse, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Cached-KV (chunked) prefill: the chunk's q_len queries attend to a cached
+ * prefix of cache_len keys followed by the chunk's own kv_len keys.  The
+ * mainloop page ("Xe SDPA Forward Mainloop") takes its first
+ * ceil(cache_len / block) K blocks from the cache and the rest from the new
+ * tensors, indexed from the first new key (sections "Startup prefetch +
+ * init", "Outer K-block loop" and the K prefetch of "mainloop_body(K)"),
+ * and masks causally only the blocks that are not cache blocks (section
+ * "mask branches").  So with causal != 0 every query sees every cached key
+ * and query i sees new key j iff j <= i + kv_len - q_len; this needs
+ * q_len <= kv_len (else SDPA_ERR_BAD_SHAPE).  The result equals
+ * sdpa_prefill_fwd over the concatenated keys [cache | new].
+ *   problem  : kv_len = the chunk's new keys; other fields as for prefill
+ *   q        : [batch, q_len, head_q, d_qk]
+ *   k_cache, v_cache : [batch, cache_cap, head_kv, d_qk|d_v], of which keys
+ *              0 .. cache_len-1 are read (0 <= cache_len <= cache_cap); may
+ *              be NULL when cache_len == 0 (then this is sdpa_prefill_fwd)
+ *   k, v     : [batch, kv_len, head_kv, d_qk|d_v] (the chunk's own keys)
+ *   o, lse   : as for sdpa_prefill_fwd
+ * 16-bit inputs only (fp16/bf16, d 64 or 128; fp8 gives
+ * SDPA_ERR_UNSUPPORTED).  No workspace; errors as for sdpa_prefill_fwd. */
+sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void* q,
+                                      const void* k_cache, const void* v_cache, int32_t cache_len,
+                                      int32_t cache_cap, const void* k, const void* v, void* o,
+                                      float* lse, void* stream);
+
 /* Two-phase split-KV decode ("xe2-sdp-kernels", section "Assets": production
  * decode, two-phase) for one new token per sequence (q_len == 1).
  * Phase 1: one workgroup per (batch, KV head, split) streams its key range

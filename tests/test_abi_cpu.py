@@ -240,3 +240,30 @@ def test_paged_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         binding._check_caches(q, pool[..., :64], pool, dense=False)    # head dim differs from q
     binding._check_caches(q, pool, pool, dense=False)
+
+
+def test_cached_prefill_argument_errors_before_any_launch():
+    import ctypes
+
+    lib = sdpa.load()
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    null = ctypes.c_void_p(0)
+    a = ctypes.c_void_p(0x1000)
+
+    def call(problem, cache_len=1024, cap=1024, kc=a, k=a, q=a):
+        return lib.sdpa_prefill_cached_fwd(None if problem is None else ctypes.byref(problem), q, kc, kc, cache_len,
+                                           cap, k, k, a, null, null)
+
+    pr = _problem(w, q_len=512, kv_len=512)
+    assert call(None) == 1
+    assert call(pr, cache_len=-1) == 2
+    assert call(pr, cache_len=100, cap=99) == 2
+    assert call(_problem(w, q_len=600, kv_len=512)) == 2          # causal: more queries than new keys
+    assert b"q_len" in lib.sdpa_last_error()
+    assert call(pr, kc=null) == 1
+    assert call(pr, kc=ctypes.c_void_p(0x1008)) == 5
+    assert call(_problem(w, q_len=512, kv_len=512, in_dtype=sdpa.FP8_E4M3, d_qk=192)) == 4
+    assert call(_problem(w, q_len=0, kv_len=512)) == 0              # no queries: a no-op
+    # nothing cached: the plain prefill's checks (k_cache may be NULL)
+    assert call(pr, cache_len=0, cap=0, kc=null, q=null) == 1
+
