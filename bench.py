@@ -124,10 +124,11 @@ def _problem(sdpa, w):
                              out_dtype=code[w.out_dtype], causal=w.causal, scale=w.scale)
 
 
-def _kernels_of(sdpa, w, num_cus=256, paged=False):
+def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
     """(kernel name, grid size in work-items) of each launch one call of
     workload `w` makes, from the host planner (`paged`: decode through a page
-    table)."""
+    table; `cached`: prefill over a cached prefix, `w.kv_len` counting cache
+    and new keys)."""
     p = sdpa.plan(_problem(sdpa, w), decode=w.decode, num_cus=num_cus)
     t = {"f16": "F16", "bf16": "Bf16"}.get(w.dtype)
     c = "true" if w.causal else "false"
@@ -143,7 +144,7 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False):
                  p.num_groups * p.waves_per_group * 64)]
     if p.rows_per_wave == 64:
         return [(f"prefill_wide_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
-    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}>",
+    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, {'true' if cached else 'false'}>",
              p.num_groups * p.waves_per_group * 64)]
 
 
@@ -151,6 +152,18 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False):
 _SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_wide.hip", "sdpa_device.h",
                         "sdpa_internal.h", "sdpa_bounds.h"],
             "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"]}
+def _cached_chunk():
+    from attention_flash_sdpa_amd import inputs
+
+    # a 512-query chunk over 3584 cached keys (4096 keys in all); q_len and
+    # kv_len as the planner sees them
+    return inputs.Workload("cached_prefill_chunk512_over3584_bf16", 1, 32, 8, 512, 4096, 128, 128, "bf16", "bf16",
+                           True, 1006)
+
+
+CACHED_CHUNK = _cached_chunk()
+CACHED_LEN = 3584
+
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
 
 
@@ -210,8 +223,9 @@ def _summarize_trace(d):
         else "(command not recorded)"
     todo = [(wname, w, False) for wname, w in inputs.WORKLOADS.items()]
     todo.append(("splitkv_decode_bf16_paged64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
+    todo.append((CACHED_CHUNK.name, CACHED_CHUNK, "cached"))
     for wname, w, paged in todo:
-        for kname, grid in _kernels_of(sdpa, w, paged=paged):
+        for kname, grid in _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached"):
             if paged and "true>" not in kname:
                 continue  # the combine kernel is the dense one
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
@@ -435,6 +449,38 @@ def main():
                        "algorithmic_gflop": round(xw.flops() / 1e9, 4), "peak": peak,
                        "frac_of_peak": round(xt / peak, 5)}
         del xq, xk, xv, xo
+    # ------- cached-KV (chunked) prefill: 512 new queries/keys over 3584 cached -------
+    from oracle import cached as ocached
+
+    cw = CACHED_CHUNK
+    g = torch.Generator().manual_seed(cw.seed)
+    new = cw.kv_len - CACHED_LEN
+    cq = torch.randn(1, cw.q_len, cw.head_q, cw.d_qk, generator=g).to(torch.bfloat16)
+    ckc, cvc, ck, cv = (torch.randn(1, n, cw.head_kv, cw.d_qk, generator=g).to(torch.bfloat16)
+                        for n in (CACHED_LEN, CACHED_LEN, new, new))
+    cqd, ckcd, cvcd, ckd, cvd = (t.to(dev) for t in (cq, ckc, cvc, ck, cv))
+    co = torch.empty(1, cw.q_len, cw.head_q, cw.d_v, dtype=torch.bfloat16, device=dev)
+
+    def cstep(i):
+        sdpa.prefill_cached(cqd, ckcd, cvcd, ckd, cvd, cache_len=CACHED_LEN, causal=True, scale=cw.scale, out=co)
+
+    cn = max(args.steps // 4, 1)
+    ceager = _time(cstep, cn, args.warmup, stream)
+    cms = _graph_time(cstep, cn, args.warmup)
+    cstep(0)
+    torch.cuda.synchronize()
+    cref = ocached.prefill_cached(cq, ckc, cvc, ck, cv, cache_len=CACHED_LEN, scale=cw.scale, causal=True)["out"]
+    cerr = float(np.abs(co.double().cpu().numpy() - cref).max())
+    ct = cw.flops() / (cms * 1e-3) / 1e12
+    cached_line = {"workload": f"{cw.q_len}-query chunk over {CACHED_LEN} cached keys, Hq {cw.head_q} / Hkv "
+                               f"{cw.head_kv}, d {cw.d_qk}, bf16, causal on the new keys",
+                   "value": round(ct, 3), "unit": "TFLOP/s", "ms_per_call": round(cms, 6),
+                   "eager_ms_per_call": round(ceager, 6), "steps": cn,
+                   "algorithmic_gflop": round(cw.flops() / 1e9, 4), "peak": PEAK_BF16_TFLOPS,
+                   "frac_of_peak": round(ct / PEAK_BF16_TFLOPS, 5),
+                   "parity": {"max_abs_err": cerr}}
+    del cqd, ckcd, cvcd, ckd, cvd
+
     # launch floor: a one-element device op, eager and replayed from a graph
     one = torch.zeros(1, device=dev)
     floor_eager = _time(lambda i: one.add_(1.0), args.steps, args.warmup, stream)
@@ -493,6 +539,7 @@ def main():
                          "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
             "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
         },
+        "prefill_cached": cached_line,
         "other_workloads": extra,
         "launch_floor_us": {"eager": round(floor_eager * 1e3, 3), "graph": round(floor_graph * 1e3, 3)},
         "device": {"name": props.name, "cus": ncu},
