@@ -1,11 +1,11 @@
 """MI355X-native fused scaled-dot-product-attention forward.
 
 Python front end of the C-ABI library ``libsdpa_mi355x.so`` (see
-``include/sdpa.h``): ``prefill`` (causal or full, GQA), ``prefill_cached``
-(a chunk over a cached prefix), ``decode`` (two-phase
-split-KV), ``decode_paged`` (variable-length and paged caches) and the host
-planner ``plan``.  The compute runs in hand-written HIP kernels for gfx950;
-PyTorch only provides device memory and streams.
+``include/sdpa.h``): ``prefill`` (causal or full, GQA), ``prefill_cached`` (a
+chunk over a cached prefix), ``decode`` (two-phase split-KV), ``decode_paged``
+(variable-length and paged caches), ``mask_convert`` (boolean to additive
+masks) and the host planner ``plan``.  The compute runs in hand-written HIP
+kernels for gfx950; PyTorch only provides device memory and streams.
 """
 from .binding import (  # noqa: F401
     BF16,
@@ -20,10 +20,11 @@ from .binding import (  # noqa: F401
     load,
     loop_counts,
     make_problem,
+    mask_convert,
     plan,
     prefill,
     prefill_cached,
 )
 
-__all__ = ["prefill", "prefill_cached", "decode", "decode_paged", "decode_workspace", "plan", "loop_counts", "make_problem", "load",
-           "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]
+__all__ = ["prefill", "prefill_cached", "decode", "decode_paged", "decode_workspace", "mask_convert", "plan",
+           "loop_counts", "make_problem", "load", "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]

@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
-    "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_loop_counts",
+    "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_loop_counts",
 )
 
 
@@ -91,6 +91,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_prefill_fwd.restype = ctypes.c_int
     lib.sdpa_prefill_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_prefill_cached_fwd.restype = ctypes.c_int
+    lib.sdpa_mask_convert.restype = ctypes.c_int
+    lib.sdpa_mask_convert.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
     lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
     lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
@@ -319,4 +321,20 @@ def decode_paged(q, k_cache, v_cache, *, page_table=None, seq_lens=None, kv_len=
                                      _ptr(page_table), num_pages, page_size, pages_per_seq, _ptr(out), _ptr(lse),
                                      int(num_splits), _ptr(workspace.tensor), workspace.nbytes,
                                      _stream_handle(stream)))
+    return out
+
+
+def mask_convert(mask, *, out_dtype=None, out=None, stream=None):
+    """Additive mask of a boolean (or uint8) device mask: 0 where the key
+    takes part (nonzero), -inf where it does not; same shape, dtype
+    ``out_dtype`` (torch.float16 or torch.bfloat16, default bfloat16)."""
+    import torch
+
+    if not mask.is_cuda or not mask.is_contiguous() or mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("mask must be a contiguous bool or uint8 device tensor")
+    if out is None:
+        out = torch.empty(mask.shape, dtype=out_dtype or torch.bfloat16, device=mask.device)
+    if out.shape != mask.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like mask")
+    _check(load().sdpa_mask_convert(_ptr(mask), _ptr(out), mask.numel(), _dtype_code(out), _stream_handle(stream)))
     return out

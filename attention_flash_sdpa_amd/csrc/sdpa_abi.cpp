@@ -227,6 +227,28 @@ sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void*
   return prefill_launch(vp, plan, q, k, v, o, lse, k_cache, v_cache, cache_len, cache_cap, stream);
 }
 
+sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32_t out_dtype, void* stream) {
+  clear_error();
+  if (n < 0) {
+    set_error("n must not be negative (got %lld)", (long long)n);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (out_dtype != SDPA_F16 && out_dtype != SDPA_BF16) {
+    set_error("mask conversion writes fp16 or bf16 (got out_dtype=%d)", out_dtype);
+    return SDPA_ERR_UNSUPPORTED;
+  }
+  if (n == 0) return SDPA_OK;
+  if (mask == nullptr || out == nullptr) {
+    set_error("mask and out must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  if (!aligned16(mask) || !aligned16(out)) {
+    set_error("mask and out must be 16-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  return hip_status(launch_mask_convert(mask, out, n, out_dtype, (ihipStream_t*)stream), "mask conversion launch");
+}
+
 // Shared by the dense and the paged decode entry points; cache rows per
 // page and the table are checked by the caller.
 static sdpa_status_t decode_common(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,

@@ -48,6 +48,7 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per CU (gfx950)
 constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows per workgroup
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
+constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
 
 // Validates the problem; fills *plan.  Writes a detail message through
@@ -109,6 +110,7 @@ int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
 int launch_prefill_wide(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 }  // namespace sdpa

@@ -162,6 +162,7 @@ def _cached_chunk():
 
 
 CACHED_CHUNK = _cached_chunk()
+MASK_SHAPE = (16, 4096, 4096)  # bool mask elements converted per call
 CACHED_LEN = 3584
 
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
@@ -215,6 +216,8 @@ def _summarize_trace(d):
     --stats` run of bench.py, written to profiles/<kernel>_<workload>_trace.txt."""
     import statistics
 
+    import numpy as np
+
     import attention_flash_sdpa_amd as sdpa
     from attention_flash_sdpa_amd import inputs
 
@@ -224,18 +227,26 @@ def _summarize_trace(d):
     todo = [(wname, w, False) for wname, w in inputs.WORKLOADS.items()]
     todo.append(("splitkv_decode_bf16_paged64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
     todo.append((CACHED_CHUNK.name, CACHED_CHUNK, "cached"))
+    todo.append(("mask_convert_16x4096x4096", None, "mask"))
     for wname, w, paged in todo:
-        for kname, grid in _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached"):
-            if paged and "true>" not in kname:
+        kernels = ([("mask_convert_kernel", None)] if paged == "mask" else
+                   _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached"))
+        for kname, grid in kernels:
+            if paged is True and "true>" not in kname:
                 continue  # the combine kernel is the dense one
-            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
-                    if kname in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid]
+
+            def hit(r):
+                return kname in r["Kernel_Name"] and (grid is None or int(r["Grid_Size_X"]) == grid)
+
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if hit(r)]
             if not durs:
                 continue
-            r0 = next(r for r in rows if kname in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid)
+            r0 = next(r for r in rows if hit(r))
+            grid = int(r0["Grid_Size_X"])
             fam = kname.split("<")[0]
             out = os.path.join(ROOT, "profiles", f"{fam}_{wname}_trace.txt")
-            alg = w.bytes_moved() if w.decode else w.flops()
+            byte_bound = w is None or w.decode
+            alg = 3 * int(np.prod(MASK_SHAPE)) if w is None else (w.bytes_moved() if w.decode else w.flops())
             with open(out, "w") as f:
                 f.write(f"kernel: {r0['Kernel_Name']}\nworkload: {wname}\n")
                 f.write(f"command: {cmd}\n")
@@ -245,7 +256,10 @@ def _summarize_trace(d):
                 f.write(f"dispatches: {len(durs)}\n")
                 f.write(f"avg_us: {statistics.mean(durs):.3f}\nmedian_us: {statistics.median(durs):.3f}\n"
                         f"min_us: {min(durs):.3f}\nmax_us: {max(durs):.3f}\n")
-                if w.decode:
+                if w is None:
+                    f.write(f"algorithmic bytes per call (mask read + additive mask written): {alg}\n"
+                            f"GB/s at median: {alg / statistics.median(durs) / 1e3:.1f}\n")
+                elif byte_bound:
                     f.write(f"algorithmic bytes per call (Q+K+V+O): {alg}\n")
                 else:
                     med = statistics.median(durs)
@@ -481,6 +495,37 @@ def main():
                    "parity": {"max_abs_err": cerr}}
     del cqd, ckcd, cvcd, ckd, cvd
 
+    # ------- boolean -> additive mask conversion, 4 rotating buffer sets -------
+    from oracle import mask as omask
+
+    mshape = MASK_SHAPE
+    mn = int(np.prod(mshape))
+    msets = []
+    for s_ in range(4):
+        g = torch.Generator(device=dev).manual_seed(1007 + 100 * s_)
+        msets.append(((torch.rand(mshape, generator=g, device=dev) < 0.5),
+                      torch.empty(mshape, dtype=torch.bfloat16, device=dev)))
+
+    def mstep(i):
+        mm, mo = msets[i % len(msets)]
+        sdpa.mask_convert(mm, out=mo)
+
+    mms = _graph_time(mstep, args.decode_steps, args.warmup, period=len(msets))
+    mbytes = 3 * mn
+    mgbs = mbytes / (mms * 1e-3) / 1e9
+    mstep(0)
+    torch.cuda.synchronize()
+    mrows = slice(0, 64)
+    mref = omask.mask_convert(msets[0][0][0, mrows].cpu().numpy().astype(np.uint8), "bf16")
+    mexact = bool(np.array_equal(msets[0][1][0, mrows].view(torch.int16).cpu().numpy().view(np.uint16), mref))
+    mask_line = {"workload": f"bool mask {list(mshape)} -> bf16 additive", "value": round(mgbs, 2), "unit": "GB/s",
+                 "ms_per_call": round(mms, 6), "steps": args.decode_steps, "buffer_sets": len(msets),
+                 "algorithmic_bytes": mbytes,
+                 "roofline": {"bound": "hbm", "achieved": round(mgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(mgbs / PEAK_HBM_GBS, 5), "traffic": None},
+                 "parity": {"bit_exact_rows": 64, "exact": mexact}}
+    del msets
+
     # launch floor: a one-element device op, eager and replayed from a graph
     one = torch.zeros(1, device=dev)
     floor_eager = _time(lambda i: one.add_(1.0), args.steps, args.warmup, stream)
@@ -540,6 +585,7 @@ def main():
             "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
         },
         "prefill_cached": cached_line,
+        "mask_convert": mask_line,
         "other_workloads": extra,
         "launch_floor_us": {"eager": round(floor_eager * 1e3, 3), "graph": round(floor_graph * 1e3, 3)},
         "device": {"name": props.name, "cus": ncu},

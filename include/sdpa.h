@@ -207,6 +207,18 @@ sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void*
                                       int32_t cache_cap, const void* k, const void* v, void* o,
                                       float* lse, void* stream);
 
+/* Boolean -> additive mask conversion, the memory-bound mask_convert kernel
+ * of "xe2-sdp-kernels" (section "Performance testing"), producing the full
+ * additive mask the mainloop's optional mask argument applies to the scores
+ * ("Xe SDPA Forward Mainloop", section "Runtime args / params").  Element e
+ * of out (out_dtype SDPA_F16 or SDPA_BF16) is +0 where mask[e] != 0 (the key
+ * takes part) and -inf where mask[e] == 0; any layout, element for element.
+ *   mask : device uint8 [n] (torch.bool storage qualifies), 16-byte aligned
+ *   out  : device 16-bit [n], 16-byte aligned, written entirely
+ * n == 0 is a no-op.  Enqueued on `stream`; nothing synchronises. */
+sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32_t out_dtype,
+                                void* stream);
+
 /* Two-phase split-KV decode ("xe2-sdp-kernels", section "Assets": production
  * decode, two-phase) for one new token per sequence (q_len == 1).
  * Phase 1: one workgroup per (batch, KV head, split) streams its key range

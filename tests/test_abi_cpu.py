@@ -267,3 +267,15 @@ def test_cached_prefill_argument_errors_before_any_launch():
     # nothing cached: the plain prefill's checks (k_cache may be NULL)
     assert call(pr, cache_len=0, cap=0, kc=null, q=null) == 1
 
+
+
+def test_mask_convert_argument_errors_before_any_launch():
+    import ctypes
+
+    lib = sdpa.load()
+    a, null = ctypes.c_void_p(0x1000), ctypes.c_void_p(0)
+    assert lib.sdpa_mask_convert(a, a, -1, sdpa.BF16, null) == 2
+    assert lib.sdpa_mask_convert(a, a, 16, sdpa.FP8_E4M3, null) == 4
+    assert lib.sdpa_mask_convert(null, a, 16, sdpa.F16, null) == 1
+    assert lib.sdpa_mask_convert(ctypes.c_void_p(0x1001), a, 16, sdpa.F16, null) == 5
+    assert lib.sdpa_mask_convert(null, null, 0, sdpa.F16, null) == 0      # empty: a no-op
