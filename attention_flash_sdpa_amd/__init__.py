@@ -2,9 +2,10 @@
 
 Python front end of the C-ABI library ``libsdpa_mi355x.so`` (see
 ``include/sdpa.h``): ``prefill`` (causal or full, GQA), ``prefill_cached`` (a
-chunk over a cached prefix), ``decode`` (two-phase split-KV), ``decode_paged``
-(variable-length and paged caches), ``mask_convert`` (boolean to additive
-masks) and the host planner ``plan``.  The compute runs in hand-written HIP
+chunk over a cached prefix), ``prefill_masked`` (a full additive mask),
+``decode`` (two-phase split-KV), ``decode_paged`` (variable-length and paged
+caches), ``mask_convert`` (boolean to additive masks) and the host planner
+``plan``.  The compute runs in hand-written HIP
 kernels for gfx950; PyTorch only provides device memory and streams.
 """
 from .binding import (  # noqa: F401
@@ -24,7 +25,8 @@ from .binding import (  # noqa: F401
     plan,
     prefill,
     prefill_cached,
+    prefill_masked,
 )
 
-__all__ = ["prefill", "prefill_cached", "decode", "decode_paged", "decode_workspace", "mask_convert", "plan",
+__all__ = ["prefill", "prefill_cached", "prefill_masked", "decode", "decode_paged", "decode_workspace", "mask_convert", "plan",
            "loop_counts", "make_problem", "load", "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]

@@ -24,7 +24,8 @@ STATUS = {
 EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
-    "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_loop_counts",
+    "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_prefill_masked_fwd",
+    "sdpa_loop_counts",
 )
 
 
@@ -92,6 +93,9 @@ def load(path: str = LIB_PATH):
     lib.sdpa_prefill_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_prefill_cached_fwd.restype = ctypes.c_int
     lib.sdpa_mask_convert.restype = ctypes.c_int
+    lib.sdpa_prefill_masked_fwd.restype = ctypes.c_int
+    lib.sdpa_prefill_masked_fwd.argtypes = [P, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, vp, vp,
+                                            vp]
     lib.sdpa_mask_convert.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
     lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
@@ -337,4 +341,36 @@ def mask_convert(mask, *, out_dtype=None, out=None, stream=None):
     if out.shape != mask.shape or not out.is_contiguous():
         raise ValueError("out must be contiguous and shaped like mask")
     _check(load().sdpa_mask_convert(_ptr(mask), _ptr(out), mask.numel(), _dtype_code(out), _stream_handle(stream)))
+    return out
+
+
+def prefill_masked(q, k, v, mask, *, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O = softmax(Q K^T * scale + mask [+ causal]) V (``sdpa_prefill_masked_fwd``).
+
+    q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] fp16/bf16; ``mask`` an additive mask
+    of q's dtype, a [Bm, Hm, Sq, W] view with Bm in {1, B}, Hm in {1, Hq}
+    (size-1 dims broadcast) and W >= Sk whose last dim is contiguous; its
+    strides must be multiples of 8 elements (pad rows to a multiple of 8 and
+    slice them to Sk: ``mask[..., :Sk]`` of a padded tensor qualifies)."""
+    import torch
+
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    for t in (q, k, v):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if mask.dim() != 4 or mask.dtype != q.dtype or not mask.is_cuda or mask.stride(-1) != 1:
+        raise ValueError("mask must be a 4-D device tensor of q's dtype with a contiguous last dim")
+    if mask.shape[0] not in (1, B) or mask.shape[1] not in (1, Hq) or mask.shape[2] != Sq or mask.shape[3] < Sk:
+        raise ValueError(f"mask shape {tuple(mask.shape)} does not cover [{B}, {Hq}, {Sq}, {Sk}]")
+    sb = 0 if mask.shape[0] == 1 else mask.stride(0)
+    sh = 0 if mask.shape[1] == 1 else mask.stride(1)
+    if out is None:
+        out = torch.empty(B, Sq, Hq, v.shape[-1], dtype=q.dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    pr = make_problem(batch=B, q_len=Sq, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=v.shape[-1],
+                      in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=causal, scale=scale)
+    _check(load().sdpa_prefill_masked_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), sb, sh,
+                                          mask.stride(2), _ptr(out), _ptr(lse), _stream_handle(stream)))
     return out

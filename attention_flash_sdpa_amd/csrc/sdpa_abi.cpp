@@ -249,6 +249,68 @@ sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32
   return hip_status(launch_mask_convert(mask, out, n, out_dtype, (ihipStream_t*)stream), "mask conversion launch");
 }
 
+sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
+                                      const void* mask, int64_t mask_stride_b, int64_t mask_stride_h,
+                                      int32_t mask_stride_row, void* o, float* lse, void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  const sdpa_problem_t& p = *problem;
+  sdpa_plan_t plan;  // shape, head and scale checks shared with the plain prefill
+  sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan);
+  if (st != SDPA_OK) return st;
+  if (p.in_dtype == SDPA_FP8_E4M3 || p.out_dtype != p.in_dtype || p.d_qk != p.d_v) {
+    set_error("the masked prefill takes fp16/bf16 inputs with the same output type and d_qk == d_v "
+              "(in=%d out=%d d_qk=%d d_v=%d)", p.in_dtype, p.out_dtype, p.d_qk, p.d_v);
+    return SDPA_ERR_UNSUPPORTED;
+  }
+  const int64_t min_row = p.kv_len > 8 ? p.kv_len : 8;
+  if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_row < min_row || mask_stride_row % 8 != 0 ||
+      mask_stride_b % 8 != 0 || mask_stride_h % 8 != 0) {
+    set_error("mask strides must be >= 0 and multiples of 8 elements, the row stride >= max(kv_len, 8) "
+              "(b=%lld h=%lld row=%d kv_len=%d)", (long long)mask_stride_b, (long long)mask_stride_h,
+              mask_stride_row, p.kv_len);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  const int64_t row_tiles = ((int64_t)p.q_len + 16 * kMaskedWaves - 1) / (16 * kMaskedWaves);
+  if ((int64_t)p.batch * p.head_q * row_tiles >= ((int64_t)1 << 31)) {
+    set_error("grid too large (%lld workgroups)", (long long)((int64_t)p.batch * p.head_q * row_tiles));
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
+  if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr || mask == nullptr))) {
+    set_error("q, k, v, mask and o must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(mask) ||
+      ((uintptr_t)lse & 3u)) {
+    set_error("q, k, v, mask, o must be 16-byte aligned and lse 4-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  MaskedArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.mask = mask;
+  a.o = o;
+  a.lse = lse;
+  a.batch = p.batch;
+  a.q_len = p.q_len;
+  a.kv_len = p.kv_len;
+  a.head_q = p.head_q;
+  a.head_kv = p.head_kv;
+  a.group = p.head_q / p.head_kv;
+  a.mask_sb = mask_stride_b;
+  a.mask_sh = mask_stride_h;
+  a.mask_row = mask_stride_row;
+  a.row_tiles = (int32_t)row_tiles;
+  a.s2 = (float)((double)p.scale * 1.4426950408889634);
+  return hip_status(launch_prefill_masked(a, p.in_dtype, p.d_qk, p.causal != 0, (ihipStream_t*)stream),
+                    "masked prefill launch");
+}
+
 // Shared by the dense and the paged decode entry points; cache rows per
 // page and the table are checked by the caller.
 static sdpa_status_t decode_common(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,

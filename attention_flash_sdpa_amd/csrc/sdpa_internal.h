@@ -48,6 +48,8 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per CU (gfx950)
 constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows per workgroup
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
+constexpr int kMaskedWaves = 4;    // masked prefill: 16-row tiles (waves) per workgroup
+constexpr int kMaskedBlockK = 32;  // masked prefill: keys per K/V/mask block
 constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
 
@@ -111,6 +113,22 @@ int launch_prefill_wide(const PrefillArgs& a, const sdpa_plan_t& plan, int causa
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream);
+
+// prefill with a full additive mask (one wave per 16 query rows of one head)
+struct MaskedArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* mask;   // [.., q_len, mask_row] additive, the inputs' 16-bit type
+  void* o;
+  float* lse;
+  int32_t batch, q_len, kv_len, head_q, head_kv, group;
+  int64_t mask_sb, mask_sh;  // element strides of the mask's batch and head (0: broadcast)
+  int32_t mask_row;          // element stride between mask rows (multiple of 8, >= max(kv_len, 8))
+  int32_t row_tiles;         // workgroups per (batch, head): ceil(q_len / 64)
+  float s2;                  // scale * log2(e)
+};
+int launch_prefill_masked(const MaskedArgs& a, int in_dtype, int d, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 }  // namespace sdpa

@@ -219,6 +219,26 @@ sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void*
 sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32_t out_dtype,
                                 void* stream);
 
+/* Prefill with a full additive mask: O = softmax(Q K^T * scale + mask) V,
+ * the mainloop's optional full mask ("Xe SDPA Forward Mainloop", section
+ * "Runtime args / params") added to every score in its mask step (section
+ * "Compact shape table", row "Mask"); with causal != 0 the bottom-right
+ * causal rule applies as well.  A row whose scores are all -inf gets O = 0
+ * and lse = -inf.
+ *   q, k, v, o, lse : as for sdpa_prefill_fwd; fp16 or bf16 inputs with the
+ *       same output type and d_qk == d_v in {64, 128}
+ *   mask : device, the inputs' 16-bit type, 16-byte aligned; the value for
+ *       (batch b, query head h, row i, key j) is at element
+ *       b*mask_stride_b + h*mask_stride_h + i*mask_stride_row + j.  A stride
+ *       of 0 broadcasts over batch or heads.  All strides are multiples of 8
+ *       elements and mask_stride_row >= max(kv_len, 8): rows may be padded,
+ *       and the padding is read but never used.
+ * No workspace; errors as for sdpa_prefill_fwd. */
+sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void* q, const void* k,
+                                      const void* v, const void* mask, int64_t mask_stride_b,
+                                      int64_t mask_stride_h, int32_t mask_stride_row, void* o,
+                                      float* lse, void* stream);
+
 /* Two-phase split-KV decode ("xe2-sdp-kernels", section "Assets": production
  * decode, two-phase) for one new token per sequence (q_len == 1).
  * Phase 1: one workgroup per (batch, KV head, split) streams its key range

@@ -279,3 +279,26 @@ def test_mask_convert_argument_errors_before_any_launch():
     assert lib.sdpa_mask_convert(null, a, 16, sdpa.F16, null) == 1
     assert lib.sdpa_mask_convert(ctypes.c_void_p(0x1001), a, 16, sdpa.F16, null) == 5
     assert lib.sdpa_mask_convert(null, null, 0, sdpa.F16, null) == 0      # empty: a no-op
+
+
+def test_masked_prefill_argument_errors_before_any_launch():
+    import ctypes
+
+    lib = sdpa.load()
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    a, null = ctypes.c_void_p(0x1000), ctypes.c_void_p(0)
+    pr = _problem(w, causal=False)
+
+    def call(problem=pr, sb=0, sh=0, row=1024, mask=a):
+        return lib.sdpa_prefill_masked_fwd(None if problem is None else ctypes.byref(problem), a, a, a, mask, sb, sh,
+                                           row, a, null, null)
+
+    assert call(None) == 1
+    assert call(row=1000) == 2                       # row stride below kv_len
+    assert call(row=1028) == 2                       # not a multiple of 8
+    assert call(sb=-8) == 2
+    assert call(sh=12) == 2
+    assert call(mask=null) == 1
+    assert call(mask=ctypes.c_void_p(0x1008)) == 5
+    assert call(_problem(w, causal=False, out_dtype=sdpa.F16)) == 4     # output type differs from the input's
+    assert call(_problem(w, causal=False, q_len=0)) == 0
