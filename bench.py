@@ -163,6 +163,16 @@ def _cached_chunk():
 
 CACHED_CHUNK = _cached_chunk()
 MASK_SHAPE = (16, 4096, 4096)  # bool mask elements converted per call
+
+
+def _masked_workload():
+    from attention_flash_sdpa_amd import inputs
+
+    return inputs.Workload("masked_prefill_bias_2048_bf16", 1, 32, 8, 2048, 2048, 128, 128, "bf16", "bf16", False,
+                           1008)
+
+
+MASKED = _masked_workload()
 CACHED_LEN = 3584
 
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
@@ -228,9 +238,14 @@ def _summarize_trace(d):
     todo.append(("splitkv_decode_bf16_paged64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
     todo.append((CACHED_CHUNK.name, CACHED_CHUNK, "cached"))
     todo.append(("mask_convert_16x4096x4096", None, "mask"))
+    todo.append((MASKED.name, MASKED, "masked"))
     for wname, w, paged in todo:
-        kernels = ([("mask_convert_kernel", None)] if paged == "mask" else
-                   _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached"))
+        if paged == "mask":
+            kernels = [("mask_convert_kernel", None)]
+        elif paged == "masked":
+            kernels = [("prefill_masked_kernel<sdpa::Bf16, 128, 128, false>", None)]
+        else:
+            kernels = _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached")
         for kname, grid in kernels:
             if paged is True and "true>" not in kname:
                 continue  # the combine kernel is the dense one
@@ -526,6 +541,41 @@ def main():
                  "parity": {"bit_exact_rows": 64, "exact": mexact}}
     del msets
 
+    # ------- prefill with a full additive mask (per-head bias) -------
+    from oracle import mask as omask2
+
+    xw = MASKED
+    g = torch.Generator().manual_seed(xw.seed)
+    mq = torch.randn(1, xw.q_len, xw.head_q, xw.d_qk, generator=g).to(torch.bfloat16)
+    mk = torch.randn(1, xw.kv_len, xw.head_kv, xw.d_qk, generator=g).to(torch.bfloat16)
+    mv = torch.randn(1, xw.kv_len, xw.head_kv, xw.d_v, generator=g).to(torch.bfloat16)
+    ii = torch.arange(xw.q_len, device=dev)[:, None]
+    jj = torch.arange(xw.kv_len, device=dev)[None, :]
+    slope = 2.0 ** (-torch.arange(1, xw.head_q + 1, device=dev) / 4.0)
+    mbias = (-(slope[:, None, None] * (ii - jj).abs()[None])).to(torch.bfloat16)[None].contiguous()
+    mqd, mkd, mvd = (t.to(dev) for t in (mq, mk, mv))
+    mo = torch.empty(1, xw.q_len, xw.head_q, xw.d_v, dtype=torch.bfloat16, device=dev)
+
+    def xmstep(i):
+        sdpa.prefill_masked(mqd, mkd, mvd, mbias, scale=xw.scale, out=mo)
+
+    xn = max(args.steps // 10, 1)
+    xmms = _graph_time(xmstep, xn, args.warmup)
+    xmstep(0)
+    torch.cuda.synchronize()
+    G = xw.head_q // xw.head_kv
+    mref = omask2.prefill_masked(mq[:, :, :G], mk[:, :, :1], mv[:, :, :1], mbias[:, :G].cpu(), scale=xw.scale,
+                                 causal=False)["out"]
+    merr = float(np.abs(mo[:, :, :G].double().cpu().numpy() - mref).max())
+    xt = xw.flops() / (xmms * 1e-3) / 1e12
+    masked_line = {"workload": f"{xw.q_len} x {xw.kv_len}, Hq {xw.head_q} / Hkv {xw.head_kv}, d {xw.d_qk}, bf16, "
+                               f"per-head additive bias [1, {xw.head_q}, {xw.q_len}, {xw.kv_len}]",
+                   "value": round(xt, 3), "unit": "TFLOP/s", "ms_per_call": round(xmms, 6), "steps": xn,
+                   "algorithmic_gflop": round(xw.flops() / 1e9, 4), "peak": PEAK_BF16_TFLOPS,
+                   "frac_of_peak": round(xt / PEAK_BF16_TFLOPS, 5),
+                   "mask_bytes": int(mbias.numel() * 2), "parity": {"max_abs_err": merr, "heads_checked": G}}
+    del mqd, mkd, mvd, mbias, mo
+
     # launch floor: a one-element device op, eager and replayed from a graph
     one = torch.zeros(1, device=dev)
     floor_eager = _time(lambda i: one.add_(1.0), args.steps, args.warmup, stream)
@@ -586,6 +636,7 @@ def main():
         },
         "prefill_cached": cached_line,
         "mask_convert": mask_line,
+        "prefill_masked": masked_line,
         "other_workloads": extra,
         "launch_floor_us": {"eager": round(floor_eager * 1e3, 3), "graph": round(floor_graph * 1e3, 3)},
         "device": {"name": props.name, "cus": ncu},
