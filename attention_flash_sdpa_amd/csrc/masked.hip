@@ -6,17 +6,19 @@
 // its mask value added before the online softmax, so every K block is a
 // masked block.  O = softmax(Q K^T * scale + mask [+ causal]) V.
 //
-// Layout of the work: one wavefront = 16 query rows of one head; a workgroup
-// = 4 consecutive 16-row tiles of that head.  S^T = K Q^T on 16x16x32 MFMAs
-// (the 16 query rows are the N dimension), so lane (n16 = l % 16, gq = l / 16)
-// holds the scores of query row n16 for keys 16t + 4gq + r of each 16-key
-// tile t; row max and row sum reduce over the four gq lane groups.  Each wave
-// streams its own K/V blocks of 32 keys into a wave-private double buffer in
-// LDS with direct 16-byte loads (no barriers), and beside them the block's
-// mask tile: 16 rows x 32 keys x 2 bytes = exactly one 1 KiB direct load
-// (lane l: row l / 4, keys 8 (l % 4) .. +7).  Each lane reads its 2 x 4 mask
-// values back with two ds_read_b64 and adds mask * log2(e) to the log2-
-// domain scores.
+// Layout of the work: one wavefront = RT tiles of 16 query rows of one head;
+// a workgroup = 4 such waves on consecutive rows of that head.  S^T = K Q^T
+// on 16x16x32 MFMAs (a tile's 16 query rows are the N dimension), so lane
+// (n16 = l % 16, gq = l / 16) holds the scores of row n16 of each tile for
+// keys 16t + 4gq + r of each 16-key part t; row max and row sum reduce over
+// the four gq lane groups.  Every K and V^T fragment read from LDS feeds the
+// MFMAs of all RT tiles, which also gives the scheduler RT independent
+// softmax chains per block.  Each wave streams its own K/V blocks of 32 keys
+// into a wave-private double buffer in LDS with direct 16-byte loads (no
+// barriers), and beside them the block's mask tiles: 16 rows x 32 keys x 2
+// bytes = exactly one 1 KiB direct load per tile (lane l: row l / 4, keys
+// 8 (l % 4) .. +7).  Each lane reads its 2 x 4 mask values per tile back with
+// two ds_read_b64 and adds mask * log2(e) to the log2-domain scores.
 #include <math.h>
 
 #include "sdpa_device.h"
@@ -34,16 +36,17 @@ __device__ __forceinline__ float half_to_float(uint32_t bits16) {
 
 template <class T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256) void prefill_masked_kernel(const MaskedArgs a) {
+  constexpr int RT = kMaskedRowTiles;         // 16-row tiles per wave
   constexpr int BK = kMaskedBlockK;           // 32 keys per block (two 16-key tiles)
   constexpr int KROW = D * 2, VROW = DV * 2;  // LDS bytes per key row
   constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte slots per row
   constexpr int KBYTES = BK * KROW, VBYTES = BK * VROW;
-  constexpr int MBYTES = 16 * BK * 2;         // mask tile: 16 rows x 32 keys
+  constexpr int MBYTES = RT * 16 * BK * 2;    // mask tiles: RT x 16 rows x 32 keys
   constexpr int STAGE = KBYTES + VBYTES + MBYTES;
   constexpr int K_INSTR = KBYTES / 1024, V_INSTR = VBYTES / 1024;
   constexpr int KS = D / 32;                  // k-steps of the QK MFMA
   constexpr int NT = DV / 16;                 // O^T accumulator tiles
-  static_assert(MBYTES == 1024, "one direct load per mask tile");
+  static_assert(MBYTES == RT * 1024, "one direct load per mask tile");
   static_assert(K_INSTR * 1024 == KBYTES && V_INSTR * 1024 == VBYTES, "whole 1 KiB pieces");
 
   __shared__ __attribute__((aligned(1024))) char smem[kMaskedWaves * 2 * STAGE];
@@ -57,28 +60,35 @@ __global__ __launch_bounds__(256) void prefill_masked_kernel(const MaskedArgs a)
   const int h = bh % a.head_q;
   const int b = bh / a.head_q;
   const int g = h / a.group;
-  const int row0 = (rt * kMaskedWaves + wave) * 16;
+  const int row0 = (rt * kMaskedWaves + wave) * 16 * RT;
   if (row0 >= Sq) return;  // no barriers in this kernel
 
-  const int n16 = lane & 15;  // query row within the tile (MFMA N index)
+  const int n16 = lane & 15;  // query row within a tile (MFMA N index)
   const int gq = lane >> 4;   // lane group of 16
-  const int qrow = row0 + n16;
-  const bool row_ok = qrow < Sq;
-  // keys the tile needs: all, or (causal) up to its last row's last visible key
-  const int last_row = min(row0 + 15, Sq - 1);
+  int qrow[RT], row_end[RT];
+  bool row_ok[RT];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    qrow[u] = row0 + 16 * u + n16;
+    row_ok[u] = qrow[u] < Sq;
+    // keys [0, row_end) of this lane's row are visible before the mask
+    row_end[u] = CAUSAL ? min(Sk, qrow[u] + off + 1) : Sk;
+  }
+  // keys the wave needs: all, or (causal) up to its last row's last visible key
+  const int last_row = min(row0 + 16 * RT - 1, Sq - 1);
   const int k_end = CAUSAL ? min(Sk, max(last_row + off + 1, 0)) : Sk;
   const int nb = (k_end + BK - 1) / BK;
-  // this lane's row: keys [0, row_end) are visible before the mask
-  const int row_end = CAUSAL ? min(Sk, qrow + off + 1) : Sk;
 
   // Q^T fragments (B operand of S^T = K Q^T): row qrow, dims 32s + 8gq .. +7
-  u32x4_t qf[KS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * Sq + min(qrow, Sq - 1)) * a.head_q + h) * D + 8 * gq;
+  u32x4_t qf[RT][KS];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const uint16_t* qp =
+        (const uint16_t*)a.q + ((size_t)(b * Sq + min(qrow[u], Sq - 1)) * a.head_q + h) * D + 8 * gq;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const u32x4_t v = *(const u32x4_t*)(qp + 32 * s);
-      qf[s] = row_ok ? v : u32x4_t{0, 0, 0, 0};
+      qf[u][s] = row_ok[u] ? v : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -104,8 +114,10 @@ __global__ __launch_bounds__(256) void prefill_masked_kernel(const MaskedArgs a)
   // mask rows of this tile (rows past the end repeat the last row), lane's
   // 8-key chunk; a chunk is clamped to the padded row (row stride >= Sk,
   // a multiple of 8), so it never leaves the row: keys past Sk are masked
-  const uint16_t* mrow = (const uint16_t*)a.mask + (size_t)b * a.mask_sb + (size_t)h * a.mask_sh +
-                         (size_t)min(row0 + (lane >> 2), Sq - 1) * a.mask_row;
+  const uint16_t* mbase = (const uint16_t*)a.mask + (size_t)b * a.mask_sb + (size_t)h * a.mask_sh;
+  const uint16_t* mrow[RT];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) mrow[u] = mbase + (size_t)min(row0 + 16 * u + (lane >> 2), Sq - 1) * a.mask_row;
   const int mcol = 8 * (lane & 3);
   auto issue_fill = [&](int key0, int stage) __attribute__((always_inline)) {
     const uint32_t kl = lds_w + stage * STAGE, vl = kl + KBYTES, ml = vl + VBYTES;
@@ -115,7 +127,8 @@ __global__ __launch_bounds__(256) void prefill_masked_kernel(const MaskedArgs a)
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i)
       global_to_lds_16(vbase + (size_t)min(key0 + vrow[i], last_key) * vstride + vcol[i], vl + i * 1024);
-    global_to_lds_16(mrow + min(key0 + mcol, a.mask_row - 8), ml);
+#pragma unroll
+    for (int u = 0; u < RT; ++u) global_to_lds_16(mrow[u] + min(key0 + mcol, a.mask_row - 8), ml + u * 1024);
   };
 
   // K fragment (A operand): key row 16t + l%16, slot 4s + l/16
@@ -139,70 +152,84 @@ __global__ __launch_bounds__(256) void prefill_masked_kernel(const MaskedArgs a)
   // mask values of row n16, keys 16t + 4gq .. +3: 8 bytes at row * 64 + 32t + 8gq
   const uint32_t moff = n16 * (BK * 2) + 8 * gq;
 
-  f32x4_t acc[NT];
+  f32x4_t acc[RT][NT];
+  float m_run[RT], l_run[RT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int u = 0; u < RT; ++u) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[u][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+  }
   const float s2 = a.s2;
 
   auto block = [&](int key0, int stage) __attribute__((always_inline)) {
     const uint32_t ks = lds_w + stage * STAGE, vs = ks + KBYTES, ms = vs + VBYTES;
-    f32x4_t sc[2];
+    f32x4_t sc[RT][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sc[t] = mfma16x16x32<T>(lds_read_b128(ks + koff[s] + 16 * t * KROW), qf[s], sc[t]);
-    }
-    // log2-domain scores plus the mask; keys past the row's end are removed
-    float x[8];
-    float bmax = -INFINITY;
+      for (int u = 0; u < RT; ++u) sc[u][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x2_t mv = *(SDPA_LDS const u32x2_t*)(uintptr_t)(ms + moff + 32 * t);
+      for (int s = 0; s < KS; ++s) {
+        const u32x4_t kf = lds_read_b128(ks + koff[s] + 16 * t * KROW);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t bits = (r < 2 ? mv.x : mv.y) >> (16 * (r & 1)) & 0xffffu;
-        const float mval = half_to_float<T>(bits);
-        const bool vis = key0 + 16 * t + 4 * gq + r < row_end;
-        const float v = vis ? __builtin_fmaf(mval, kLog2e, sc[t][r] * s2) : -INFINITY;
-        x[4 * t + r] = v;
-        bmax = fmaxf(bmax, v);
+        for (int u = 0; u < RT; ++u) sc[u][t] = mfma16x16x32<T>(kf, qf[u][s], sc[u][t]);
       }
     }
-    bmax = fmaxf(bmax, xor_lane(bmax, 16));
-    bmax = fmaxf(bmax, xor_lane(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
-    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_sub);
-    m_run = m_new;
-    // P^T as the B operand: k = 8gq + j takes tile 0 register j (j < 4) and
-    // tile 1 register j-4 (j >= 4)
-    u32x4_t pf;
-    pf.x = pack2<T>(fast_exp2(x[0] - m_sub), fast_exp2(x[1] - m_sub));
-    pf.y = pack2<T>(fast_exp2(x[2] - m_sub), fast_exp2(x[3] - m_sub));
-    pf.z = pack2<T>(fast_exp2(x[4] - m_sub), fast_exp2(x[5] - m_sub));
-    pf.w = pack2<T>(fast_exp2(x[6] - m_sub), fast_exp2(x[7] - m_sub));
-    float psum = add_pair<T>(pf.x, 0.f);
-    psum = add_pair<T>(pf.y, psum);
-    psum = add_pair<T>(pf.z, psum);
-    psum = add_pair<T>(pf.w, psum);
-    l_run = l_run * alpha + psum;
+    u32x4_t pf[RT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+    for (int u = 0; u < RT; ++u) {
+      // log2-domain scores plus the mask; keys past the row's end are removed
+      float x[8];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x2_t mv = *(SDPA_LDS const u32x2_t*)(uintptr_t)(ms + u * 1024 + moff + 32 * t);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t bits = (r < 2 ? mv.x : mv.y) >> (16 * (r & 1)) & 0xffffu;
+          const float mval = half_to_float<T>(bits);
+          const bool vis = key0 + 16 * t + 4 * gq + r < row_end[u];
+          const float v = vis ? __builtin_fmaf(mval, kLog2e, sc[u][t][r] * s2) : -INFINITY;
+          x[4 * t + r] = v;
+          bmax = fmaxf(bmax, v);
+        }
+      }
+      bmax = fmaxf(bmax, xor_lane(bmax, 16));
+      bmax = fmaxf(bmax, xor_lane(bmax, 32));
+      const float m_new = fmaxf(m_run[u], bmax);
+      const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[u] - m_sub);
+      m_run[u] = m_new;
+      // P^T as the B operand: k = 8gq + j takes part 0 register j (j < 4)
+      // and part 1 register j-4 (j >= 4)
+      pf[u].x = pack2<T>(fast_exp2(x[0] - m_sub), fast_exp2(x[1] - m_sub));
+      pf[u].y = pack2<T>(fast_exp2(x[2] - m_sub), fast_exp2(x[3] - m_sub));
+      pf[u].z = pack2<T>(fast_exp2(x[4] - m_sub), fast_exp2(x[5] - m_sub));
+      pf[u].w = pack2<T>(fast_exp2(x[6] - m_sub), fast_exp2(x[7] - m_sub));
+      float psum = add_pair<T>(pf[u].x, 0.f);
+      psum = add_pair<T>(pf[u].y, psum);
+      psum = add_pair<T>(pf[u].z, psum);
+      psum = add_pair<T>(pf[u].w, psum);
+      l_run[u] = l_run[u] * alpha + psum;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[u][t] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const u32x2_t lo = lds_read_tr16(vs + voff[0][t]);
       const u32x2_t hi = lds_read_tr16(vs + voff[1][t]);
       const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
-      acc[t] = mfma16x16x32<T>(vf, pf, acc[t]);
+#pragma unroll
+      for (int u = 0; u < RT; ++u) acc[u][t] = mfma16x16x32<T>(vf, pf[u], acc[u][t]);
     }
   };
 
   // K/V/mask pipeline: block i+1 in flight while block i computes; the
   // direct loads are invisible to the compiler's wait counting, so every
   // wait is explicit (buffers private to the wave: no barrier)
-  constexpr int PER_BLOCK = K_INSTR + V_INSTR + 1;
+  constexpr int PER_BLOCK = K_INSTR + V_INSTR + RT;
   if (nb > 0) {
     issue_fill(0, 0);
     int i = 0;
@@ -216,17 +243,21 @@ __global__ __launch_bounds__(256) void prefill_masked_kernel(const MaskedArgs a)
   }
 
   // epilogue: O = O^T / l for row qrow (lane holds values 16t + 4gq + r)
-  float l_tot = l_run + xor_lane(l_run, 16);
-  l_tot += xor_lane(l_tot, 32);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = (uint16_t*)a.o + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV + 4 * gq;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      *(u32x2_t*)(op + 16 * t) = u32x2_t{pack2<T>(acc[t][0] * inv, acc[t][1] * inv),
-                                         pack2<T>(acc[t][2] * inv, acc[t][3] * inv)};
-    if (a.lse != nullptr && gq == 0)
-      a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  for (int u = 0; u < RT; ++u) {
+    float l_tot = l_run[u] + xor_lane(l_run[u], 16);
+    l_tot += xor_lane(l_tot, 32);
+    if (row_ok[u]) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* op = (uint16_t*)a.o + ((size_t)(b * Sq + qrow[u]) * a.head_q + h) * DV + 4 * gq;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *(u32x2_t*)(op + 16 * t) = u32x2_t{pack2<T>(acc[u][t][0] * inv, acc[u][t][1] * inv),
+                                           pack2<T>(acc[u][t][2] * inv, acc[u][t][3] * inv)};
+      if (a.lse != nullptr && gq == 0)
+        a.lse[((size_t)b * a.head_q + h) * Sq + qrow[u]] =
+            l_tot > 0.f ? (m_run[u] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 

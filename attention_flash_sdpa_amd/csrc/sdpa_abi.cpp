@@ -274,7 +274,8 @@ sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void*
               mask_stride_row, p.kv_len);
     return SDPA_ERR_BAD_SHAPE;
   }
-  const int64_t row_tiles = ((int64_t)p.q_len + 16 * kMaskedWaves - 1) / (16 * kMaskedWaves);
+  const int64_t rows_per_group = 16 * kMaskedRowTiles * kMaskedWaves;
+  const int64_t row_tiles = ((int64_t)p.q_len + rows_per_group - 1) / rows_per_group;
   if ((int64_t)p.batch * p.head_q * row_tiles >= ((int64_t)1 << 31)) {
     set_error("grid too large (%lld workgroups)", (long long)((int64_t)p.batch * p.head_q * row_tiles));
     return SDPA_ERR_BAD_SHAPE;

@@ -48,7 +48,8 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per CU (gfx950)
 constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows per workgroup
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
-constexpr int kMaskedWaves = 4;    // masked prefill: 16-row tiles (waves) per workgroup
+constexpr int kMaskedWaves = 4;    // masked prefill: waves per workgroup
+constexpr int kMaskedRowTiles = 2; // masked prefill: 16-row tiles per wave
 constexpr int kMaskedBlockK = 32;  // masked prefill: keys per K/V/mask block
 constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
@@ -125,7 +126,7 @@ struct MaskedArgs {
   int32_t batch, q_len, kv_len, head_q, head_kv, group;
   int64_t mask_sb, mask_sh;  // element strides of the mask's batch and head (0: broadcast)
   int32_t mask_row;          // element stride between mask rows (multiple of 8, >= max(kv_len, 8))
-  int32_t row_tiles;         // workgroups per (batch, head): ceil(q_len / 64)
+  int32_t row_tiles;         // workgroups per (batch, head): ceil(q_len / (16 * tiles * waves))
   float s2;                  // scale * log2(e)
 };
 int launch_prefill_masked(const MaskedArgs& a, int in_dtype, int d, int causal, ihipStream_t* stream);
