@@ -49,7 +49,7 @@ constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows p
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
 constexpr int kMaskedWaves = 4;    // masked prefill: waves per workgroup
-constexpr int kMaskedRowTiles = 2; // masked prefill: 16-row tiles per wave
+constexpr int kMaskedRowTiles = 4; // masked prefill: 16-row tiles per wave
 constexpr int kMaskedBlockK = 32;  // masked prefill: keys per K/V/mask block
 constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
