@@ -80,6 +80,8 @@ CASES = [
     (1, 1, 500, 512, 1, 8, 1, 64, torch.bfloat16, True),         # one new token
     (1, 200, 5, 5, 200, 4, 2, 64, torch.float16, True),          # a few cached keys
     (1, 40, 700, 700, 0, 8, 2, 128, torch.bfloat16, False),      # no new keys: the cache only
+    (2, 96, 64, 64, 40, 8, 4, 64, torch.float16, False),         # full attention, more queries than new keys
+    (1, 300, 4000, 4096, 300, 16, 2, 128, torch.float16, True),  # fp16, d 128, long cache, 8 query heads per KV head
 ]
 
 

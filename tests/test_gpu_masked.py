@@ -80,6 +80,8 @@ CASES = [
     (1, 333, 1000, 4, 4, 128, torch.bfloat16, True, 1, 1, "bias"),
     (2, 17, 5, 2, 1, 64, torch.bfloat16, False, 2, 1, "keep"),
     (3, 50, 300, 6, 3, 128, torch.float16, False, 3, 6, "bias+keep"),
+    (1, 200, 150, 4, 1, 64, torch.bfloat16, True, 1, 1, "bias"),      # causal, more queries than keys: empty rows
+    (2, 257, 513, 8, 8, 128, torch.bfloat16, False, 2, 8, "keep"),    # ragged rows and keys, per-(batch, head) mask
 ]
 
 

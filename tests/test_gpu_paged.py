@@ -80,6 +80,8 @@ PAGED = [
     (3, 450, 12, 3, 64, torch.bfloat16, 32, 40, "mix"),    # many splits, most of them empty
     (1, 8192, 4, 1, 64, torch.bfloat16, 32, 1, "full"),    # 256 pages in one split: table reloads
     (3, 5000, 6, 2, 128, torch.float16, 32, 2, "mix"),     # 79 pages per split: table reloads, lengths 0, 1, full
+    (4, 3000, 16, 1, 128, torch.bfloat16, 256, 0, "mix"),  # 16 query heads per KV head, 256-key pages
+    (2, 640, 12, 12, 64, torch.float16, 64, 3, "full"),    # no grouping (MHA)
 ]
 
 
