@@ -311,6 +311,8 @@ def decode_paged(q, k_cache, v_cache, *, page_table=None, seq_lens=None, kv_len=
     else:
         num_pages = page_size = pages_per_seq = 0
         kv_len = int(k_cache.shape[1]) if kv_len is None else kv_len
+        if kv_len > k_cache.shape[1]:  # the dense cache is also the row stride: it must hold kv_len keys
+            raise ValueError(f"kv_len {kv_len} exceeds the dense cache's {k_cache.shape[1]} keys")
     if seq_lens is not None and seq_lens.shape != (B,):
         raise ValueError("seq_lens must be [B]")
     if out is None:

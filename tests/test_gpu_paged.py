@@ -193,3 +193,10 @@ def test_paged_decode_empty_batch_and_zero_lengths(dev):
     assert (out.float() == 0).all() and torch.isneginf(lse).all()
     empty = sdpa.decode_paged(q[:0], pool, pool, page_table=table[:0])
     assert empty.shape == (0, 8, 128)
+
+
+def test_dense_kv_len_beyond_the_cache_is_rejected(dev):
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(2, 64, 2, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        sdpa.decode_paged(q, k, k, kv_len=65)
