@@ -151,7 +151,8 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
 # kernel-source files whose text decides each profiled kernel's code
 _SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_wide.hip", "sdpa_device.h",
                         "sdpa_internal.h", "sdpa_bounds.h"],
-            "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"]}
+            "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"],
+            "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"]}
 def _cached_chunk():
     from attention_flash_sdpa_amd import inputs
 
@@ -181,7 +182,8 @@ _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_deco
 def _counters_pass():
     """Short run for `rocprofv3 --pmc`: a plain 256 MiB device copy (the
     calibration of the byte counters), then 5 calls each of the causal GQA
-    prefill and of the split-KV decode (rotating K/V sets)."""
+    prefill and of the split-KV decode (rotating K/V sets), then 6 mask
+    conversions (two alternating buffer sets)."""
     import torch
 
     import attention_flash_sdpa_amd as sdpa
@@ -211,7 +213,13 @@ def _counters_pass():
     for i in range(4 * 5):
         sdpa.decode(dqd, sets[i % 4][0], sets[i % 4][1], scale=dw.scale, out=dout, workspace=ws)
     torch.cuda.synchronize()
-    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20", flush=True)
+    del sets
+    msets = [(torch.rand(MASK_SHAPE, device=dev) < 0.5, torch.empty(MASK_SHAPE, dtype=torch.bfloat16, device=dev))
+             for _ in range(2)]
+    for i in range(6):
+        sdpa.mask_convert(msets[i % 2][0], out=msets[i % 2][1])
+    torch.cuda.synchronize()
+    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20, mask conversion x6", flush=True)
 
 
 def _read_csv(path):
@@ -288,11 +296,14 @@ def _summarize_counters(fetch_dir, write_dir):
     reads for the 256 MiB device copy, written to profiles/*_counters.txt."""
     import statistics
 
+    import numpy as np
+
     import attention_flash_sdpa_amd as sdpa
     from attention_flash_sdpa_amd import inputs
 
     copy_bytes = 256 << 20
     res = {}
+    mres = {}  # mask conversion: (mean KiB per dispatch, dispatches)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
@@ -308,6 +319,9 @@ def _summarize_counters(fetch_dir, write_dir):
                         if kname in r["Kernel_Name"] and int(r["Grid_Size"]) == grid]
                 per[(wname, kname)] = (statistics.mean(vals), len(vals))
         res[counter] = (kib_copy, factor, per, copies[0]["Kernel_Name"])
+        mvals = [float(r["Counter_Value"]) for r in rows if "mask_convert_kernel" in r["Kernel_Name"]]
+        if mvals:
+            mres[counter] = (statistics.mean(mvals), len(mvals))
     for wname, stem in _PROFILED.items():
         w = inputs.WORKLOADS[wname]
         kind = "decode" if w.decode else "prefill"
@@ -334,6 +348,26 @@ def _summarize_counters(fetch_dir, write_dir):
             f.write(f"hbm_bytes_per_launch: {total:.0f}\n")
             f.write(f"ratio to algorithmic: {total / alg:.3f}\n")
             f.write(f"source_sha256: {_src_hash(*_SOURCES[kind])}\n")
+        print("wrote", out)
+    if len(mres) == 2:
+        out = os.path.join(ROOT, "profiles", "mask_convert_16x4096x4096_counters.txt")
+        total = 0.0
+        with open(out, "w") as f:
+            f.write(f"workload: bool mask {list(MASK_SHAPE)} -> bf16 additive\n")
+            f.write("commands: as for prefill_gqa_causal_bf16_counters.txt (the counters pass ends with 6 mask "
+                    "conversions)\n")
+            for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                kib_copy, factor, _, cname = res[counter]
+                kib, n = mres[counter]
+                b = kib * 1024.0 * factor
+                total += b
+                f.write(f"{counter}: scale factor {factor:.4f} ({cname}); mask_convert_kernel: {kib:.1f} "
+                        f"KiB/dispatch over {n} dispatches -> {b:.0f} B\n")
+            alg = 3 * int(np.prod(MASK_SHAPE))
+            f.write(f"algorithmic bytes per call (mask read once, additive mask written once): {alg}\n")
+            f.write(f"hbm_bytes_per_launch: {total:.0f}\n")
+            f.write(f"ratio to algorithmic: {total / alg:.3f}\n")
+            f.write(f"source_sha256: {_src_hash(*_SOURCES['mask'])}\n")
         print("wrote", out)
 
 
@@ -537,7 +571,8 @@ def main():
                  "ms_per_call": round(mms, 6), "steps": args.decode_steps, "buffer_sets": len(msets),
                  "algorithmic_bytes": mbytes,
                  "roofline": {"bound": "hbm", "achieved": round(mgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": round(mgbs / PEAK_HBM_GBS, 5), "traffic": None},
+                              "frac": round(mgbs / PEAK_HBM_GBS, 5),
+                              "traffic": _traffic("mask_convert_16x4096x4096_counters.txt", _SOURCES["mask"])},
                  "parity": {"bit_exact_rows": 64, "exact": mexact}}
     del msets
 
