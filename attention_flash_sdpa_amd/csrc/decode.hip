@@ -27,11 +27,13 @@
 // length launch mode, section "Launcher -> kernel"): sequence b holds
 // seq_lens[b] keys, and with a page table its keys p*page_size ..
 // (p+1)*page_size - 1 sit in physical page page_table[b][p] of a
-// [num_pages, page_size, head_kv, d] pool.  page_size is a multiple of the
-// 32-key block, so every block lies in one page and costs one table entry,
-// read from a register that holds 64 of the split's entries (one per lane).
-// An entry outside [0, num_pages) is never dereferenced: page 0 is read in
-// its place and the affected rows come out NaN.
+// [num_pages, page_size, head_kv, d] pool.  A page size that is a multiple
+// of the 32-key block puts every block in one page (one table entry, a scalar
+// base); pages of 8 or 16 keys split a block over 4 or 2 pages, and each lane
+// takes its key row's page.  Table entries come from a register that holds
+// 64 of the split's entries (one per lane).  An entry outside [0, num_pages)
+// is never dereferenced: page 0 is read in its place and the affected rows
+// come out NaN.
 #include <math.h>
 
 #include "sdpa_device.h"
@@ -122,6 +124,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   int pt_vals = 0;
   bool pt_bad = false;
   const int32_t* pt = PAGED ? a.page_table + (size_t)b * a.pages_per_seq : nullptr;
+  // pages of fewer than BK keys: a block covers nsub = BK / page_size whole
+  // pages (blocks start at multiples of BK, so pt_row stays 0)
+  const int nsub = PAGED && a.page_size < BK ? BK / a.page_size : 1;
+  const int sub_shift = nsub == 4 ? 3 : 4;  // log2 of the keys per page (8 or 16)
   if constexpr (PAGED) {
     if (nb > 0) {
       pt_page = k_begin / a.page_size;
@@ -138,9 +144,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     const int lim = last_key - key0;
     size_t row0 = (size_t)key0;
     if constexpr (PAGED) {
-      if (pt_page - pt_first >= 64) {  // next 64 entries (long splits only)
-        pt_first += 64;
+      if (pt_page - pt_first + nsub > 64) {  // next 64 entries (long splits only)
+        pt_first = pt_page;
         pt_vals = (int)global_load_dword_sync(pt + min(pt_first + lane, a.pages_per_seq - 1));
+      }
+      if (nsub > 1) {
+        // small pages: entries of the block's pages that hold a key of the
+        // sequence (rows past its end are clamped to its last key, so the
+        // others are never used and may hold anything)
+        int ph[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool used = j < nsub && (j << sub_shift) <= lim;
+          int e = __builtin_amdgcn_readlane(pt_vals, pt_page - pt_first + (used ? j : 0));
+          if ((uint32_t)e >= (uint32_t)a.num_pages) {
+            pt_bad = pt_bad || used;
+            e = 0;
+          }
+          ph[j] = e;
+        }
+        pt_page += nsub;
+        auto addr = [&](const char* base, int r, size_t stride, int col) __attribute__((always_inline)) {
+          const int j = r >> sub_shift;
+          const int e = j == 0 ? ph[0] : (j == 1 ? ph[1] : (j == 2 ? ph[2] : ph[3]));
+          const size_t row = (size_t)e * a.page_size + (r & ((1 << sub_shift) - 1));
+          return base + row * stride + col;
+        };
+#pragma unroll
+        for (int i = 0; i < K_INSTR; ++i)
+          global_to_lds_16(addr(kbase, min(krow[i], lim), kstride, kcol[i]), kl + i * 1024);
+#pragma unroll
+        for (int i = 0; i < V_INSTR; ++i)
+          global_to_lds_16(addr(vbase, min(vrow[i], lim), vstride, vcol[i]), vl + i * 1024);
+        return;
       }
       int phys = __builtin_amdgcn_readlane(pt_vals, pt_page - pt_first);
       if ((uint32_t)phys >= (uint32_t)a.num_pages) {

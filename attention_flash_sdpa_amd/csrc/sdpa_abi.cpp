@@ -388,8 +388,8 @@ sdpa_status_t sdpa_decode_paged_fwd(const sdpa_problem_t* problem, const void* q
   }
   const sdpa_problem_t& p = *problem;
   if (page_table != nullptr && p.batch > 0 && p.kv_len > 0) {
-    if (page_size <= 0 || page_size % kDecodeBlockK != 0) {
-      set_error("page_size must be a positive multiple of %d (got %d)", kDecodeBlockK, page_size);
+    if (!(page_size == 8 || page_size == 16 || (page_size > 0 && page_size % kDecodeBlockK == 0))) {
+      set_error("page_size must be 8, 16 or a positive multiple of %d (got %d)", kDecodeBlockK, page_size);
       return SDPA_ERR_BAD_SHAPE;
     }
     if (num_pages <= 0 || pages_per_seq <= 0 || (int64_t)pages_per_seq * page_size < p.kv_len) {

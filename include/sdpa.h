@@ -269,8 +269,8 @@ sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, cons
  *   page_table != NULL : k_cache, v_cache are pools [num_pages, page_size,
  *       head_kv, d_qk|d_v]; page_table is device int32 [batch, pages_per_seq]
  *       and keys p*page_size .. (p+1)*page_size - 1 of sequence b sit in
- *       physical page page_table[b * pages_per_seq + p].  page_size must be a
- *       positive multiple of 32, pages_per_seq * page_size >= kv_len.
+ *       physical page page_table[b * pages_per_seq + p].  page_size must be 8,
+ *       16 or a positive multiple of 32, pages_per_seq * page_size >= kv_len.
  *   seq_lens : device int32 [batch], sequence b attends to its first
  *       seq_lens[b] keys (clamped to [0, kv_len]; 0 gives O = 0 and
  *       lse = -inf), or NULL for kv_len keys each.

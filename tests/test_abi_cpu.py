@@ -211,9 +211,12 @@ def test_paged_decode_argument_errors_before_any_launch():
                                          num_pages, page_size, per_seq, a, null, 0, ws, ws_bytes, null)
 
     assert call(problem=None) == 1
-    assert call(page_size=48) == 2                      # not a multiple of the 32-key block
+    assert call(page_size=48) == 2                      # not 8, 16 or a multiple of the 32-key block
     assert b"page_size" in lib.sdpa_last_error()
     assert call(page_size=0) == 2
+    assert call(page_size=24) == 2
+    assert call(page_size=4) == 2
+    assert call(page_size=16, per_seq=dw.kv_len // 16, num_pages=dw.batch * dw.kv_len // 16, ws_bytes=need - 16) == 6
     assert call(per_seq=pages - 1) == 2                 # table row shorter than kv_len
     assert call(num_pages=0) == 2
     assert call(num_pages=2 ** 30) == 2                 # pool rows overflow int32

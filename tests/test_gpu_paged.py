@@ -82,6 +82,9 @@ PAGED = [
     (3, 5000, 6, 2, 128, torch.float16, 32, 2, "mix"),     # 79 pages per split: table reloads, lengths 0, 1, full
     (4, 3000, 16, 1, 128, torch.bfloat16, 256, 0, "mix"),  # 16 query heads per KV head, 256-key pages
     (2, 640, 12, 12, 64, torch.float16, 64, 3, "full"),    # no grouping (MHA)
+    (4, 1000, 8, 2, 128, torch.bfloat16, 16, 0, "mix"),    # 16-key pages: two pages per block
+    (3, 777, 16, 4, 64, torch.float16, 8, 0, "mix"),       # 8-key pages: four pages per block
+    (3, 5000, 6, 2, 128, torch.bfloat16, 8, 2, "mix"),     # 8-key pages, 316 pages per split: table reloads
 ]
 
 
@@ -200,3 +203,40 @@ def test_dense_kv_len_beyond_the_cache_is_rejected(dev):
     k = torch.zeros(2, 64, 2, 128, dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError):
         sdpa.decode_paged(q, k, k, kv_len=65)
+
+
+@pytest.mark.parametrize("ps", [8, 16, 64])
+def test_table_entries_past_the_sequence_end_are_ignored(dev, ps):
+    """Entries of a table row past a sequence's last page may hold anything
+    (here out-of-range values): they are never used and poison nothing."""
+    from oracle import paged as op
+
+    B, Sk, Hq, Hkv, D = 4, 300, 8, 2, 64
+    q, k, v = _draw(B, Sk, Hq, Hkv, D, torch.bfloat16, 21 + ps)
+    kp, vp, table = inputs.paginate(k, v, ps, seed=22, spare_pages=1)
+    lens = torch.tensor([0, 1, 77, 300], dtype=torch.int32)
+    garbage = table.clone()
+    for b in range(B):
+        garbage[b, -(-int(lens[b]) // ps):] = -7 - b
+    _say(f"garbage past the sequence ends, page {ps}")
+    out, lse = _run(dev, q, kp, vp, table=garbage, lens=lens, kv_len=Sk)
+    ref = op.decode_paged(q, kp, vp, page_table=table, page_size=ps, seq_lens=lens.tolist(), scale=1 / math.sqrt(D))
+    _check(out, lse, ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("ps", [8, 16])
+def test_small_page_out_of_range_entry_poisons_its_sequence(dev, ps):
+    from oracle import paged as op
+
+    B, Sk, Hq, Hkv, D = 3, 200, 4, 1, 128
+    q, k, v = _draw(B, Sk, Hq, Hkv, D, torch.bfloat16, 31 + ps)
+    kp, vp, table = inputs.paginate(k, v, ps, seed=32, fill=0.0)
+    bad = table.clone()
+    bad[1, 5] = kp.shape[0]
+    _say(f"out-of-range entry with {ps}-key pages")
+    out, lse = _run(dev, q, kp, vp, table=bad, lens=None, kv_len=Sk)
+    o = out.double().cpu().numpy()
+    assert np.isnan(o[1]).all() and np.isnan(lse[1].cpu().numpy()).all()
+    ref = op.decode_paged(q, kp, vp, page_table=table, page_size=ps, seq_lens=None, scale=1 / math.sqrt(D),
+                          kv_len=Sk)
+    assert np.abs(o[[0, 2]] - ref["out"][[0, 2]]).max() <= TOL16
