@@ -243,7 +243,7 @@ def _summarize_trace(d):
     cmd = open(os.path.join(d, "command.txt")).read().strip() if os.path.exists(os.path.join(d, "command.txt")) \
         else "(command not recorded)"
     todo = [(wname, w, False) for wname, w in inputs.WORKLOADS.items()]
-    todo.append(("splitkv_decode_bf16_paged64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
+    todo.append(("splitkv_decode_bf16_paged_16_and_64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
     todo.append((CACHED_CHUNK.name, CACHED_CHUNK, "cached"))
     todo.append(("mask_convert_16x4096x4096", None, "mask"))
     todo.append((MASKED.name, MASKED, "masked"))
@@ -460,35 +460,45 @@ def main():
     decode_err = float(np.abs(dgot - dref).max())
     del sets
 
-    # ------- the same decode over a paged cache: 64-key pages, shuffled -------
+    # ------- the same decode over a paged cache: 64- and 16-key pages, shuffled -------
     from oracle import paged as opaged
 
-    PS = 64
-    P = dw.kv_len // PS
-    kp0, vp0, table0 = inputs.paginate(dk0, dv0, PS, seed=dw.seed + 1)
-    psets = [(kp0.to(dev), vp0.to(dev), table0.to(dev))]
-    for s in range(1, dw.kv_sets):
-        g = torch.Generator(device=dev).manual_seed(dw.seed + 100 * s)
-        pk, pv = (torch.randn(t.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-                  for t in (kp0, vp0))
-        perm = torch.randperm(dw.batch * P, generator=torch.Generator().manual_seed(dw.seed + 100 * s + 1))
-        psets.append((pk, pv, perm.reshape(dw.batch, P).to(torch.int32).to(dev)))
-    full = torch.full((dw.batch,), dw.kv_len, dtype=torch.int32, device=dev)
+    paged_lines = {}
+    for PS in (64, 16):
+        P = dw.kv_len // PS
+        kp0, vp0, table0 = inputs.paginate(dk0, dv0, PS, seed=dw.seed + 1)
+        psets = [(kp0.to(dev), vp0.to(dev), table0.to(dev))]
+        for s in range(1, dw.kv_sets):
+            g = torch.Generator(device=dev).manual_seed(dw.seed + 100 * s)
+            pk, pv = (torch.randn(t.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                      for t in (kp0, vp0))
+            perm = torch.randperm(dw.batch * P, generator=torch.Generator().manual_seed(dw.seed + 100 * s + 1))
+            psets.append((pk, pv, perm.reshape(dw.batch, P).to(torch.int32).to(dev)))
+        full = torch.full((dw.batch,), dw.kv_len, dtype=torch.int32, device=dev)
 
-    def pstep(i):
-        pk, pv, pt = psets[i % len(psets)]
-        sdpa.decode_paged(dqd, pk, pv, page_table=pt, seq_lens=full, scale=dw.scale, out=dout, workspace=ws)
+        def pstep(i):
+            pk, pv, pt = psets[i % len(psets)]
+            sdpa.decode_paged(dqd, pk, pv, page_table=pt, seq_lens=full, scale=dw.scale, out=dout, workspace=ws)
 
-    peager_ms = _time(pstep, args.decode_steps, args.warmup, stream)
-    pms = _graph_time(pstep, args.decode_steps, args.warmup, period=len(psets))
-    pbytes = dbytes + table0.numel() * 4 + dw.batch * 4
-    pgbs = pbytes / (pms * 1e-3) / 1e9
-    pstep(0)
-    torch.cuda.synchronize()
-    pref = opaged.decode_paged(dq.reshape(dw.batch, dw.head_q, dw.d_qk), kp0, vp0, page_table=table0,
-                               page_size=PS, seq_lens=None, scale=dw.scale)["out"]
-    paged_err = float(np.abs(dout.double().cpu().numpy() - pref).max())
-    del psets, kp0, vp0
+        peager_ms = _time(pstep, args.decode_steps, args.warmup, stream)
+        pms = _graph_time(pstep, args.decode_steps, args.warmup, period=len(psets))
+        pbytes = dbytes + table0.numel() * 4 + dw.batch * 4
+        pgbs = pbytes / (pms * 1e-3) / 1e9
+        pstep(0)
+        torch.cuda.synchronize()
+        pref = opaged.decode_paged(dq.reshape(dw.batch, dw.head_q, dw.d_qk), kp0, vp0, page_table=table0,
+                                   page_size=PS, seq_lens=None, scale=dw.scale)["out"]
+        paged_err = float(np.abs(dout.double().cpu().numpy() - pref).max())
+        del psets, kp0, vp0
+        paged_lines[PS] = {
+            "workload": f"{dw.name} in {PS}-key pages (shuffled physical order, every sequence full)",
+            "value": round(pgbs, 2), "unit": "GB/s", "ms_per_call": round(pms, 6),
+            "eager_ms_per_call": round(peager_ms, 6), "steps": args.decode_steps, "kv_sets": dw.kv_sets,
+            "algorithmic_bytes": pbytes,
+            "roofline": {"bound": "hbm", "achieved": round(pgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
+            "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
+        }
 
     # ---------------- other prefill workloads (context lines) ----------------
     extra = {}
@@ -660,15 +670,8 @@ def main():
                          "frac": round(dgbs / PEAK_HBM_GBS, 5), "traffic": dtraffic},
             "parity": {"max_abs_err": decode_err},
         },
-        "decode_paged": {
-            "workload": f"{dw.name} in {PS}-key pages (shuffled physical order, every sequence full)",
-            "value": round(pgbs, 2), "unit": "GB/s", "ms_per_call": round(pms, 6),
-            "eager_ms_per_call": round(peager_ms, 6), "steps": args.decode_steps, "kv_sets": dw.kv_sets,
-            "algorithmic_bytes": pbytes,
-            "roofline": {"bound": "hbm", "achieved": round(pgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
-            "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
-        },
+        "decode_paged": paged_lines[64],
+        "decode_paged_16": paged_lines[16],
         "prefill_cached": cached_line,
         "mask_convert": mask_line,
         "prefill_masked": masked_line,
