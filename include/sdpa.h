@@ -1,7 +1,9 @@
 /*
  * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product-attention
- * forward library: a causal/full prefill mainloop and a two-phase split-KV
- * decode, both computing
+ * forward library: a causal/full prefill mainloop (also over a cached prefix,
+ * and with a full additive mask), a two-phase split-KV decode (also over
+ * variable-length and paged caches) and a boolean-to-additive mask
+ * conversion.  The attention calls compute
  *
  *     O = softmax(Q K^T * scale + mask) V
  *
