@@ -329,10 +329,10 @@ def _summarize_counters(fetch_dir, write_dir):
         total = 0.0
         with open(out, "w") as f:
             f.write(f"workload: {wname}\n")
-            f.write("commands:\n  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run "
-                    "-- python3 bench.py --counters-pass\n  rocprofv3 --pmc WRITE_SIZE --output-format csv "
-                    "-d gpurun_out/pmc_write -o run -- python3 bench.py --counters-pass\n"
-                    "  python3 bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write\n")
+            f.write(f"commands:\n  rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run "
+                    f"-- python3 bench.py --counters-pass\n  rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                    f"-d {write_dir} -o run -- python3 bench.py --counters-pass\n"
+                    f"  python3 bench.py --summarize-counters {fetch_dir} {write_dir}\n")
             for counter in ("FETCH_SIZE", "WRITE_SIZE"):
                 kib_copy, factor, per, cname = res[counter]
                 f.write(f"{counter}: calibration copy of {copy_bytes} B ({cname}) reads {kib_copy:.1f} KiB "
