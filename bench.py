@@ -63,6 +63,11 @@ def _traffic(profile_name, src_names):
     return float(t.group(1))
 
 
+def _cpu_line(value, unit, cores, sample):
+    """The oracle as it stands, timed on the host beside a GPU leg."""
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
+
+
 def _time(fn, steps, warmup, stream):
     """Eager: K back-to-back calls from Python, after W warmup calls."""
     import torch
@@ -459,6 +464,14 @@ def main():
     dgot = dout.cpu()[drows[:, 0], drows[:, 2]].double().numpy()
     decode_err = float(np.abs(dgot - dref).max())
     del sets
+    dcpu = None
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        oracle.sdpa(dq, dk0, dv0, scale=dw.scale, causal=False, want_lse=False, threads=threads)
+        sec = time.perf_counter() - t0
+        dcpu = _cpu_line(round(dbytes / sec / 1e9, 3), "GB/s", threads,
+                         f"whole decode workload ({dw.batch * dw.head_q} rows x {dw.kv_len} keys) in {sec:.2f} s, fp64")
 
     # ------- the same decode over a paged cache: 64- and 16-key pages, shuffled -------
     from oracle import paged as opaged
@@ -486,8 +499,10 @@ def main():
         pgbs = pbytes / (pms * 1e-3) / 1e9
         pstep(0)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
         pref = opaged.decode_paged(dq.reshape(dw.batch, dw.head_q, dw.d_qk), kp0, vp0, page_table=table0,
                                    page_size=PS, seq_lens=None, scale=dw.scale)["out"]
+        psec = time.perf_counter() - t0
         paged_err = float(np.abs(dout.double().cpu().numpy() - pref).max())
         del psets, kp0, vp0
         paged_lines[PS] = {
@@ -498,6 +513,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(pgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
             "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
+            "cpu_baseline": _cpu_line(round(pbytes / psec / 1e9, 3), "GB/s", torch.get_num_threads(),
+                                      f"whole workload through the paged oracle in {psec:.2f} s, fp64"),
         }
 
     # ---------------- other prefill workloads (context lines) ----------------
@@ -542,7 +559,9 @@ def main():
     cms = _graph_time(cstep, cn, args.warmup)
     cstep(0)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     cref = ocached.prefill_cached(cq, ckc, cvc, ck, cv, cache_len=CACHED_LEN, scale=cw.scale, causal=True)["out"]
+    csec = time.perf_counter() - t0
     cerr = float(np.abs(co.double().cpu().numpy() - cref).max())
     ct = cw.flops() / (cms * 1e-3) / 1e12
     cached_line = {"workload": f"{cw.q_len}-query chunk over {CACHED_LEN} cached keys, Hq {cw.head_q} / Hkv "
@@ -551,7 +570,10 @@ def main():
                    "eager_ms_per_call": round(ceager, 6), "steps": cn,
                    "algorithmic_gflop": round(cw.flops() / 1e9, 4), "peak": PEAK_BF16_TFLOPS,
                    "frac_of_peak": round(ct / PEAK_BF16_TFLOPS, 5),
-                   "parity": {"max_abs_err": cerr}}
+                   "parity": {"max_abs_err": cerr},
+                   "cpu_baseline": _cpu_line(round(cw.flops() / csec / 1e12, 6), "TFLOP/s", torch.get_num_threads(),
+                                             f"whole chunk through the cached-prefill oracle in {csec:.2f} s, "
+                                             f"fp64")}
     del cqd, ckcd, cvcd, ckd, cvd
 
     # ------- boolean -> additive mask conversion, 4 rotating buffer sets -------
@@ -574,6 +596,10 @@ def main():
     mgbs = mbytes / (mms * 1e-3) / 1e9
     mstep(0)
     torch.cuda.synchronize()
+    msample = msets[0][0][0].cpu().numpy().astype(np.uint8)
+    t0 = time.perf_counter()
+    omask.mask_convert(msample, "bf16")
+    msec = time.perf_counter() - t0
     mrows = slice(0, 64)
     mref = omask.mask_convert(msets[0][0][0, mrows].cpu().numpy().astype(np.uint8), "bf16")
     mexact = bool(np.array_equal(msets[0][1][0, mrows].view(torch.int16).cpu().numpy().view(np.uint16), mref))
@@ -583,7 +609,10 @@ def main():
                  "roofline": {"bound": "hbm", "achieved": round(mgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(mgbs / PEAK_HBM_GBS, 5),
                               "traffic": _traffic("mask_convert_16x4096x4096_counters.txt", _SOURCES["mask"])},
-                 "parity": {"bit_exact_rows": 64, "exact": mexact}}
+                 "parity": {"bit_exact_rows": 64, "exact": mexact},
+                 "cpu_baseline": _cpu_line(round(3 * msample.size / msec / 1e9, 3), "GB/s", 1,
+                                           f"one [{MASK_SHAPE[1]}, {MASK_SHAPE[2]}] slice ({msample.size} elements) "
+                                           f"through the numpy oracle in {msec:.2f} s")}
     del msets
 
     # ------- prefill with a full additive mask (per-head bias) -------
@@ -609,8 +638,11 @@ def main():
     xmstep(0)
     torch.cuda.synchronize()
     G = xw.head_q // xw.head_kv
-    mref = omask2.prefill_masked(mq[:, :, :G], mk[:, :, :1], mv[:, :, :1], mbias[:, :G].cpu(), scale=xw.scale,
+    mb_cpu = mbias[:, :G].cpu()
+    t0 = time.perf_counter()
+    mref = omask2.prefill_masked(mq[:, :, :G], mk[:, :, :1], mv[:, :, :1], mb_cpu, scale=xw.scale,
                                  causal=False)["out"]
+    xsec = time.perf_counter() - t0
     merr = float(np.abs(mo[:, :, :G].double().cpu().numpy() - mref).max())
     xt = xw.flops() / (xmms * 1e-3) / 1e12
     masked_line = {"workload": f"{xw.q_len} x {xw.kv_len}, Hq {xw.head_q} / Hkv {xw.head_kv}, d {xw.d_qk}, bf16, "
@@ -618,7 +650,11 @@ def main():
                    "value": round(xt, 3), "unit": "TFLOP/s", "ms_per_call": round(xmms, 6), "steps": xn,
                    "algorithmic_gflop": round(xw.flops() / 1e9, 4), "peak": PEAK_BF16_TFLOPS,
                    "frac_of_peak": round(xt / PEAK_BF16_TFLOPS, 5),
-                   "mask_bytes": int(mbias.numel() * 2), "parity": {"max_abs_err": merr, "heads_checked": G}}
+                   "mask_bytes": int(mbias.numel() * 2), "parity": {"max_abs_err": merr, "heads_checked": G},
+                   "cpu_baseline": _cpu_line(round(xw.flops() * G / xw.head_q / xsec / 1e12, 6), "TFLOP/s",
+                                             torch.get_num_threads(),
+                                             f"{G} of {xw.head_q} heads (one GQA group) through the masked "
+                                             f"oracle in {xsec:.2f} s, fp64")}
     del mqd, mkd, mvd, mbias, mo
 
     # launch floor: a one-element device op, eager and replayed from a graph
@@ -669,6 +705,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dgbs / PEAK_HBM_GBS, 5), "traffic": dtraffic},
             "parity": {"max_abs_err": decode_err},
+            "cpu_baseline": dcpu,
         },
         "decode_paged": paged_lines[64],
         "decode_paged_16": paged_lines[16],
