@@ -70,3 +70,45 @@ def test_decode_graph_replay(dev):
     ws = sdpa.decode_workspace(qd, kd, vd)
     _say("decode graph: B16 32/8 heads kv 1500")
     _replays_match(dev, lambda i: sdpa.decode(qd, kd, vd, scale=w.scale, out=out, workspace=ws), out, 2)
+
+
+def test_paged_decode_graph_replay(dev):
+    d = inputs.WORKLOADS["splitkv_decode_bf16"]
+    q, k, v, _ = inputs.make_qkv(d, kv_len=900)
+    qd = q.reshape(d.batch, d.head_q, d.d_qk).to(dev)
+    kp, vp, table = inputs.paginate(k, v, 16, seed=3, spare_pages=4)
+    lens = inputs.length_mix(d.batch, 900, seed=4).to(dev)
+    kpd, vpd, td = kp.to(dev), vp.to(dev), table.to(dev)
+    out = torch.empty(d.batch, d.head_q, d.d_v, dtype=torch.bfloat16, device=dev)
+    ws = sdpa.decode_workspace(qd, kpd, vpd, kv_len=900)
+    _say("paged decode graph: 16-key pages, mixed lengths")
+    _replays_match(dev, lambda i: sdpa.decode_paged(qd, kpd, vpd, page_table=td, seq_lens=lens, kv_len=900,
+                                                    out=out, workspace=ws), out, 2)
+
+
+def test_cached_prefill_graph_replay(dev):
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    q, k, v, _ = inputs.make_qkv(w, q_len=128, kv_len=400)
+    qd = q.to(dev)
+    kc, vc = k[:, :272].contiguous().to(dev), v[:, :272].contiguous().to(dev)
+    kn, vn = k[:, 272:].contiguous().to(dev), v[:, 272:].contiguous().to(dev)
+    out = torch.empty(w.batch, 128, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
+    _say("cached prefill graph: 128 queries over 272 cached keys")
+    _replays_match(dev, lambda i: sdpa.prefill_cached(qd, kc, vc, kn, vn, cache_len=272, causal=True, out=out),
+                   out, 2)
+
+
+def test_mask_convert_and_masked_prefill_graph_replay(dev):
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    q, k, v, _ = inputs.make_qkv(w, q_len=96, kv_len=160)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    keep = (torch.rand(1, 1, 96, 160, generator=torch.Generator().manual_seed(5)) < 0.7).to(dev)
+    add = torch.empty(1, 1, 96, 160, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(w.batch, 96, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        sdpa.mask_convert(keep, out=add)
+        sdpa.prefill_masked(qd, kd, vd, add, out=out)
+
+    _say("mask conversion + masked prefill graph")
+    _replays_match(dev, call, out, 2)
