@@ -267,8 +267,9 @@ sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void*
     return SDPA_ERR_UNSUPPORTED;
   }
   const int64_t min_row = p.kv_len > 8 ? p.kv_len : 8;
-  if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_row < min_row || mask_stride_row % 8 != 0 ||
-      mask_stride_b % 8 != 0 || mask_stride_h % 8 != 0) {
+  if (p.kv_len > 0 &&  // without keys the mask is never read
+      (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_row < min_row || mask_stride_row % 8 != 0 ||
+       mask_stride_b % 8 != 0 || mask_stride_h % 8 != 0)) {
     set_error("mask strides must be >= 0 and multiples of 8 elements, the row stride >= max(kv_len, 8) "
               "(b=%lld h=%lld row=%d kv_len=%d)", (long long)mask_stride_b, (long long)mask_stride_h,
               mask_stride_row, p.kv_len);

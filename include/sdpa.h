@@ -234,7 +234,9 @@ sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32
  *       b*mask_stride_b + h*mask_stride_h + i*mask_stride_row + j.  A stride
  *       of 0 broadcasts over batch or heads.  All strides are multiples of 8
  *       elements and mask_stride_row >= max(kv_len, 8): rows may be padded,
- *       and the padding is read but never used.
+ *       and the padding is read but never used.  With kv_len == 0 the mask
+ *       is not read (its pointer and strides are not checked); O = 0 and
+ *       lse = -inf.
  * No workspace; errors as for sdpa_prefill_fwd. */
 sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void* q, const void* k,
                                       const void* v, const void* mask, int64_t mask_stride_b,

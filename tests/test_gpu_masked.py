@@ -141,3 +141,14 @@ def test_masked_prefill_rejects_bad_strides(dev):
     with pytest.raises(sdpa.SdpaError) as ei:
         sdpa.prefill_masked(q, k, k, m)
     assert ei.value.status == 2
+
+
+def test_masked_prefill_without_keys(dev):
+    q = torch.randn(1, 20, 4, 64).to(torch.bfloat16).to(dev)
+    k = torch.empty(1, 0, 2, 64, dtype=torch.bfloat16, device=dev)
+    m = torch.empty(1, 1, 20, 0, dtype=torch.bfloat16, device=dev)
+    out = torch.full((1, 20, 4, 64), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(1, 4, 20, device=dev)
+    sdpa.prefill_masked(q, k, k, m, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
