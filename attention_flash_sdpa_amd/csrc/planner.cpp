@@ -157,14 +157,12 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     bool occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
     if (variant == 3 || variant == 4) occ2 = false;
     if (variant == 5) occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192;
-    if (cached) occ2 = false;
     if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
     // Four key ranges of 32-key blocks, two waves (heads or query tiles) per
     // range, 8 waves per workgroup at two waves per SIMD: the same grid as the
     // two-range split with twice the waves in flight.
     bool split4 = false;
     if (variant == 6) split4 = rows == kRowsPerWave && kid != kPrefillFp8D192;
-    if (cached) split4 = false;
     if (split4) {
       ks = kSplitRanges;
       groups = shape(kSplitWaves / kSplitRanges, &hp, &qtiles);

@@ -1,10 +1,12 @@
 // prefill_cached.hip -- cached-KV (chunked) prefill instantiations of the
-// one-wave prefill kernel (prefill_kernel.h with CACHED = true): the chunk's
+// one-wave and the two-waves-per-SIMD prefill kernels (prefill_kernel.h and
+// prefill_o2_kernel.h with CACHED = true): the chunk's
 // queries over a cached prefix followed by the chunk's own keys, the mode
 // "Xe SDPA Forward Mainloop" runs with kblocks_cache > 0 (sections "Startup
 // prefetch + init" and "Outer K-block loop").  Compiled apart from
 // prefill.hip only so that the two sets of instantiations build in parallel.
 #include "prefill_kernel.h"
+#include "prefill_o2_kernel.h"
 
 namespace sdpa {
 
@@ -24,13 +26,32 @@ static int launch_cached_one(const PrefillArgs& a, const sdpa_plan_t& plan, int 
                               : launch_cached_ks<T, D, 1>(a, causal, stream);
 }
 
+template <class T, int D, int NW, int KS, int BK>
+static int launch_cached_o2(const PrefillArgs& a, int causal, ihipStream_t* stream) {
+  dim3 grid(a.num_groups), block(64 * NW);
+  if (causal)
+    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, true, NW, KS, BK, true>), grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, false, NW, KS, BK, true>), grid, block, 0, (hipStream_t)stream,
+                       a);
+  return (int)hipGetLastError();
+}
+
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
   switch (plan.kernel) {
+    case kOccF16D64: return launch_cached_o2<F16, 64, 4, 1, 64>(a, causal, stream);
+    case kOccBf16D64: return launch_cached_o2<Bf16, 64, 4, 1, 64>(a, causal, stream);
+    case kOccF16D128: return launch_cached_o2<F16, 128, 4, 1, 64>(a, causal, stream);
+    case kOccBf16D128: return launch_cached_o2<Bf16, 128, 4, 1, 64>(a, causal, stream);
+    case kSplitF16D64: return launch_cached_o2<F16, 64, 8, 4, 32>(a, causal, stream);
+    case kSplitBf16D64: return launch_cached_o2<Bf16, 64, 8, 4, 32>(a, causal, stream);
+    case kSplitF16D128: return launch_cached_o2<F16, 128, 8, 4, 32>(a, causal, stream);
+    case kSplitBf16D128: return launch_cached_o2<Bf16, 128, 8, 4, 32>(a, causal, stream);
     case kPrefillF16D64: return launch_cached_one<F16, 64>(a, plan, causal, stream);
     case kPrefillBf16D64: return launch_cached_one<Bf16, 64>(a, plan, causal, stream);
     case kPrefillF16D128: return launch_cached_one<F16, 128>(a, plan, causal, stream);
     case kPrefillBf16D128: return launch_cached_one<Bf16, 128>(a, plan, causal, stream);
-    default: return (int)hipErrorInvalidValue;  // the planner picks no other kernel for a cached prefill
+    default: return (int)hipErrorInvalidValue;  // no wide or fp8 form reads a cache
   }
 }
 

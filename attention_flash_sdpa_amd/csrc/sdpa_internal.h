@@ -61,7 +61,7 @@ constexpr int kDefaultCUs = 256;
 // kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
 // 32-row kernel, 6 = its 8-wave, four-key-range form (tuning sweeps and tests
 // only).  cached: a cached-KV prefill (kv_len counts cache and new keys),
-// which only the one-wave 32-row kernel implements.
+// which the 32-row kernels implement (not the wide or the fp8 one).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan, int variant = 0, bool cached = false);
 

@@ -154,8 +154,8 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
 
 
 # kernel-source files whose text decides each profiled kernel's code
-_SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_wide.hip", "sdpa_device.h",
-                        "sdpa_internal.h", "sdpa_bounds.h"],
+_SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_o2_kernel.h", "prefill_wide.hip",
+                        "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
             "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"],
             "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"]}
 def _cached_chunk():
