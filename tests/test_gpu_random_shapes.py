@@ -1,0 +1,136 @@
+"""Seeded random shapes for the paged / variable-length decode, the cached
+prefill and the masked prefill, each against its fp64 oracle (the bar of the
+dedicated tests: no NaN, max |gpu - oracle| <= 2e-2).  The shapes are drawn
+once from a fixed seed, so every run checks the same cases."""
+import math
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_flash_sdpa_amd as sdpa
+from attention_flash_sdpa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL16 = 2e-2
+_R = random.Random(20261202)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    sdpa.load()
+    return torch.device("cuda:0")
+
+
+def _heads():
+    hkv = _R.choice([1, 2, 4, 8])
+    return hkv * _R.choice([1, 2, 3, 4, 8, 16]), hkv
+
+
+def _check(out, want):
+    got = out.double().cpu().numpy()
+    nan = int(np.isnan(got).sum())
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    _say(f"  nan={nan} max_abs={err:.3e}")
+    assert nan == 0 and err <= TOL16, (nan, err)
+
+
+PAGED = []
+for _ in range(12):
+    hq, hkv = _heads()
+    PAGED.append((_R.randint(1, 6), _R.randint(1, 3000), hq, hkv, _R.choice([64, 128]),
+                  _R.choice([torch.bfloat16, torch.float16]), _R.choice([8, 16, 32, 64, 96, 128, 256]),
+                  _R.choice([0, 0, 1, 3, 7, 20]), _R.random() < 0.7))
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[f"p{i}" for i in range(len(PAGED))])
+def test_random_paged_decode(dev, case):
+    from oracle import paged as op
+
+    B, Sk, Hq, Hkv, D, dt, ps, splits, varlen = case
+    _say(f"random paged decode B={B} kv_len={Sk} Hq={Hq} Hkv={Hkv} D={D} {dt} page={ps} splits={splits} "
+         f"varlen={varlen}")
+    g = torch.Generator().manual_seed(Sk * 7 + B)
+    q = torch.randn(B, Hq, D, generator=g).to(dt)
+    k = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    v = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    kp, vp, table = inputs.paginate(k, v, ps, seed=Sk + 1, spare_pages=_R.randint(0, 3))
+    lens = inputs.length_mix(B, Sk, seed=Sk + 2) if varlen else None
+    out = sdpa.decode_paged(q.to(dev), kp.to(dev), vp.to(dev), page_table=table.to(dev),
+                            seq_lens=None if lens is None else lens.to(dev), kv_len=Sk, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = op.decode_paged(q, kp, vp, page_table=table, page_size=ps, seq_lens=None if lens is None else lens.tolist(),
+                          scale=1 / math.sqrt(D), kv_len=Sk)
+    _check(out, ref["out"])
+
+
+CACHED = []
+for _ in range(10):
+    hq, hkv = _heads()
+    new = _R.randint(1, 700)
+    causal = _R.random() < 0.7
+    sq = _R.randint(1, new) if causal else _R.randint(1, 700)
+    sc = _R.randint(0, 1500)
+    CACHED.append((_R.randint(1, 2), sq, sc, sc + _R.choice([0, 0, 16, 100]), new, hq, hkv, _R.choice([64, 128]),
+                   _R.choice([torch.bfloat16, torch.float16]), causal))
+
+
+@pytest.mark.parametrize("case", CACHED, ids=[f"c{i}" for i in range(len(CACHED))])
+def test_random_cached_prefill(dev, case):
+    from oracle import cached as oc
+
+    B, Sq, Sc, cap, Sk, Hq, Hkv, D, dt, causal = case
+    _say(f"random cached prefill B={B} q={Sq} cache={Sc}/{cap} new={Sk} Hq={Hq} Hkv={Hkv} D={D} {dt} causal={causal}")
+    g = torch.Generator().manual_seed(Sq + 3 * Sc + Sk)
+    q = torch.randn(B, Sq, Hq, D, generator=g).to(dt)
+    kc = torch.randn(B, cap, Hkv, D, generator=g).to(dt)
+    vc = torch.randn(B, cap, Hkv, D, generator=g).to(dt)
+    kc[:, Sc:] = float("nan")
+    vc[:, Sc:] = float("nan")
+    k = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    v = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    out = sdpa.prefill_cached(*(t.to(dev) for t in (q, kc, vc, k, v)), cache_len=Sc, causal=causal)
+    torch.cuda.synchronize()
+    ref = oc.prefill_cached(q, kc, vc, k, v, cache_len=Sc, scale=1 / math.sqrt(D), causal=causal)
+    _check(out, ref["out"])
+
+
+MASKED = []
+for _ in range(10):
+    hq, hkv = _heads()
+    MASKED.append((_R.randint(1, 2), _R.randint(1, 400), _R.randint(1, 600), hq, hkv, _R.choice([64, 128]),
+                   _R.choice([torch.bfloat16, torch.float16]), _R.random() < 0.4, _R.random() < 0.5,
+                   _R.random() < 0.5))
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[f"m{i}" for i in range(len(MASKED))])
+def test_random_masked_prefill(dev, case):
+    from oracle import mask as om
+
+    B, Sq, Sk, Hq, Hkv, D, dt, causal, per_head, per_batch = case
+    _say(f"random masked prefill B={B} q={Sq} k={Sk} Hq={Hq} Hkv={Hkv} D={D} {dt} causal={causal} "
+         f"per_head={per_head} per_batch={per_batch}")
+    g = torch.Generator().manual_seed(Sq * 5 + Sk)
+    q = torch.randn(B, Sq, Hq, D, generator=g).to(dt)
+    k = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    v = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    mb, mh = (B if per_batch else 1), (Hq if per_head else 1)
+    m = torch.randn(mb, mh, Sq, Sk, generator=g) * 2
+    m[torch.rand(mb, mh, Sq, Sk, generator=g) < 0.2] = float("-inf")
+    m = m.to(dt)
+    W = max(8, -(-Sk // 8) * 8)
+    buf = torch.full((mb, mh, Sq, W), float("nan"), dtype=dt)
+    buf[..., :Sk] = m
+    out = sdpa.prefill_masked(q.to(dev), k.to(dev), v.to(dev), buf.to(dev)[..., :Sk], causal=causal)
+    torch.cuda.synchronize()
+    ref = om.prefill_masked(q, k, v, m, scale=1 / math.sqrt(D), causal=causal)
+    _check(out, ref["out"])
