@@ -26,7 +26,8 @@ from .binding import (  # noqa: F401
     prefill,
     prefill_cached,
     prefill_masked,
+    set_prefill_variant,
 )
 
 __all__ = ["prefill", "prefill_cached", "prefill_masked", "decode", "decode_paged", "decode_workspace", "mask_convert", "plan",
-           "loop_counts", "make_problem", "load", "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]
+           "loop_counts", "set_prefill_variant", "make_problem", "load", "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]

@@ -25,7 +25,7 @@ EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
     "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_prefill_masked_fwd",
-    "sdpa_loop_counts",
+    "sdpa_loop_counts", "sdpa_set_prefill_variant",
 )
 
 
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_plan.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Plan)]
     lib.sdpa_loop_counts.restype = ctypes.c_int
     lib.sdpa_loop_counts.argtypes = [ctypes.c_int] * 9 + [ctypes.POINTER(LoopCounts)]
+    lib.sdpa_set_prefill_variant.restype = ctypes.c_int
+    lib.sdpa_set_prefill_variant.argtypes = [ctypes.c_char_p]
     lib.sdpa_prefill_workspace_bytes.restype = sz
     lib.sdpa_prefill_workspace_bytes.argtypes = [P]
     lib.sdpa_decode_workspace_bytes.restype = sz
@@ -141,6 +143,13 @@ def loop_counts(*, q_len, kv_len, d_qk, d_v, block_q, block_k, block_d, block_v,
     return out
 
 
+def set_prefill_variant(name: str | None) -> None:
+    """Forces one form of the 16-bit prefill kernels ("narrow1", "narrow2",
+    "occ2", "split4") for later calls in this process; None or "" restores the
+    planner's choice.  For tuning sweeps and tests."""
+    _check(load().sdpa_set_prefill_variant((name or "").encode()))
+
+
 def _stream_handle(stream):
     import torch
 
@@ -152,6 +161,46 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_inputs(names, tensors, *, same_dtype=True):
+    """Every input is a contiguous tensor on one device, with one dtype."""
+    dev = tensors[0].device
+    for n, t in zip(names, tensors):
+        _require(t.is_cuda and t.is_contiguous(), f"{n} must be a contiguous device tensor")
+        _require(t.device == dev, f"{n} is on {t.device}, {names[0]} on {dev}")
+        if same_dtype:
+            _require(t.dtype == tensors[0].dtype, f"{n} has dtype {t.dtype}, {names[0]} {tensors[0].dtype}")
+
+
+def _check_output(name, t, shape, dtypes, device):
+    """A caller's output buffer: exact shape, an accepted dtype, contiguous, on
+    the inputs' device (the kernels write every element of that shape)."""
+    if t is None:
+        return
+    _require(tuple(t.shape) == tuple(shape), f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    _require(t.dtype in dtypes, f"{name} must have dtype in {[str(d) for d in dtypes]}, got {t.dtype}")
+    _require(t.is_cuda and t.is_contiguous() and t.device == device,
+             f"{name} must be a contiguous tensor on {device}")
+
+
+def _check_prefill_shapes(q, k, v):
+    """q [B, Sq, Hq, D], k [B, Sk, Hkv, D], v [B, Sk, Hkv, Dv]."""
+    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
+    _require(k.shape[0] == q.shape[0] and v.shape[0] == q.shape[0], "q, k, v must have the same batch")
+    _require(k.shape[-1] == q.shape[-1], f"k head dim {k.shape[-1]} != q head dim {q.shape[-1]}")
+    _require(v.shape[:3] == k.shape[:3], f"v {tuple(v.shape)} does not match k {tuple(k.shape)} in [B, Sk, Hkv]")
+
+
+def _out_dtypes(q):
+    import torch
+
+    return (torch.bfloat16, torch.float16) if q.dtype == torch.float8_e4m3fn else (q.dtype,)
+
+
 def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1.0, 1.0, 1.0), out_dtype=None,
             stream=None):
     """O = softmax(Q K^T * scale + mask) V on the GPU.
@@ -161,14 +210,15 @@ def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1
     optional fp32 [B, Hq, Sq] tensor to receive the log-sum-exp."""
     import torch
 
+    _check_inputs(("q", "k", "v"), (q, k, v))
+    _check_prefill_shapes(q, k, v)
     B, Sq, Hq, D = q.shape
     _, Sk, Hkv, _ = k.shape
     Dv = v.shape[-1]
-    for t in (q, k, v):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("q, k, v must be contiguous device tensors")
     if out_dtype is None:
         out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    _check_output("out", out, (B, Sq, Hq, Dv), _out_dtypes(q), q.device)
+    _check_output("lse", lse, (B, Hq, Sq), (torch.float32,), q.device)
     if out is None:
         out = torch.empty(B, Sq, Hq, Dv, dtype=out_dtype, device=q.device)
     if scale is None:
@@ -193,18 +243,20 @@ def prefill_cached(q, k_cache, v_cache, k, v, *, cache_len, scale=None, causal=F
     (bottom-right, Sq <= Sk).  Returns O [B, Sq, Hq, Dv]."""
     import torch
 
+    _check_inputs(("q", "k_cache", "v_cache", "k", "v"), (q, k_cache, v_cache, k, v))
+    _check_prefill_shapes(q, k, v)
+    _require(k_cache.dim() == 4 and v_cache.dim() == 4, "k_cache, v_cache must be 4-D")
     B, Sq, Hq, D = q.shape
     _, Sk, Hkv, _ = k.shape
     Dv = v.shape[-1]
-    for t in (q, k, v, k_cache, v_cache):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("q, k, v, k_cache, v_cache must be contiguous device tensors")
     if k_cache.shape[0] != B or k_cache.shape[2:] != k.shape[2:] or v_cache.shape[:3] != k_cache.shape[:3] \
             or v_cache.shape[-1] != Dv or v.shape[:3] != k.shape[:3] or k.shape[0] != B or k.shape[-1] != D:
         raise ValueError(f"shapes disagree: q {tuple(q.shape)}, k_cache {tuple(k_cache.shape)}, "
                          f"v_cache {tuple(v_cache.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not 0 <= cache_len <= k_cache.shape[1]:
         raise ValueError(f"cache_len {cache_len} outside [0, {k_cache.shape[1]}]")
+    _check_output("out", out, (B, Sq, Hq, Dv), (q.dtype,), q.device)
+    _check_output("lse", lse, (B, Hq, Sq), (torch.float32,), q.device)
     if out is None:
         out = torch.empty(B, Sq, Hq, Dv, dtype=q.dtype, device=q.device)
     if scale is None:
@@ -262,12 +314,12 @@ def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=N
     returns O [B, Hq, Dv].  ``lse`` is an optional fp32 [B, Hq] tensor."""
     import torch
 
+    _check_inputs(("q", "k", "v"), (q, k, v))
+    _check_caches(q, k, v, dense=True)
     B, Hq, D = q.shape
     Dv = v.shape[-1]
-    for t in (q, k, v):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("q, k, v must be contiguous device tensors")
-    _check_caches(q, k, v, dense=True)
+    _check_output("out", out, (B, Hq, Dv), (q.dtype,), q.device)
+    _check_output("lse", lse, (B, Hq), (torch.float32,), q.device)
     if out is None:
         out = torch.empty(B, Hq, Dv, dtype=q.dtype, device=q.device)
     if scale is None:
@@ -276,6 +328,7 @@ def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=N
     lib = load()
     if workspace is None:
         workspace = decode_workspace(q, k, v, num_splits=num_splits, descale=descale)
+    _require(workspace.tensor.device == q.device, "workspace must be on q's device")
     _check(lib.sdpa_decode_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(num_splits),
                                _ptr(workspace.tensor), workspace.nbytes, _stream_handle(stream)))
     return out
@@ -292,11 +345,12 @@ def decode_paged(q, k_cache, v_cache, *, page_table=None, seq_lens=None, kv_len=
     [B] on the device, or None) gives each sequence's key count."""
     import torch
 
+    _check_inputs(("q", "k_cache", "v_cache"), (q, k_cache, v_cache))
     B, Hq, D = q.shape
     Dv = v_cache.shape[-1]
-    for t in (q, k_cache, v_cache, page_table, seq_lens):
-        if t is not None and (not t.is_contiguous() or not t.is_cuda):
-            raise ValueError("q, caches, page_table and seq_lens must be contiguous device tensors")
+    for t in (page_table, seq_lens):
+        if t is not None and (not t.is_contiguous() or not t.is_cuda or t.device != q.device):
+            raise ValueError("page_table and seq_lens must be contiguous tensors on q's device")
     for t in (page_table, seq_lens):
         if t is not None and t.dtype != torch.int32:
             raise TypeError("page_table and seq_lens must be int32")
@@ -315,6 +369,8 @@ def decode_paged(q, k_cache, v_cache, *, page_table=None, seq_lens=None, kv_len=
             raise ValueError(f"kv_len {kv_len} exceeds the dense cache's {k_cache.shape[1]} keys")
     if seq_lens is not None and seq_lens.shape != (B,):
         raise ValueError("seq_lens must be [B]")
+    _check_output("out", out, (B, Hq, Dv), (q.dtype,), q.device)
+    _check_output("lse", lse, (B, Hq), (torch.float32,), q.device)
     if out is None:
         out = torch.empty(B, Hq, Dv, dtype=q.dtype, device=q.device)
     if scale is None:
@@ -323,6 +379,7 @@ def decode_paged(q, k_cache, v_cache, *, page_table=None, seq_lens=None, kv_len=
     lib = load()
     if workspace is None:
         workspace = decode_workspace(q, k_cache, v_cache, num_splits=num_splits, descale=descale, kv_len=kv_len)
+    _require(workspace.tensor.device == q.device, "workspace must be on q's device")
     _check(lib.sdpa_decode_paged_fwd(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                      _ptr(page_table), num_pages, page_size, pages_per_seq, _ptr(out), _ptr(lse),
                                      int(num_splits), _ptr(workspace.tensor), workspace.nbytes,
@@ -340,8 +397,7 @@ def mask_convert(mask, *, out_dtype=None, out=None, stream=None):
         raise ValueError("mask must be a contiguous bool or uint8 device tensor")
     if out is None:
         out = torch.empty(mask.shape, dtype=out_dtype or torch.bfloat16, device=mask.device)
-    if out.shape != mask.shape or not out.is_contiguous():
-        raise ValueError("out must be contiguous and shaped like mask")
+    _check_output("out", out, tuple(mask.shape), (torch.float16, torch.bfloat16), mask.device)
     _check(load().sdpa_mask_convert(_ptr(mask), _ptr(out), mask.numel(), _dtype_code(out), _stream_handle(stream)))
     return out
 
@@ -356,17 +412,19 @@ def prefill_masked(q, k, v, mask, *, scale=None, causal=False, out=None, lse=Non
     slice them to Sk: ``mask[..., :Sk]`` of a padded tensor qualifies)."""
     import torch
 
+    _check_inputs(("q", "k", "v"), (q, k, v))
+    _check_prefill_shapes(q, k, v)
     B, Sq, Hq, D = q.shape
     _, Sk, Hkv, _ = k.shape
-    for t in (q, k, v):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("q, k, v must be contiguous device tensors")
+    _require(mask.device == q.device, f"mask is on {mask.device}, q on {q.device}")
     if mask.dim() != 4 or mask.dtype != q.dtype or not mask.is_cuda or mask.stride(-1) != 1:
         raise ValueError("mask must be a 4-D device tensor of q's dtype with a contiguous last dim")
     if mask.shape[0] not in (1, B) or mask.shape[1] not in (1, Hq) or mask.shape[2] != Sq or mask.shape[3] < Sk:
         raise ValueError(f"mask shape {tuple(mask.shape)} does not cover [{B}, {Hq}, {Sq}, {Sk}]")
     sb = 0 if mask.shape[0] == 1 else mask.stride(0)
     sh = 0 if mask.shape[1] == 1 else mask.stride(1)
+    _check_output("out", out, (B, Sq, Hq, v.shape[-1]), (q.dtype,), q.device)
+    _check_output("lse", lse, (B, Hq, Sq), (torch.float32,), q.device)
     if out is None:
         out = torch.empty(B, Sq, Hq, v.shape[-1], dtype=q.dtype, device=q.device)
     if scale is None:

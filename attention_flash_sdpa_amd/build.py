@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsdpa_mi355x.so")
-SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_cached.hip", "prefill_o2.hip", "prefill_wide.hip",
+SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_cached.hip", "prefill_o2.hip",
            "prefill_fp8.hip", "decode.hip", "mask.hip", "masked.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,11 +29,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
 
 
-# Per-source backend options.  The wide prefill kernel runs one wave per SIMD
-# with both register files: MFMA results stay in VGPRs (the softmax reads the
-# scores with VALU instructions), AGPRs take what does not fit.
-EXTRA = {"prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+# Per-source backend options.  The one-wave-per-SIMD prefill kernels use both
+# register files: MFMA results stay in VGPRs (the softmax reads the scores with
+# VALU instructions), AGPRs take what does not fit.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "prefill_cached.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

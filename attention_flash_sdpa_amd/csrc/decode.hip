@@ -9,8 +9,11 @@
 // Phase 1 (decode_split_kernel): one wavefront per (batch, KV head, split);
 // a workgroup holds 4 adjacent KV heads of one split so that its loads of a
 // key are contiguous.  The G = head_q / head_kv query heads of the group are
-// the MFMA N dimension (16x16x32 MFMA, G <= 16), so every K/V byte is read
-// from HBM exactly once for all heads of the group.  K and V blocks of 32
+// the MFMA N dimension (16x16x32 MFMA), so every K/V byte is read from HBM
+// exactly once for all heads of the group ("xe2-sdp-kernels", section "GQA
+// layout", which puts no bound on the group size).  A group of more than 16
+// query heads takes one wave per 16-head tile, adjacent in the workgroup, so
+// the tiles' reads of the same keys meet in L2.  K and V blocks of 32
 // keys go HBM -> LDS with direct 16-byte loads (whole key rows per 16 lanes),
 // one block ahead, into two wave-private stages; K fragments come back with
 // ds_read_b128 and V^T fragments with ds_read_b64_tr_b16, both swizzled to
@@ -58,16 +61,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lds_w = (uint32_t)(uintptr_t)(SDPA_LDS char*)smem + wave * 2 * STAGE;
 
-  // workgroup = (batch, split, group of 4 adjacent KV heads); wave = KV head,
-  // so the workgroup's loads of one key cover 4 consecutive head rows
+  // workgroup = (batch, split, 4 adjacent wave tasks); a wave task is one KV
+  // head and one tile of up to 16 of its query heads (the MFMA N dimension):
+  // task t covers KV head t / gtiles, query heads 16 * (t % gtiles) .. +15 of
+  // its group.  Tiles of one KV head are adjacent, so a workgroup's loads of a
+  // key are contiguous (4 head rows) or repeat one row, served by L2.
   const int S = a.num_splits;
-  const int hgroups = (a.head_kv + kDecodeWaves - 1) / kDecodeWaves;
+  const int tasks = a.head_kv * a.gtiles;
+  const int hgroups = (tasks + kDecodeWaves - 1) / kDecodeWaves;
   const int hgi = blockIdx.x % hgroups;
   const int split = (blockIdx.x / hgroups) % S;
   const int b = blockIdx.x / (hgroups * S);
-  const int g = hgi * kDecodeWaves + wave;
-  if (g >= a.head_kv) return;  // no barriers in this kernel
-  const int G = a.group;
+  const int task = hgi * kDecodeWaves + wave;
+  if (task >= tasks) return;  // no barriers in this kernel
+  const int g = task / a.gtiles;
+  const int h0 = 16 * (task - g * a.gtiles);   // first query head of the tile within the group
+  const int G = min(a.group - h0, 16);          // query heads of this tile
   const int Sk = a.kv_len;
   // this sequence's keys: kv_len, or its own length clamped to [0, kv_len]
   const int seq_len = a.seq_lens == nullptr ? Sk : min(max(a.seq_lens[b], 0), Sk);
@@ -78,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int n16 = lane & 15;   // query head within the group (MFMA N index)
   const int gq = lane >> 4;    // lane group of 16
   const bool head_ok = n16 < G;
-  const int h = g * G + min(n16, G - 1);
+  const int h = g * a.group + h0 + min(n16, G - 1);
 
   // Q^T fragments (B operand of S^T = K Q^T): head n16, dims 32s + 8*gq .. +7
   u32x4_t qf[KS];

@@ -77,11 +77,18 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     return SDPA_ERR_BAD_SCALE;
   }
   const float ds[3] = {p.q_descale, p.k_descale, p.v_descale};
-  for (float d : ds)
+  for (float d : ds) {
     if (!isfinite(d) || d < 0.f) {
       set_error("descale factors must be finite and >= 0 (got %g)", (double)d);
       return SDPA_ERR_BAD_SCALE;
     }
+    // dequantisation factors belong to fp8 inputs only: a 16-bit tensor holds
+    // its values as they are, so any other factor would silently rescale them
+    if (p.in_dtype != SDPA_FP8_E4M3 && d != 1.f) {
+      set_error("descale factors must be 1 for fp16/bf16 inputs (got %g)", (double)d);
+      return SDPA_ERR_BAD_SCALE;
+    }
+  }
   const int64_t G = p.head_q / p.head_kv;
   // element offsets inside one batch entry are 32-bit in the kernels
   const int64_t lim = (int64_t)1 << 31;
@@ -99,28 +106,11 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
                 p.d_qk, p.d_v);
       return SDPA_ERR_UNSUPPORTED;
     }
-    // Wide kernel (64 query rows per wave, one wave per SIMD) when the grid
-    // still gives every CU about three waves; otherwise the 32-row kernel,
-    // which doubles the wave count for small problems.
-    int rows = kRowsPerWave;
-    if (kid != kPrefillFp8D192) {
-      const int64_t wide_waves = (int64_t)p.batch * p.head_q * ceil_div(p.q_len, kWideRowsPerWave);
-      // (the wide kernel is selectable for tuning; the 32-row kernel is the
-      // default until the wide one measures faster)
-      bool wide = false;
-      (void)wide_waves;
-      if (variant == 1 || variant == 3 || variant == 4 || variant == 5) wide = false;
-      if (variant == 2) wide = true;
-      if (cached) wide = false;
-      if (wide) {
-        rows = kWideRowsPerWave;
-        kid = kid - kPrefillF16D64 + kWideF16D64;
-      }
-    }
+    const int rows = kRowsPerWave;
     plan->kernel = kid;
     plan->waves_per_group = kPrefillWaves;
     plan->rows_per_wave = rows;
-    plan->block_k = rows == kWideRowsPerWave ? kWideBlockK : kPrefillBlockK;
+    plan->block_k = kPrefillBlockK;
     plan->stages = 2;
     plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);
     // Pack query heads of one GQA group into the workgroup when the group
@@ -145,24 +135,24 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // Too few workgroups to give every CU one: split the key range of each
     // workgroup in two halves, each streamed by half of its waves and merged
     // at the end, which doubles the workgroup count.
-    bool split = rows == kRowsPerWave && kid != kPrefillFp8D192 && groups < num_cus && plan->kv_blocks >= 2;
+    bool split = kid != kPrefillFp8D192 && groups < num_cus && plan->kv_blocks >= 2;
     if (variant == 3 || variant == 5) split = false;
-    if (variant == 4) split = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (variant == 4) split = kid != kPrefillFp8D192;
     if (split) {
       ks = 2;
       groups = shape(kPrefillWaves / 2, &hp, &qtiles);
     }
     // More workgroups than CUs: the two-waves-per-SIMD form keeps two of them
     // on every CU at once (the one-wave form would run in rounds).
-    bool occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
+    bool occ2 = kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
     if (variant == 3 || variant == 4) occ2 = false;
-    if (variant == 5) occ2 = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (variant == 5) occ2 = kid != kPrefillFp8D192;
     if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
     // Four key ranges of 32-key blocks, two waves (heads or query tiles) per
     // range, 8 waves per workgroup at two waves per SIMD: the same grid as the
     // two-range split with twice the waves in flight.
     bool split4 = false;
-    if (variant == 6) split4 = rows == kRowsPerWave && kid != kPrefillFp8D192;
+    if (variant == 6) split4 = kid != kPrefillFp8D192;
     if (split4) {
       ks = kSplitRanges;
       groups = shape(kSplitWaves / kSplitRanges, &hp, &qtiles);
@@ -198,10 +188,6 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
               p.d_v);
     return SDPA_ERR_UNSUPPORTED;
   }
-  if (G > kDecodeMaxGroup) {
-    set_error("decode supports at most %d query heads per KV head (got %lld)", kDecodeMaxGroup, (long long)G);
-    return SDPA_ERR_UNSUPPORTED;
-  }
   if (num_splits < 0 || num_splits > 4096) {
     set_error("num_splits must be in [0, 4096] (got %d)", num_splits);
     return SDPA_ERR_BAD_SHAPE;
@@ -216,7 +202,9 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
   plan->stages = 2;
   plan->q_tiles = 1;
   plan->kv_blocks = (int32_t)ceil_div(p.kv_len, kDecodeBlockK);
-  const int64_t pairs = (int64_t)p.batch * p.head_kv;
+  // one wave per (batch, KV head, tile of up to 16 query heads, split)
+  const int64_t gtiles = ceil_div(G, kDecodeMaxGroup);
+  const int64_t pairs = (int64_t)p.batch * p.head_kv * gtiles;
   int64_t S;
   if (num_splits > 0) {
     S = num_splits;
@@ -245,8 +233,8 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     set_error("grid too large (%lld waves)", (long long)waves);
     return SDPA_ERR_BAD_SHAPE;
   }
-  // one workgroup per (batch, split, 4 adjacent KV heads)
-  plan->num_groups = (int32_t)(p.batch * S * ceil_div(p.head_kv, kDecodeWaves));
+  // one workgroup per (batch, split, 4 adjacent (KV head, query-head tile) tasks)
+  plan->num_groups = (int32_t)(p.batch * S * ceil_div((int64_t)p.head_kv * gtiles, kDecodeWaves));
   plan->combine_groups = (int32_t)ceil_div((int64_t)p.batch * p.head_q, kCombineRows);
   plan->lds_bytes = (uint64_t)kDecodeWaves * 2 * kDecodeBlockK * (p.d_qk + p.d_v) * 2;
   const uint64_t po = (uint64_t)p.batch * p.head_q * S * p.d_v * 4;

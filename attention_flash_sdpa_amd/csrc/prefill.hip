@@ -59,10 +59,6 @@ int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ih
     case kPrefillF16D128: return launch_one<F16, 128>(a, plan, causal, stream);
     case kPrefillBf16D128: return launch_one<Bf16, 128>(a, plan, causal, stream);
     case kPrefillFp8D192: return launch_prefill_fp8(a, causal, stream);
-    case kWideF16D64:
-    case kWideBf16D64:
-    case kWideF16D128:
-    case kWideBf16D128: return launch_prefill_wide(a, plan, causal, stream);
     case kOccF16D64:
     case kOccBf16D64:
     case kOccF16D128:

@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "sdpa_internal.h"
 
 namespace sdpa {
@@ -33,18 +35,31 @@ int device_cus() {
   return cached[dev];
 }
 
-// SDPA_PREFILL_VARIANT=narrow|wide overrides the planner's prefill kernel
-// choice (for tuning sweeps); unset or anything else keeps the planner's.
-int prefill_variant() {
-  const char* e = getenv("SDPA_PREFILL_VARIANT");
-  if (e == nullptr) return 0;
-  if (!strcmp(e, "narrow")) return 1;
-  if (!strcmp(e, "wide")) return 2;
+// A forced form of the 16-bit prefill kernels (for tuning sweeps and tests):
+// narrow1 / narrow2 = one wave per SIMD with one / two key ranges, occ2 = two
+// waves per SIMD, split4 = its four-key-range form; "" or "auto" = the
+// planner's choice.  The environment variable SDPA_PREFILL_VARIANT sets the
+// initial value, read once per process; sdpa_set_prefill_variant changes it.
+int variant_code(const char* e) {
+  if (e == nullptr || !*e || !strcmp(e, "auto")) return 0;
   if (!strcmp(e, "narrow1")) return 3;
   if (!strcmp(e, "narrow2")) return 4;
   if (!strcmp(e, "occ2")) return 5;
   if (!strcmp(e, "split4")) return 6;
-  return 0;
+  return -1;
+}
+
+std::atomic<int> g_variant{-1};  // -1: the environment has not been read yet
+
+int prefill_variant() {
+  int v = g_variant.load(std::memory_order_relaxed);
+  if (v < 0) {
+    v = variant_code(getenv("SDPA_PREFILL_VARIANT"));
+    if (v < 0) v = 0;
+    int expected = -1;
+    if (!g_variant.compare_exchange_strong(expected, v)) v = expected;
+  }
+  return v;
 }
 
 sdpa_status_t hip_status(int err, const char* what) {
@@ -74,6 +89,17 @@ const char* sdpa_status_string(int status) {
 }
 
 const char* sdpa_last_error(void) { return last_error_text(); }
+
+sdpa_status_t sdpa_set_prefill_variant(const char* name) {
+  clear_error();
+  const int v = variant_code(name);
+  if (v < 0) {
+    set_error("unknown prefill variant \"%s\"", name);
+    return SDPA_ERR_UNSUPPORTED;
+  }
+  g_variant.store(v, std::memory_order_relaxed);
+  return SDPA_OK;
+}
 
 sdpa_status_t sdpa_plan(const sdpa_problem_t* problem, int is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan) {
@@ -355,6 +381,7 @@ static sdpa_status_t decode_common(const sdpa_problem_t* problem, const void* q,
   a.num_splits = plan.num_splits;
   a.blocks_per_split = plan.blocks_per_split;
   a.split_waves = plan.num_splits;
+  a.gtiles = (a.group + kDecodeMaxGroup - 1) / kDecodeMaxGroup;
   a.s2 = (float)((double)p.scale * 1.4426950408889634 * (double)p.q_descale * (double)p.k_descale);
   a.v_descale = p.v_descale;
   a.seq_lens = seq_lens;

@@ -2,6 +2,7 @@
 // planner and the kernel launchers.  Not part of the public ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/sdpa.h"
@@ -17,10 +18,6 @@ enum KernelId : int32_t {
   kPrefillF16D128 = 2,
   kPrefillBf16D128 = 3,
   kPrefillFp8D192 = 4,
-  kWideF16D64 = 8,
-  kWideBf16D64 = 9,
-  kWideF16D128 = 10,
-  kWideBf16D128 = 11,
   kOccF16D64 = 12,  // 32-row kernel, two waves per SIMD (large grids)
   kOccBf16D64 = 13,
   kOccF16D128 = 14,
@@ -36,8 +33,6 @@ enum KernelId : int32_t {
 };
 
 constexpr int kRowsPerWave = 32;   // prefill: query rows per wave (MFMA N)
-constexpr int kWideRowsPerWave = 64;  // wide prefill: two 32-row tiles per wave
-constexpr int kWideBlockK = 32;       // wide prefill: keys per K/V block
 constexpr int kPrefillWaves = 4;   // prefill: waves per workgroup
 constexpr int kPrefillBlockK = 64; // prefill: keys per K/V block
 constexpr int kSplitWaves = 8;     // 4-range prefill: waves per workgroup
@@ -46,7 +41,7 @@ constexpr int kSplitBlockK = 32;   // 4-range prefill: keys per K/V block
 constexpr int kDecodeBlockK = 32;  // decode: keys per K/V block
 constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per CU (gfx950)
 constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows per workgroup
-constexpr int kDecodeMaxGroup = 16;  // decode: query heads per KV head (MFMA N)
+constexpr int kDecodeMaxGroup = 16;  // decode: query heads per wave (MFMA N); larger groups take several waves
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
 constexpr int kMaskedWaves = 4;    // masked prefill: waves per workgroup
 constexpr int kMaskedRowTiles = 4; // masked prefill: 16-row tiles per wave
@@ -56,12 +51,11 @@ constexpr int kDefaultCUs = 256;
 
 // Validates the problem; fills *plan.  Writes a detail message through
 // set_error() on failure.  Pure host code.
-// variant: 0 = planner's choice, 1 = the 32-row kernels (planner picks the
-// form), 2 = the wide (64-row) kernel, 3 / 4 = the one-wave-per-SIMD 32-row
+// variant: 0 = planner's choice, 3 / 4 = the one-wave-per-SIMD 32-row
 // kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
 // 32-row kernel, 6 = its 8-wave, four-key-range form (tuning sweeps and tests
 // only).  cached: a cached-KV prefill (kv_len counts cache and new keys),
-// which the 32-row kernels implement (not the wide or the fp8 one).
+// which the 16-bit kernels implement (not the fp8 one).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan, int variant = 0, bool cached = false);
 
@@ -99,6 +93,7 @@ struct DecodeArgs {
   float* part_ml;   // [batch, head_q, splits, 2] = (max in log2 domain, sum)
   int32_t batch, kv_len, head_q, head_kv, group;
   int32_t num_splits, blocks_per_split, split_waves;
+  int32_t gtiles;   // tiles of up to 16 query heads per KV head (the MFMA N dimension)
   float s2;
   float v_descale;
   // variable-length and paged key/value caches (both NULL: every sequence
@@ -110,7 +105,6 @@ struct DecodeArgs {
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
-int launch_prefill_wide(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream);

@@ -4,6 +4,7 @@
     python bench.py --counters-pass              # short run for rocprofv3 --pmc
     python bench.py --summarize-trace DIR        # kernel-trace CSV -> profiles/
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
+    python bench.py --summarize-sq DIR           # SQ counter run -> profiles/
 
 One step = one call of the hot path on its workload:
   * headline: causal GQA bf16 prefill (batch 1, 32 query / 8 KV heads,
@@ -14,12 +15,14 @@ One step = one call of the hot path on its workload:
     cache cannot serve them -- achieved HBM GB/s over algorithmic bytes
     (Q + K + V read once, O written once).
 Inputs are resident in HBM before the timed region.  The calls go through the
-Python binding and the C ABI; a chunk of C = gcd(K, W) consecutive calls is
+Python binding and the C ABI; a chunk of C consecutive calls (the largest
+divisor of K that is a multiple of the input-rotation period, at most 200) is
 captured once into a HIP graph (the library allocates and synchronizes
-nothing, so its launches capture as they are).  W/C untimed replays, then K/C
-replays bracketed by HIP events on the stream the kernels run on; the prefill
-step is a single kernel, so its time per step is also that kernel's average
-launch duration.  The same K calls issued one by one from Python are timed too
+nothing, so its launches capture as they are).  At least one untimed replay
+(and at least W untimed calls), then K/C replays bracketed by HIP events on
+the stream the kernels run on.  The prefill step is a single kernel, so its
+time per step is that kernel's launch-to-launch period back to back, an upper
+bound of its average duration.  The same K calls issued one by one from Python are timed too
 ("eager", host-bound for small workloads).  Rank 0 prints ONE JSON line.
 """
 from __future__ import annotations
@@ -85,20 +88,31 @@ def _time(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps   # ms per call
 
 
+def _graph_chunk(steps, period, cap=200):
+    """Calls per captured graph: the largest divisor of `steps` that is a
+    multiple of `period` (rotating inputs keep their order) and at most `cap`
+    (`steps` itself is rounded up to a multiple of `period` first)."""
+    steps = -(-steps // period) * period
+    best = period
+    for c in range(period, min(steps, cap) + 1, period):
+        if steps % c == 0:
+            best = c
+    return steps, best
+
+
 def _graph_time(fn, steps, warmup, period=1):
-    """K calls as replays of one captured chunk of C calls (C = gcd(K, W), a
-    multiple of `period` so rotating inputs keep their order); W/C untimed
-    replays first.  Returns ms per call."""
+    """K calls as replays of one captured chunk of C calls (C divides K and is
+    a multiple of `period`); at least one untimed replay (and at least W
+    untimed calls) first, then K/C replays between HIP events on the launch
+    stream.  Returns ms per call."""
     import torch
 
-    c = math.gcd(steps, warmup) if warmup else steps
-    if c % period:
-        c = steps
+    steps, c = _graph_chunk(steps, period)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(c):
             fn(i)
-    for _ in range(warmup // c):
+    for _ in range(max(1, -(-warmup // c))):
         g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -109,7 +123,11 @@ def _graph_time(fn, steps, warmup, period=1):
         g.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / (steps // c * c)
+    return start.elapsed_time(end) / steps
+
+
+# timed calls of each secondary leg at least (independent of --steps)
+MIN_LEG_CALLS = 20
 
 
 def _cpu_model():
@@ -147,16 +165,16 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
         shape = "4, 1, 64" if p.kernel <= 15 else "8, 4, 32"   # waves, key ranges, keys per block
         return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {shape}>",
                  p.num_groups * p.waves_per_group * 64)]
-    if p.rows_per_wave == 64:
-        return [(f"prefill_wide_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}>", p.num_groups * p.waves_per_group * 64)]
     return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, {'true' if cached else 'false'}>",
              p.num_groups * p.waves_per_group * 64)]
 
 
 # kernel-source files whose text decides each profiled kernel's code
-_SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_o2_kernel.h", "prefill_wide.hip",
+_SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_o2_kernel.h",
                         "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
             "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"],
+            "fp8": ["prefill_fp8.hip", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
+            "masked": ["masked.hip", "sdpa_device.h", "sdpa_internal.h"],
             "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"]}
 def _cached_chunk():
     from attention_flash_sdpa_amd import inputs
@@ -224,7 +242,113 @@ def _counters_pass():
     for i in range(6):
         sdpa.mask_convert(msets[i % 2][0], out=msets[i % 2][1])
     torch.cuda.synchronize()
-    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20, mask conversion x6", flush=True)
+    del msets
+    # the other profiled prefills: 3 calls each
+    for name in ("unaligned_full_bf16", "mla_fp8_causal_prefill"):
+        xw = inputs.WORKLOADS[name]
+        xq, xk, xv, xds = inputs.make_qkv(xw)
+        xq, xk, xv = (t.to(dev) for t in (xq, xk, xv))
+        for _ in range(3):
+            sdpa.prefill(xq, xk, xv, scale=xw.scale, causal=xw.causal, descale=xds)
+        torch.cuda.synchronize()
+        del xq, xk, xv
+    cw = CACHED_CHUNK
+    g = torch.Generator().manual_seed(cw.seed)
+    new = cw.kv_len - CACHED_LEN
+    cq = torch.randn(1, cw.q_len, cw.head_q, cw.d_qk, generator=g).to(torch.bfloat16).to(dev)
+    ckc, cvc, ck, cv = (torch.randn(1, n, cw.head_kv, cw.d_qk, generator=g).to(torch.bfloat16).to(dev)
+                        for n in (CACHED_LEN, CACHED_LEN, new, new))
+    for _ in range(3):
+        sdpa.prefill_cached(cq, ckc, cvc, ck, cv, cache_len=CACHED_LEN, causal=True, scale=cw.scale)
+    torch.cuda.synchronize()
+    mq, mk, mv, mbias = _masked_inputs(dev)
+    for _ in range(3):
+        sdpa.prefill_masked(mq, mk, mv, mbias, scale=MASKED.scale)
+    torch.cuda.synchronize()
+    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20, mask conversion x6, "
+          f"unaligned / fp8 / cached / masked prefill x3 each", flush=True)
+
+
+def _masked_inputs(dev):
+    """The masked-prefill leg's inputs: seeded Q, K, V and a per-head linear
+    distance bias [1, Hq, Sq, Sk] (slopes 2^(-h/4)), on the device."""
+    import torch
+
+    xw = MASKED
+    g = torch.Generator().manual_seed(xw.seed)
+    mq = torch.randn(1, xw.q_len, xw.head_q, xw.d_qk, generator=g).to(torch.bfloat16)
+    mk = torch.randn(1, xw.kv_len, xw.head_kv, xw.d_qk, generator=g).to(torch.bfloat16)
+    mv = torch.randn(1, xw.kv_len, xw.head_kv, xw.d_v, generator=g).to(torch.bfloat16)
+    ii = torch.arange(xw.q_len, device=dev)[:, None]
+    jj = torch.arange(xw.kv_len, device=dev)[None, :]
+    slope = 2.0 ** (-torch.arange(1, xw.head_q + 1, device=dev) / 4.0)
+    mbias = (-(slope[:, None, None] * (ii - jj).abs()[None])).to(torch.bfloat16)[None].contiguous()
+    return mq.to(dev), mk.to(dev), mv.to(dev), mbias
+
+
+# SQ counters of one --pmc pass (at most 8 SQ and 2 GRBM counters per pass)
+SQ_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU",
+               "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def _sq_profiles():
+    """(profile stem, kernel-name fragment, grid work-items or None, source
+    files, workload label) of every kernel the SQ summary covers."""
+    import attention_flash_sdpa_amd as sdpa
+    from attention_flash_sdpa_amd import inputs
+
+    out = []
+    for wname in ("gqa_causal_prefill_bf16", "unaligned_full_bf16", "mla_fp8_causal_prefill", "splitkv_decode_bf16"):
+        w = inputs.WORKLOADS[wname]
+        for kname, grid in _kernels_of(sdpa, w):
+            fam = kname.split("<")[0]
+            src = _SOURCES["decode"] if w.decode else (_SOURCES["fp8"] if w.dtype == "fp8_e4m3" else
+                                                       _SOURCES["prefill"])
+            out.append((f"{fam}_{wname}", kname, grid, src, wname))
+    for kname, grid in _kernels_of(sdpa, CACHED_CHUNK, cached=True):
+        out.append((f"{kname.split('<')[0]}_{CACHED_CHUNK.name}", kname, grid, _SOURCES["prefill"], CACHED_CHUNK.name))
+    out.append((f"prefill_masked_kernel_{MASKED.name}", "prefill_masked_kernel<sdpa::Bf16, 128, 128, false>", None,
+                _SOURCES["masked"], MASKED.name))
+    return out
+
+
+def _summarize_sq(d):
+    """Per-kernel SQ counter summaries (MFMA busy, instruction mix, LDS bank
+    conflicts) from one `rocprofv3 --pmc <SQ_COUNTERS>` run of the counters
+    pass, written to profiles/<kernel>_<workload>_sq_counters.txt."""
+    import statistics
+
+    rows = _read_csv(os.path.join(d, "run_counter_collection.csv"))
+    for stem, kname, grid, src, wname in _sq_profiles():
+        per = {}
+        for r in rows:
+            if kname in r["Kernel_Name"] and (grid is None or int(r["Grid_Size"]) == grid):
+                per.setdefault(r["Counter_Name"], {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+                per[r["Counter_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        if not per:
+            continue
+        avg = {c: statistics.mean(v.values()) for c, v in per.items()}
+        n = max(len(v) for v in per.values())
+        out = os.path.join(ROOT, "profiles", f"{stem}_sq_counters.txt")
+        with open(out, "w") as f:
+            f.write(f"kernel: {kname}\nworkload: {wname}\n")
+            f.write(f"command:\n  rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {d} -o run "
+                    f"-- python3 bench.py --counters-pass\n  python3 bench.py --summarize-sq {d}\n")
+            f.write(f"dispatches: {n}\nper dispatch (mean):\n")
+            for c in SQ_COUNTERS:
+                if c in avg:
+                    f.write(f"  {c}: {avg[c]:.0f}\n")
+            mf, valu = avg.get("SQ_INSTS_MFMA"), avg.get("SQ_INSTS_VALU")
+            busy, cu = avg.get("SQ_VALU_MFMA_BUSY_CYCLES"), avg.get("SQ_BUSY_CU_CYCLES")
+            if mf and valu:
+                f.write(f"non-MFMA VALU instructions per MFMA: {(valu - mf) / mf:.2f}\n")
+            if busy and cu:
+                f.write(f"SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES: {busy / cu:.3f}\n")
+            if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_INSTS_LDS" in avg and avg["SQ_INSTS_LDS"]:
+                f.write(f"LDS bank-conflict cycles per LDS instruction: "
+                        f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.3f}\n")
+            f.write(f"source_sha256: {_src_hash(*src)}\n")
+        print("wrote", out)
 
 
 def _read_csv(path):
@@ -386,6 +510,7 @@ def main():
     ap.add_argument("--counters-pass", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-sq", metavar="DIR")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention path "
@@ -396,6 +521,8 @@ def main():
         return _summarize_trace(args.summarize_trace)
     if args.summarize_counters:
         return _summarize_counters(*args.summarize_counters)
+    if args.summarize_sq:
+        return _summarize_sq(args.summarize_sq)
     if args.counters_pass:
         return _counters_pass()
 
@@ -440,11 +567,9 @@ def main():
     dw = inputs.WORKLOADS["splitkv_decode_bf16"]
     dq, dk0, dv0, _ = inputs.make_qkv(dw)
     dqd = dq.reshape(dw.batch, dw.head_q, dw.d_qk).to(dev)
-    sets = [(dk0.to(dev), dv0.to(dev))]
-    for s in range(1, dw.kv_sets):
-        g = torch.Generator(device=dev).manual_seed(dw.seed + 100 * s)
-        sets.append(tuple(torch.randn(t.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-                          for t in (dk0, dv0)))
+    # every rotating K/V set is drawn by the seeded CPU recipe (seed + 100 * set)
+    cpu_sets = [(dk0, dv0)] + [inputs.make_qkv(dw, kv_set=s_)[1:3] for s_ in range(1, dw.kv_sets)]
+    sets = [(kk.to(dev), vv.to(dev)) for kk, vv in cpu_sets]
     dout = torch.empty(dw.batch, dw.head_q, dw.d_v, dtype=torch.bfloat16, device=dev)
     ws = sdpa.decode_workspace(dqd, sets[0][0], sets[0][1])
 
@@ -457,12 +582,18 @@ def main():
     dbytes = dw.bytes_moved()
     dgbs = dbytes / (dms * 1e-3) / 1e9
     dplan = sdpa.plan(_problem(sdpa, dw), decode=True, num_cus=ncu)
-    sdpa.decode(dqd, sets[0][0], sets[0][1], scale=dw.scale, out=dout, workspace=ws)
-    torch.cuda.synchronize()
+    # sampled parity of every set against the oracle
     drows = np.array([(b, 0, h) for b in (0, 7, 15) for h in (0, 17, 31)], dtype=np.int64)
-    dref = oracle.sdpa(dq, dk0, dv0, scale=dw.scale, causal=False, rows=drows, want_lse=False)["out"]
-    dgot = dout.cpu()[drows[:, 0], drows[:, 2]].double().numpy()
-    decode_err = float(np.abs(dgot - dref).max())
+    decode_err = 0.0
+    decode_nan = 0
+    for s_, (kk, vv) in enumerate(sets):
+        sdpa.decode(dqd, kk, vv, scale=dw.scale, out=dout, workspace=ws)
+        torch.cuda.synchronize()
+        dref = oracle.sdpa(dq, cpu_sets[s_][0], cpu_sets[s_][1], scale=dw.scale, causal=False, rows=drows,
+                           want_lse=False)["out"]
+        dgot = dout.cpu()[drows[:, 0], drows[:, 2]].double().numpy()
+        decode_err = max(decode_err, float(np.abs(dgot - dref).max()))
+        decode_nan += int(np.isnan(dgot).sum())
     del sets
     dcpu = None
     if not args.no_cpu_baseline:
@@ -481,12 +612,10 @@ def main():
         P = dw.kv_len // PS
         kp0, vp0, table0 = inputs.paginate(dk0, dv0, PS, seed=dw.seed + 1)
         psets = [(kp0.to(dev), vp0.to(dev), table0.to(dev))]
-        for s in range(1, dw.kv_sets):
-            g = torch.Generator(device=dev).manual_seed(dw.seed + 100 * s)
-            pk, pv = (torch.randn(t.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-                      for t in (kp0, vp0))
-            perm = torch.randperm(dw.batch * P, generator=torch.Generator().manual_seed(dw.seed + 100 * s + 1))
-            psets.append((pk, pv, perm.reshape(dw.batch, P).to(torch.int32).to(dev)))
+        for s_ in range(1, dw.kv_sets):
+            pk, pv, pt = inputs.paginate(cpu_sets[s_][0], cpu_sets[s_][1], PS, seed=dw.seed + 100 * s_ + 1)
+            psets.append((pk.to(dev), pv.to(dev), pt.to(dev)))
+            del pk, pv
         full = torch.full((dw.batch,), dw.kv_len, dtype=torch.int32, device=dev)
 
         def pstep(i):
@@ -497,6 +626,15 @@ def main():
         pms = _graph_time(pstep, args.decode_steps, args.warmup, period=len(psets))
         pbytes = dbytes + table0.numel() * 4 + dw.batch * 4
         pgbs = pbytes / (pms * 1e-3) / 1e9
+        # sets 1-3: sampled rows against the dense oracle of the same keys
+        paged_err_rest = 0.0
+        for s_ in range(1, len(psets)):
+            pstep(s_)
+            torch.cuda.synchronize()
+            pref_s = oracle.sdpa(dq, cpu_sets[s_][0], cpu_sets[s_][1], scale=dw.scale, causal=False, rows=drows,
+                                 want_lse=False)["out"]
+            pgot = dout.cpu()[drows[:, 0], drows[:, 2]].double().numpy()
+            paged_err_rest = max(paged_err_rest, float(np.abs(pgot - pref_s).max()))
         pstep(0)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -512,10 +650,14 @@ def main():
             "algorithmic_bytes": pbytes,
             "roofline": {"bound": "hbm", "achieved": round(pgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
-            "parity": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
+            "parity": {"max_abs_err": max(paged_err, paged_err_rest),
+                       "set0": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
+                       "sets1_3": {"max_abs_err": paged_err_rest, "rows_per_set": int(len(drows))}},
             "cpu_baseline": _cpu_line(round(pbytes / psec / 1e9, 3), "GB/s", torch.get_num_threads(),
                                       f"whole workload through the paged oracle in {psec:.2f} s, fp64"),
         }
+
+    del cpu_sets
 
     # ---------------- other prefill workloads (context lines) ----------------
     extra = {}
@@ -525,7 +667,7 @@ def main():
         xq, xk, xv = (t.to(dev) for t in (xq, xk, xv))
         odt = torch.bfloat16 if xw.out_dtype == "bf16" else torch.float16
         xo = torch.empty(xw.batch, xw.q_len, xw.head_q, xw.d_v, dtype=odt, device=dev)
-        n = 100 if xw.flops() < 1e9 else max(args.steps // 4, 1)
+        n = 100 if xw.flops() < 1e9 else max(args.steps // 4, MIN_LEG_CALLS)
 
         def xstep(i):
             sdpa.prefill(xq, xk, xv, scale=xw.scale, causal=xw.causal, out=xo, descale=xds)
@@ -554,7 +696,7 @@ def main():
     def cstep(i):
         sdpa.prefill_cached(cqd, ckcd, cvcd, ckd, cvd, cache_len=CACHED_LEN, causal=True, scale=cw.scale, out=co)
 
-    cn = max(args.steps // 4, 1)
+    cn = max(args.steps // 4, MIN_LEG_CALLS)
     ceager = _time(cstep, cn, args.warmup, stream)
     cms = _graph_time(cstep, cn, args.warmup)
     cstep(0)
@@ -619,21 +761,14 @@ def main():
     from oracle import mask as omask2
 
     xw = MASKED
-    g = torch.Generator().manual_seed(xw.seed)
-    mq = torch.randn(1, xw.q_len, xw.head_q, xw.d_qk, generator=g).to(torch.bfloat16)
-    mk = torch.randn(1, xw.kv_len, xw.head_kv, xw.d_qk, generator=g).to(torch.bfloat16)
-    mv = torch.randn(1, xw.kv_len, xw.head_kv, xw.d_v, generator=g).to(torch.bfloat16)
-    ii = torch.arange(xw.q_len, device=dev)[:, None]
-    jj = torch.arange(xw.kv_len, device=dev)[None, :]
-    slope = 2.0 ** (-torch.arange(1, xw.head_q + 1, device=dev) / 4.0)
-    mbias = (-(slope[:, None, None] * (ii - jj).abs()[None])).to(torch.bfloat16)[None].contiguous()
-    mqd, mkd, mvd = (t.to(dev) for t in (mq, mk, mv))
+    mqd, mkd, mvd, mbias = _masked_inputs(dev)
+    mq, mk, mv = (t.cpu() for t in (mqd, mkd, mvd))
     mo = torch.empty(1, xw.q_len, xw.head_q, xw.d_v, dtype=torch.bfloat16, device=dev)
 
     def xmstep(i):
         sdpa.prefill_masked(mqd, mkd, mvd, mbias, scale=xw.scale, out=mo)
 
-    xn = max(args.steps // 10, 1)
+    xn = max(args.steps // 10, MIN_LEG_CALLS)
     xmms = _graph_time(xmstep, xn, args.warmup)
     xmstep(0)
     torch.cuda.synchronize()
@@ -691,7 +826,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "head_q": w.head_q, "head_kv": w.head_kv,
                    "q_len": w.q_len, "kv_len": w.kv_len, "d_qk": w.d_qk, "d_v": w.d_v, "causal": True,
                    "algorithmic_gflop": round(flops / 1e9, 4), "grid": plan.num_groups,
-                   "launch": "hip graph replay of gcd(steps, warmup) calls"},
+                   "launch": "hip graph replays of a captured chunk of calls (chunk divides steps; at least one "
+                             "untimed replay first)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 5), "traffic": traffic},
         "cpu_baseline": cpu,
@@ -704,7 +840,8 @@ def main():
             "algorithmic_bytes": dbytes,
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dgbs / PEAK_HBM_GBS, 5), "traffic": dtraffic},
-            "parity": {"max_abs_err": decode_err},
+            "parity": {"max_abs_err": decode_err, "nan": decode_nan, "sets_checked": dw.kv_sets,
+                       "rows_per_set": int(len(drows))},
             "cpu_baseline": dcpu,
         },
         "decode_paged": paged_lines[64],

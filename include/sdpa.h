@@ -64,7 +64,8 @@ typedef enum {
   SDPA_ERR_BAD_SHAPE = 2,   /* negative size, head_q % head_kv != 0, decode
                                with q_len != 1, sizes overflowing 32-bit
                                element offsets per batch entry, ...          */
-  SDPA_ERR_BAD_SCALE = 3,   /* scale or a descale not finite, or negative     */
+  SDPA_ERR_BAD_SCALE = 3,   /* scale or a descale not finite, or negative, or
+                               a descale != 1 with fp16/bf16 inputs          */
   SDPA_ERR_UNSUPPORTED = 4, /* (dtype, d_qk, d_v) outside the supported set   */
   SDPA_ERR_MISALIGNED = 5,  /* a data pointer not 16-byte aligned             */
   SDPA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required        */
@@ -75,7 +76,9 @@ typedef enum {
  * 1/sqrt(d_qk)); it is folded with log2(e) so that every exponential is a
  * base-2 exponential ("Xe SDPA Forward Mainloop", section "Arguments /
  * params").  q/k/v_descale are the per-tensor dequantisation factors of fp8
- * inputs (x = x_q * descale); they must be 1 for fp16/bf16 inputs. */
+ * inputs (x = x_q * descale), host floats known when the inputs were
+ * quantised; any value other than 1 with fp16/bf16 inputs is rejected with
+ * SDPA_ERR_BAD_SCALE by every entry point. */
 typedef struct sdpa_problem {
   int32_t batch;
   int32_t q_len;
@@ -150,6 +153,19 @@ const char* sdpa_status_string(int status);
 
 /* Detail text of the last failing call on the calling thread ("" if none). */
 const char* sdpa_last_error(void);
+
+/* Forces one form of the 16-bit prefill kernels for every later call of this
+ * process, for tuning sweeps and tests (the forms compute the same result):
+ *   "narrow1" / "narrow2" : one wave per SIMD, one / two key ranges per
+ *                           workgroup merged at the end;
+ *   "occ2"                : two waves per SIMD, one key range;
+ *   "split4"              : two waves per SIMD, four key ranges of 32-key blocks;
+ *   "" / "auto" / NULL    : the planner's choice (the default).
+ * The environment variable SDPA_PREFILL_VARIANT gives the initial value (read
+ * once).  Unknown names return SDPA_ERR_UNSUPPORTED and change nothing.
+ * Host-only; process-wide; do not change it while another thread plans or
+ * launches a prefill. */
+sdpa_status_t sdpa_set_prefill_variant(const char* name);
 
 /* Validates a problem and fills the plan the entry points would use.
  * is_decode selects the split-KV decode path (q_len must be 1).  num_cus is

@@ -18,3 +18,13 @@ def oracle_mod():
 
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture
+def prefill_variant():
+    """Forces a form of the 16-bit prefill kernels for one test (restored to
+    the planner's choice afterwards)."""
+    import attention_flash_sdpa_amd as sdpa
+
+    yield sdpa.set_prefill_variant
+    sdpa.set_prefill_variant(None)

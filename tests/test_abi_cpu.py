@@ -121,25 +121,63 @@ def test_plans_for_workloads():
     assert d64.num_splits == 16 and d64.num_groups == 512
 
 
-def test_prefill_variant_override(monkeypatch):
+def test_decode_large_groups_take_one_wave_per_16_heads():
+    """More than 16 query heads per KV head: one wave per (KV head, tile of up
+    to 16 query heads), four such tasks per workgroup."""
+    import dataclasses
+
+    w = dataclasses.replace(inputs.WORKLOADS["splitkv_decode_bf16"], head_q=64, head_kv=2)   # G = 32
+    d = sdpa.plan(_problem(w), decode=True, num_cus=256)
+    tasks = 16 * 2 * 2   # batch x KV heads x tiles
+    assert d.num_groups == 16 * d.num_splits * ((2 * 2 + 3) // 4)
+    assert d.num_splits == min(-(-256 * 4 // tasks), 8192 // 32 // 2)
+    w20 = dataclasses.replace(w, head_q=20, head_kv=1, batch=1)   # G = 20: tiles of 16 and 4
+    d20 = sdpa.plan(_problem(w20), decode=True, num_cus=256)
+    assert d20.num_groups == d20.num_splits * 1   # 2 tasks fit one workgroup
+    assert d20.workspace_bytes == 1 * 20 * d20.num_splits * (128 * 4 + 8)
+
+
+def test_prefill_variant_override(prefill_variant):
     w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "wide")
-    pw = sdpa.plan(_problem(w))
-    assert (pw.rows_per_wave, pw.block_k, pw.block_q, pw.q_tiles) == (64, 32, 64, 8)
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow")
-    assert sdpa.plan(_problem(inputs.WORKLOADS["unaligned_full_bf16"])).rows_per_wave == 32
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow1")
+    prefill_variant("narrow1")
     p1 = sdpa.plan(_problem(w))
     assert (p1.num_splits, p1.heads_per_group, p1.num_groups, p1.lds_bytes) == (1, 4, 128, 65536)
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "narrow2")
+    prefill_variant("narrow2")
     p2 = sdpa.plan(_problem(inputs.WORKLOADS["unaligned_full_bf16"]))
     assert (p2.num_splits, p2.heads_per_group, p2.qtiles_per_group, p2.num_groups) == (2, 1, 2, 2 * 4 * 7 * 16)
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", "split4")
+    prefill_variant("split4")
     p4 = sdpa.plan(_problem(w))
     assert (p4.kernel, p4.num_splits, p4.waves_per_group, p4.block_k, p4.kv_blocks) == (27, 4, 8, 32, 32)
     assert (p4.heads_per_group, p4.qtiles_per_group, p4.num_groups, p4.lds_bytes) == (2, 1, 8 * 2 * 16, 131072)
-    monkeypatch.delenv("SDPA_PREFILL_VARIANT")
-    assert sdpa.plan(_problem(w)).rows_per_wave == 32
+    with pytest.raises(sdpa.SdpaError, match="UNSUPPORTED"):
+        prefill_variant("wide")   # unknown names change nothing
+    assert sdpa.plan(_problem(w)).num_splits == 4
+    prefill_variant(None)
+    assert sdpa.plan(_problem(w)).rows_per_wave == 32 and sdpa.plan(_problem(w)).num_splits == 2
+
+
+def test_descale_must_be_one_for_16bit_inputs():
+    """Dequantisation factors belong to fp8 inputs; with fp16/bf16 inputs any
+    factor other than 1 is rejected by the planner, so every entry point
+    (prefill, cached, masked, decode, paged) refuses it before a launch."""
+    for name in ("gqa_causal_prefill_bf16", "single_head_f16_128"):
+        w = inputs.WORKLOADS[name]
+        for ds in ((2.0, 1.0, 1.0), (1.0, 0.5, 1.0), (1.0, 1.0, 3.0)):
+            pr = sdpa.make_problem(batch=w.batch, q_len=w.q_len, kv_len=w.kv_len, head_q=w.head_q,
+                                   head_kv=w.head_kv, d_qk=w.d_qk, d_v=w.d_v,
+                                   in_dtype=sdpa.BF16 if w.dtype == "bf16" else sdpa.F16,
+                                   out_dtype=sdpa.BF16 if w.dtype == "bf16" else sdpa.F16, causal=w.causal,
+                                   scale=w.scale, descale=ds)
+            for dec in (False, True):
+                if dec:
+                    pr.q_len = 1
+                with pytest.raises(sdpa.SdpaError, match="BAD_SCALE"):
+                    sdpa.plan(pr, decode=dec)
+    w = inputs.WORKLOADS["mla_fp8_causal_prefill"]
+    pr = sdpa.make_problem(batch=1, q_len=w.q_len, kv_len=w.kv_len, head_q=w.head_q, head_kv=w.head_kv,
+                           d_qk=w.d_qk, d_v=w.d_v, in_dtype=sdpa.FP8_E4M3, out_dtype=sdpa.BF16, causal=True,
+                           scale=w.scale, descale=(0.01, 0.02, 0.03))
+    sdpa.plan(pr)   # fp8: any finite factor >= 0
 
 
 def test_decode_split_choices():
@@ -158,7 +196,7 @@ def test_decode_split_choices():
     (dict(head_q=30), False, 2), (dict(q_len=-1), False, 2), (dict(scale=-1.0), False, 3),
     (dict(scale=float("inf")), False, 3), (dict(scale=float("nan")), False, 3), (dict(d_qk=96, d_v=96), False, 4),
     (dict(d_qk=128, d_v=64), False, 4), (dict(out_dtype=sdpa.F16), False, 4), (dict(descale=(1.0, -2.0, 1.0)), False, 3),
-    (dict(q_len=2), True, 2), (dict(head_q=8 * 17), True, 4), (dict(in_dtype=sdpa.FP8_E4M3), True, 4),
+    (dict(q_len=2), True, 2), (dict(d_qk=96, d_v=96), True, 4), (dict(in_dtype=sdpa.FP8_E4M3), True, 4),
 ])
 def test_validation_errors(over, decode, code):
     base = inputs.WORKLOADS["splitkv_decode_bf16" if decode else "gqa_causal_prefill_bf16"]
@@ -305,3 +343,36 @@ def test_masked_prefill_argument_errors_before_any_launch():
     assert call(mask=ctypes.c_void_p(0x1008)) == 5
     assert call(_problem(w, causal=False, out_dtype=sdpa.F16)) == 4     # output type differs from the input's
     assert call(_problem(w, causal=False, q_len=0)) == 0
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks every tensor the kernels index before any launch:
+    one dtype and device for q/k/v, consistent batch / head / dim, and the
+    exact shape and dtype of a caller's out / lse.  The CPU tensors here fail
+    the device check first, so a second set of checks runs through the
+    shape/dtype validators directly."""
+    import torch
+
+    from attention_flash_sdpa_amd import binding as bd
+
+    q = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        sdpa.prefill(q, k, v)
+    with pytest.raises(ValueError, match="batch"):
+        bd._check_prefill_shapes(q, torch.zeros(2, 16, 2, 64), torch.zeros(2, 16, 2, 64))
+    with pytest.raises(ValueError, match="head dim"):
+        bd._check_prefill_shapes(q, torch.zeros(1, 16, 2, 128), torch.zeros(1, 16, 2, 64))
+    with pytest.raises(ValueError, match="does not match k"):
+        bd._check_prefill_shapes(q, k, torch.zeros(1, 15, 2, 64))
+    bd._check_prefill_shapes(q, k, v)
+    with pytest.raises(ValueError, match="must be"):
+        bd._check_output("out", torch.zeros(1, 8, 4, 32, dtype=torch.bfloat16), (1, 8, 4, 64), (torch.bfloat16,),
+                         q.device)
+    with pytest.raises(ValueError, match="dtype"):
+        bd._check_output("lse", torch.zeros(1, 4, 8, dtype=torch.float16), (1, 4, 8), (torch.float32,), q.device)
+    with pytest.raises(ValueError, match="contiguous"):
+        bd._check_output("lse", torch.zeros(1, 8, 4).transpose(1, 2), (1, 4, 8), (torch.float32,), q.device)
+    assert bd._out_dtypes(q) == (torch.bfloat16,)
+    assert set(bd._out_dtypes(q.to(torch.float8_e4m3fn))) == {torch.bfloat16, torch.float16}

@@ -88,10 +88,10 @@ CASES = [
 @pytest.mark.parametrize("variant", ["", "narrow1", "narrow2", "occ2", "split4"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_q{c[1]}_c{c[2]}of{c[3]}_k{c[4]}_h{c[5]}x{c[6]}_d{c[7]}_"
                                              f"{'causal' if c[9] else 'full'}" for c in CASES])
-def test_cached_prefill(dev, case, variant, monkeypatch):
+def test_cached_prefill(dev, case, variant, prefill_variant):
     B, Sq, Sc, cap, Sk, Hq, Hkv, D, dt, causal = case
     if variant:
-        monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
+        prefill_variant(variant)
     _say(f"cached prefill B={B} q={Sq} cache={Sc}/{cap} new={Sk} Hq={Hq} Hkv={Hkv} D={D} {dt} causal={causal} "
          f"variant={variant or 'default'}")
     q, kc, vc, k, v = _draw(B, Sq, Sc, cap, Sk, Hq, Hkv, D, dt, Sq + 7 * Sc + Sk)

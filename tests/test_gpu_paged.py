@@ -85,6 +85,7 @@ PAGED = [
     (4, 1000, 8, 2, 128, torch.bfloat16, 16, 0, "mix"),    # 16-key pages: two pages per block
     (3, 777, 16, 4, 64, torch.float16, 8, 0, "mix"),       # 8-key pages: four pages per block
     (3, 5000, 6, 2, 128, torch.bfloat16, 8, 2, "mix"),     # 8-key pages, 316 pages per split: table reloads
+    (3, 1200, 64, 2, 128, torch.bfloat16, 64, 0, "mix"),   # 32 query heads per KV head (two 16-head tiles)
 ]
 
 

@@ -103,9 +103,9 @@ def test_gqa_causal_prefill_bf16(dev, oracle_mod):
 
 
 @pytest.mark.parametrize("variant", ["narrow1", "occ2", "split4"])
-def test_gqa_causal_prefill_bf16_forms(dev, oracle_mod, variant, monkeypatch):
+def test_gqa_causal_prefill_bf16_forms(dev, oracle_mod, variant, prefill_variant):
     """The full-size causal GQA workload through the other 32-row forms."""
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
+    prefill_variant(variant)
     w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
     q, k, v, _ = inputs.make_qkv(w)
     _prefill_case(dev, oracle_mod, q, k, v, causal=w.causal, scale=w.scale, what=f"{w.name} {variant}")
@@ -176,13 +176,13 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "split4", "wide"])
+@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "split4"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}_q{c[1]}_k{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_{str(c[6])[6:]}_{'c' if c[7] else 'f'}" for c in EDGE])
-def test_prefill_edge_shapes(dev, oracle_mod, case, variant, monkeypatch):
-    """Every edge shape through every 16-bit prefill kernel: 32-row waves (one
-    wave per SIMD with one or two key ranges per workgroup, two waves per
-    SIMD with one or four key ranges) and 64-row waves."""
-    monkeypatch.setenv("SDPA_PREFILL_VARIANT", variant)
+def test_prefill_edge_shapes(dev, oracle_mod, case, variant, prefill_variant):
+    """Every edge shape through every 16-bit prefill kernel form: one wave per
+    SIMD with one or two key ranges per workgroup, two waves per SIMD with one
+    or four key ranges."""
+    prefill_variant(variant)
     B, Sq, Sk, Hq, Hkv, D, dt, causal = case
     g = torch.Generator().manual_seed(Sq * 1000 + Sk)
     q = torch.randn(B, Sq, Hq, D, generator=g).to(dt)
@@ -264,6 +264,9 @@ DECODE_EDGE = [
     (4, 333, 12, 4, 64, torch.float16, 0),
     (3, 70, 6, 2, 128, torch.bfloat16, 0),     # 18 (batch, head) rows: a partly filled combine workgroup
     (1, 2000, 6, 3, 64, torch.float16, 40),    # more than 32 splits (looped combine), 6 rows
+    (2, 1500, 64, 2, 128, torch.bfloat16, 0),  # 32 query heads per KV head: two 16-head tiles per KV head
+    (3, 700, 20, 1, 64, torch.float16, 0),     # 20 per KV head: a full and a 4-head tile
+    (1, 900, 160, 5, 128, torch.bfloat16, 3),  # 32 per KV head, 10 tasks: a partly filled workgroup
 ]
 
 
@@ -285,3 +288,35 @@ def test_decode_kv_len_zero(dev):
     sdpa.decode(q, k, k, out=out, lse=lse)
     torch.cuda.synchronize()
     assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_binding_rejects_mismatched_device_tensors(dev):
+    """Mismatched device tensors are refused by the binding before any launch
+    (an fp8 K under bf16 Q, a short K batch or a small out / lse would
+    otherwise be indexed past their ends)."""
+    q = torch.zeros(2, 64, 8, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(2, 96, 2, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(2, 96, 2, 128, dtype=torch.bfloat16, device=dev)
+    bad = [
+        dict(k=k.to(torch.float8_e4m3fn)),
+        dict(k=k[:1].contiguous(), v=v[:1].contiguous()),
+        dict(v=v[:, :95].contiguous()),
+        dict(out=torch.empty(2, 64, 8, 64, dtype=torch.bfloat16, device=dev)),
+        dict(out=torch.empty(2, 64, 8, 128, dtype=torch.float16, device=dev)),
+        dict(lse=torch.empty(2, 8, 63, dtype=torch.float32, device=dev)),
+        dict(lse=torch.empty(2, 8, 64, dtype=torch.float16, device=dev)),
+    ]
+    for case in bad:
+        args = dict(q=q, k=k, v=v)
+        args.update({n: t for n, t in case.items() if n in ("k", "v")})
+        kw = {n: t for n, t in case.items() if n in ("out", "lse")}
+        with pytest.raises(ValueError):
+            sdpa.prefill(args["q"], args["k"], args["v"], causal=True, **kw)
+    qd = torch.zeros(2, 8, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        sdpa.decode(qd, k.to(torch.float16), v)
+    with pytest.raises(ValueError):
+        sdpa.decode(qd, k, v, out=torch.empty(2, 8, 64, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        sdpa.decode(qd, k, v, lse=torch.empty(2, 4, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
