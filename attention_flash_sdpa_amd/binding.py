@@ -25,7 +25,7 @@ EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
     "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_prefill_masked_fwd",
-    "sdpa_loop_counts", "sdpa_set_prefill_variant",
+    "sdpa_loop_counts", "sdpa_set_prefill_variant", "sdpa_decode_fwd_noalloc",
 )
 
 
@@ -102,6 +102,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
     lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.sdpa_decode_fwd_noalloc.restype = ctypes.c_int
+    lib.sdpa_decode_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     i32 = ctypes.c_int32
     lib.sdpa_decode_paged_fwd.restype = ctypes.c_int
     lib.sdpa_decode_paged_fwd.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int, vp, sz, vp]
@@ -331,6 +333,29 @@ def decode(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, workspace=N
     _require(workspace.tensor.device == q.device, "workspace must be on q's device")
     _check(lib.sdpa_decode_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(num_splits),
                                _ptr(workspace.tensor), workspace.nbytes, _stream_handle(stream)))
+    return out
+
+
+def decode_noalloc(q, k, v, *, scale=None, out=None, lse=None, num_splits=0, descale=(1.0, 1.0, 1.0), stream=None):
+    """Two-phase split-KV decode through ``sdpa_decode_fwd_noalloc``: the
+    split partials live in the library's static per-GPU scratch, so no
+    workspace is allocated (``out`` is still allocated here when not given).
+    Arguments as for ``decode``; calls that overlap on one GPU race."""
+    import torch
+
+    _check_inputs(("q", "k", "v"), (q, k, v))
+    _check_caches(q, k, v, dense=True)
+    B, Hq, D = q.shape
+    Dv = v.shape[-1]
+    _check_output("out", out, (B, Hq, Dv), (q.dtype,), q.device)
+    _check_output("lse", lse, (B, Hq), (torch.float32,), q.device)
+    if out is None:
+        out = torch.empty(B, Hq, Dv, dtype=q.dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    pr = _decode_problem(q, k, v, scale, descale, out)
+    _check(load().sdpa_decode_fwd_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                          int(num_splits), _stream_handle(stream)))
     return out
 
 

@@ -39,6 +39,8 @@
 // come out NaN.
 #include <math.h>
 
+#include <mutex>
+
 #include "sdpa_device.h"
 #include "sdpa_internal.h"
 
@@ -414,6 +416,32 @@ __global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const
     o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
   }
   if (a.lse != nullptr && lane == 0) a.lse[bh] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
+}
+
+// ---- scratch of the no-allocation decode entry point -----------------------
+// Split partials of sdpa_decode_fwd_noalloc live in this file-scope array, one
+// copy per GPU the library runs on, held until the process ends.  In host code
+// `scratch` only names a host-side stand-in: its device address on the current
+// GPU comes from hipGetSymbolAddress, fetched once per device and kept.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 template <class T, int D>

@@ -404,6 +404,30 @@ sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, cons
                        0, 0, 0);
 }
 
+sdpa_status_t sdpa_decode_fwd_noalloc(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
+                                      void* o, float* lse, int num_splits, void* stream) {
+  clear_error();
+  if (problem == nullptr) {
+    set_error("problem must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  sdpa_plan_t plan;
+  sdpa_status_t st = make_plan(*problem, true, device_cus(), num_splits, &plan);
+  if (st != SDPA_OK) return st;
+  if (plan.workspace_bytes > kNoAllocScratchBytes) {
+    set_error("the split partials need %llu bytes, more than the %llu-byte static scratch of the no-allocation "
+              "decode; use sdpa_decode_fwd with a workspace", (unsigned long long)plan.workspace_bytes,
+              (unsigned long long)kNoAllocScratchBytes);
+    return SDPA_ERR_WORKSPACE;
+  }
+  if (problem->batch == 0) return SDPA_OK;
+  void* ws = nullptr;
+  const int e = noalloc_scratch(&ws);
+  if (e != 0) return hip_status(e, "static decode scratch lookup");
+  return decode_common(problem, q, k, v, o, lse, num_splits, ws, kNoAllocScratchBytes, stream, nullptr, nullptr, 0,
+                       0, 0);
+}
+
 sdpa_status_t sdpa_decode_paged_fwd(const sdpa_problem_t* problem, const void* q, const void* k_cache,
                                     const void* v_cache, const int32_t* seq_lens, const int32_t* page_table,
                                     int32_t num_pages, int32_t page_size, int32_t pages_per_seq, void* o,

@@ -126,4 +126,12 @@ struct MaskedArgs {
 int launch_prefill_masked(const MaskedArgs& a, int in_dtype, int d, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
+// The no-allocation decode keeps its split partials in a static device array
+// of this size (per GPU); larger problems are refused.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+// Device address of that array on the current GPU (looked up on the first
+// call per device, then cached).  Returns a hipError_t value (0 = success).
+int noalloc_scratch(void** ptr);
+
 }  // namespace sdpa

@@ -277,6 +277,23 @@ sdpa_status_t sdpa_decode_fwd(const sdpa_problem_t* problem, const void* q, cons
                               const void* v, void* o, float* lse, int num_splits,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* sdpa_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials go to a static device
+ * array of 64 MiB held by the library on each GPU it runs on until the
+ * process ends; its address is looked up on the first call per device.  The
+ * call itself allocates and frees nothing.
+ *   arguments as for sdpa_decode_fwd, less workspace / workspace_bytes.
+ * A problem whose partials (sdpa_decode_workspace_bytes) exceed 64 MiB
+ * returns SDPA_ERR_WORKSPACE before any launch.  Every call on one GPU uses
+ * the same array, which keeps the last call's contents (nothing in it needs
+ * clearing: each call writes every partial it reads): calls that overlap on
+ * one GPU (two streams, or two threads) race and must be serialised by the
+ * caller, e.g. on one stream. */
+sdpa_status_t sdpa_decode_fwd_noalloc(const sdpa_problem_t* problem, const void* q, const void* k,
+                                      const void* v, void* o, float* lse, int num_splits,
+                                      void* stream);
+
 /* Decode over variable-length and/or paged key/value caches.  The mainloop
  * page ("Xe SDPA Forward Mainloop", section "Runtime args / params") lists
  * an optional page table, page size and per-sequence page counts among its
