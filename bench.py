@@ -343,7 +343,10 @@ def _summarize_sq(d):
             if mf and valu:
                 f.write(f"non-MFMA VALU instructions per MFMA: {(valu - mf) / mf:.2f}\n")
             if busy and cu:
-                f.write(f"SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES: {busy / cu:.3f}\n")
+                # busy cycles are counted per SIMD (32 per 32x32x16 MFMA), CU-busy
+                # cycles per CU: four SIMDs per CU
+                f.write(f"MFMA busy share of SIMD cycles while the CUs are busy, "
+                        f"SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES): {busy / (4 * cu):.3f}\n")
             if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_INSTS_LDS" in avg and avg["SQ_INSTS_LDS"]:
                 f.write(f"LDS bank-conflict cycles per LDS instruction: "
                         f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.3f}\n")

@@ -60,6 +60,15 @@ def test_vector_writes_before_mfma_inputs(asm, src):
 
 
 @pytest.mark.parametrize("src", SOURCES)
+def test_asm_lds_reads_waited_for(asm, src):
+    # an LDS read written in inline asm is invisible to the compiler's wait
+    # count pass: nothing (a register copy or spill included) may touch its
+    # result before a wait that covers it, on any path
+    bad, n = isa_scan.asm_lds_reads_waited(asm[src])
+    assert n > 0 and not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", SOURCES)
 def test_transcendental_results_waited_for(asm, src):
     bad, n = isa_scan.trans_result_use(asm[src])
     assert n > 0 and not bad, bad[:5]
