@@ -11,12 +11,17 @@
 //    the MLA op of the Modular MAX page, which streams K through 32x32x64 fp8
 //    fragments).  The per-tensor dequantisation factors of Q and K are folded
 //    into the softmax scale; the one of V is applied in the epilogue.
-//  * P V runs in bf16: V fragments come out of LDS transposed with
-//    ds_read_b64_tr_b8 (eight keys of one value column per lane, the 8-bit
-//    transposed read the same page uses for its V fragments) and are widened
-//    exactly to bf16; P is rounded to bf16 (relative error <= 2^-9 instead of
-//    the 2^-4 of fp8, which would put short causal rows near the accuracy
-//    bound), and the row sum is taken over those rounded values.
+//  * P V runs at the fp8 rate on the blocks every row of the workgroup sees
+//    whole: P is rounded to e4m3 (relative error <= 2^-4 per value) and meets
+//    the V^T fragments as they come out of LDS, 32 keys per lane from four
+//    ds_read_b64_tr_b8 reads (eight keys of one value column each, the 8-bit
+//    transposed read the same page uses for its V fragments), in one
+//    32x32x64 fp8 MFMA per value tile and block; the row sum is taken over
+//    the unrounded fp32 P.  Masked blocks (the causal diagonal, the ragged
+//    tail, the last block) run P V in bf16 instead, V widened exactly from
+//    fp8 and P rounded to bf16 (relative error <= 2^-9) with the row sum over
+//    the rounded values, so rows with few visible keys, whose output is an
+//    average of few P values, keep the finer rounding.
 //  * K rows are 192 bytes, so each K block is kept in LDS as a 128-byte part
 //    (dims 0..127) and a 64-byte part (dims 128..191), each with a
 //    power-of-two swizzle that keeps the fragment reads free of bank
@@ -260,31 +265,48 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     return MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
   };
 
-  // Softmax part 2: P = 2^(s2*S - m), rounded to bf16 as the PV B operand;
-  // the row sum is taken over the rounded values.
-  auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], auto masked_tag)
+  // Softmax part 2: P = 2^(s2*S - m).  Masked blocks: rounded to bf16, four
+  // dwords per 16-key chunk c (the B operand of the bf16 P V), row sum over
+  // the rounded values.  Unmasked blocks: rounded to e4m3, eight dwords for
+  // the 64 keys of the block (the B operand of the fp8 P V): dword 4t + r/4
+  // holds registers r..r+3 (r % 4 == 0) of score tile t, i.e. bytes 4(r/4%2)..
+  // of chunk 2t + r/8, the key order of the transposed V reads; row sum over
+  // the unrounded values.
+  auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], i32x8_t& pf8, auto masked_tag)
       __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0, p1;
-        if constexpr (MASKED) {
-          p0 = fast_exp2(sc[t][r] - m_sub);
-          p1 = fast_exp2(sc[t][r + 1] - m_sub);
-        } else {
-          p0 = fast_exp2(fmaf(sc[t][r], s2, -m_sub));
-          p1 = fast_exp2(fmaf(sc[t][r + 1], s2, -m_sub));
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(sc[t][r] - m_sub);
+          const float p1 = fast_exp2(sc[t][r + 1] - m_sub);
+          const uint32_t pk = pack2<Bf16>(p0, p1);
+          pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
+          l_run = add_pair<Bf16>(pk, l_run);
         }
-        const uint32_t pk = pack2<Bf16>(p0, p1);
-        pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
-        l_run = add_pair<Bf16>(pk, l_run);
-      }
+    } else {
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const float p0 = fast_exp2(fmaf(sc[t][r], s2, -m_sub));
+          const float p1 = fast_exp2(fmaf(sc[t][r + 1], s2, -m_sub));
+          const float p2 = fast_exp2(fmaf(sc[t][r + 2], s2, -m_sub));
+          const float p3 = fast_exp2(fmaf(sc[t][r + 3], s2, -m_sub));
+          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          pf8[4 * t + r / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+          la += p0 + p1;
+          lb += p2 + p3;
+        }
+      l_run += la + lb;
+    }
   };
 
-  // GEMM 2 (bf16): O^T += V^T P^T from V buffer VB, V widened from fp8 after
-  // the transposed read
+  // GEMM 2, masked blocks (bf16): O^T += V^T P^T from V buffer VB, V widened
+  // from fp8 after the transposed read
   auto pv = [&](auto vb_tag, const u32x4_t (&pf)[4]) __attribute__((always_inline)) {
     constexpr uint32_t VB = decltype(vb_tag)::value;
 #pragma unroll
@@ -296,6 +318,23 @@ void prefill_fp8_kernel(const PrefillArgs a) {
         const u32x4_t vf = {lo.x, lo.y, hi.x, hi.y};
         acc[t] = mfma32x32x16<Bf16>(vf, pf[c], acc[t]);
       }
+  };
+  // GEMM 2, unmasked blocks (fp8): one 32x32x64 MFMA per value tile over the
+  // whole block; the V^T fragment is the four transposed reads of chunks
+  // 0..3 (eight keys each, in the byte order of P's packing above)
+  auto pv_fp8 = [&](auto vb_tag, const i32x8_t& pf8) __attribute__((always_inline)) {
+    constexpr uint32_t VB = decltype(vb_tag)::value;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      i32x8_t vf;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x2_t v8 = lds_read_tr8(v_off[t] + VB + (16 * c) * VROW);
+        vf[2 * c] = (int)v8.x;
+        vf[2 * c + 1] = (int)v8.y;
+      }
+      acc[t] = mfma32x32x64_fp8(vf, pf8, acc[t]);
+    }
   };
 
   // One pipeline iteration j (PAR = j & 1): the scores of block j are in
@@ -324,11 +363,13 @@ void prefill_fp8_kernel(const PrefillArgs a) {
       wait_vmcnt<0>();
     }
     __syncthreads();
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const float m_sub = softmax_max(j, s_cur, masked_tag);
     u32x4_t pf[4];
+    i32x8_t pf8;
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) qk(std::integral_constant<uint32_t, KB_NEXT>{}, s_nxt);
-    softmax_exp(s_cur, m_sub, pf, masked_tag);
+    softmax_exp(s_cur, m_sub, pf, pf8, masked_tag);
     if constexpr (NEXT) {
       // per QK MFMA (64 cycles on the matrix core): its two K reads and a
       // share of the exponentials
@@ -336,11 +377,14 @@ void prefill_fp8_kernel(const PrefillArgs a) {
       for (int i = 0; i < 6; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // fourteen VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 14 : 20, 0);  // VALU
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
+    if constexpr (MASKED)
+      pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
+    else
+      pv_fp8(std::integral_constant<uint32_t, VB_CUR>{}, pf8);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) __syncthreads();  // this iteration's buffers are refilled next
   };
