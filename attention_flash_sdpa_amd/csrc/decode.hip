@@ -183,10 +183,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
         };
 #pragma unroll
         for (int i = 0; i < K_INSTR; ++i)
-          global_to_lds_16(addr(kbase, min(krow[i], lim), kstride, kcol[i]), kl + i * 1024);
+          global_to_lds_16_nt(addr(kbase, min(krow[i], lim), kstride, kcol[i]), kl + i * 1024);
 #pragma unroll
         for (int i = 0; i < V_INSTR; ++i)
-          global_to_lds_16(addr(vbase, min(vrow[i], lim), vstride, vcol[i]), vl + i * 1024);
+          global_to_lds_16_nt(addr(vbase, min(vrow[i], lim), vstride, vcol[i]), vl + i * 1024);
         return;
       }
       int phys = __builtin_amdgcn_readlane(pt_vals, pt_page - pt_first);
@@ -205,10 +205,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     const char* vb = vbase + row0 * vstride;
 #pragma unroll
     for (int i = 0; i < K_INSTR; ++i)
-      global_to_lds_16(kb + (size_t)min(krow[i], lim) * kstride + kcol[i], kl + i * 1024);
+      global_to_lds_16_nt(kb + (size_t)min(krow[i], lim) * kstride + kcol[i], kl + i * 1024);
 #pragma unroll
     for (int i = 0; i < V_INSTR; ++i)
-      global_to_lds_16(vb + (size_t)min(vrow[i], lim) * vstride + vcol[i], vl + i * 1024);
+      global_to_lds_16_nt(vb + (size_t)min(vrow[i], lim) * vstride + vcol[i], vl + i * 1024);
   };
 
   // K fragment (A operand of 16x16x32): key row 16t + l%16, slot 4s + l/16

@@ -293,6 +293,12 @@ __device__ __forceinline__ void global_to_lds_16(const void* gptr, uint32_t lds_
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
+// As global_to_lds_16 with the non-temporal hint: for data read once (the
+// decode's stream of K/V), which then does not displace reused lines.
+__device__ __forceinline__ void global_to_lds_16_nt(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+
 // As global_to_lds_16 with a wavefront-uniform 64-bit base in SGPRs and a
 // per-lane 32-bit byte offset (no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void global_to_lds_16_sbase(const void* sbase, uint32_t voffset, uint32_t lds_base) {
