@@ -25,7 +25,7 @@ EXPORTS = (
     "sdpa_abi_version", "sdpa_status_string", "sdpa_last_error", "sdpa_plan",
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
     "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_prefill_masked_fwd",
-    "sdpa_loop_counts", "sdpa_set_prefill_variant", "sdpa_decode_fwd_noalloc",
+    "sdpa_loop_counts", "sdpa_set_prefill_variant", "sdpa_decode_fwd_noalloc", "sdpa_hbm_read_probe",
 )
 
 
@@ -99,6 +99,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_prefill_masked_fwd.argtypes = [P, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, vp, vp,
                                             vp]
     lib.sdpa_mask_convert.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
+    lib.sdpa_hbm_read_probe.restype = ctypes.c_int
+    lib.sdpa_hbm_read_probe.argtypes = [vp, ctypes.c_int64, vp, vp]
     lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
     lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
@@ -425,6 +427,26 @@ def mask_convert(mask, *, out_dtype=None, out=None, stream=None):
     _check_output("out", out, tuple(mask.shape), (torch.float16, torch.bfloat16), mask.device)
     _check(load().sdpa_mask_convert(_ptr(mask), _ptr(out), mask.numel(), _dtype_code(out), _stream_handle(stream)))
     return out
+
+
+def hbm_read_probe(data, *, sink=None, stream=None):
+    """Measurement helper (``sdpa_hbm_read_probe``): reads every byte of the
+    contiguous device tensor ``data`` once; its time gives the streaming-read
+    rate.  ``sink`` is a uint32-compatible device tensor of 2048 elements
+    (allocated if None), returned."""
+    import torch
+
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous device tensor")
+    nbytes = data.numel() * data.element_size()
+    if nbytes % 16:
+        raise ValueError(f"data must hold a multiple of 16 bytes (got {nbytes})")
+    if sink is None:
+        sink = torch.empty(2048, dtype=torch.int32, device=data.device)
+    _require(sink.is_cuda and sink.is_contiguous() and sink.element_size() == 4 and sink.numel() >= 2048,
+             "sink must be a contiguous 4-byte device tensor of at least 2048 elements")
+    _check(load().sdpa_hbm_read_probe(_ptr(data), nbytes, _ptr(sink), _stream_handle(stream)))
+    return sink
 
 
 def prefill_masked(q, k, v, mask, *, scale=None, causal=False, out=None, lse=None, stream=None):

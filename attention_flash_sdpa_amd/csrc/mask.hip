@@ -71,6 +71,35 @@ __global__ __launch_bounds__(256) void mask_convert_kernel(const uint8_t* __rest
   }
 }
 
+// Streaming-read probe: every 16-byte chunk of the buffer is loaded once with
+// the non-temporal hint, four loads in flight per thread, grid-stride over a
+// fixed grid; the words are folded by XOR and the fold is written only when
+// it equals a constant no measured buffer is filled to produce, so the
+// kernel's HBM traffic is its reads.
+__global__ __launch_bounds__(256) void hbm_read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16,
+                                                              uint32_t* __restrict__ sink) {
+  constexpr int U = 4;
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += stride) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+int launch_hbm_read_probe(const void* data, int64_t bytes, uint32_t* sink, ihipStream_t* stream) {
+  hipLaunchKernelGGL(hbm_read_probe_kernel, dim3(kProbeGroups), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4_t*)data, bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
 int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream) {
   // -inf: binary16 0xfc00, bfloat16 0xff80
   const uint32_t neg = out_dtype == SDPA_F16 ? 0xfc00u : 0xff80u;

@@ -275,6 +275,24 @@ sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32
   return hip_status(launch_mask_convert(mask, out, n, out_dtype, (ihipStream_t*)stream), "mask conversion launch");
 }
 
+sdpa_status_t sdpa_hbm_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream) {
+  clear_error();
+  if (bytes < 0 || bytes % 16 != 0) {
+    set_error("bytes must be a non-negative multiple of 16 (got %lld)", (long long)bytes);
+    return SDPA_ERR_BAD_SHAPE;
+  }
+  if (bytes == 0) return SDPA_OK;
+  if (data == nullptr || sink == nullptr) {
+    set_error("data and sink must not be NULL");
+    return SDPA_ERR_NULL_PTR;
+  }
+  if (!aligned16(data) || ((uintptr_t)sink & 3) != 0) {
+    set_error("data must be 16-byte and sink 4-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  return hip_status(launch_hbm_read_probe(data, bytes, sink, (ihipStream_t*)stream), "read probe launch");
+}
+
 sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
                                       const void* mask, int64_t mask_stride_b, int64_t mask_stride_h,
                                       int32_t mask_stride_row, void* o, float* lse, void* stream) {

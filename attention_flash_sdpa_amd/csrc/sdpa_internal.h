@@ -108,6 +108,9 @@ int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream);
+// HBM streaming-read probe (mask.hip): kProbeGroups workgroups
+constexpr int kProbeGroups = 2048;
+int launch_hbm_read_probe(const void* data, int64_t bytes, uint32_t* sink, ihipStream_t* stream);
 
 // prefill with a full additive mask (one wave per 16 query rows of one head)
 struct MaskedArgs {

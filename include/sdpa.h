@@ -237,6 +237,18 @@ sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void*
 sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32_t out_dtype,
                                 void* stream);
 
+/* Measurement helper, not part of the attention computation: the HBM
+ * streaming-read rate that bounds the split-KV decode.  Loads every byte of
+ * data once (16-byte non-temporal loads, a fixed grid of 2048 workgroups of
+ * 256 threads) and folds it by XOR; a workgroup writes its fold to
+ * sink[workgroup] only in the unlikely case that it equals 0x9e3779b9, so
+ * timed over a buffer its traffic is the read of `bytes`.
+ *   data  : device, 16-byte aligned, `bytes` readable bytes
+ *   bytes : a multiple of 16 (0: no-op)
+ *   sink  : device uint32 [2048], may be written
+ * Enqueued on `stream`; nothing synchronises. */
+sdpa_status_t sdpa_hbm_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Prefill with a full additive mask: O = softmax(Q K^T * scale + mask) V,
  * the mainloop's optional full mask ("Xe SDPA Forward Mainloop", section
  * "Runtime args / params") added to every score in its mask step (section

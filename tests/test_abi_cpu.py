@@ -322,6 +322,24 @@ def test_mask_convert_argument_errors_before_any_launch():
     assert lib.sdpa_mask_convert(null, null, 0, sdpa.F16, null) == 0      # empty: a no-op
 
 
+def test_hbm_read_probe_argument_errors_before_any_launch():
+    import ctypes
+
+    import torch
+
+    lib = sdpa.load()
+    a, null = ctypes.c_void_p(0x1000), ctypes.c_void_p(0)
+    assert lib.sdpa_hbm_read_probe(a, -16, a, null) == 2
+    assert lib.sdpa_hbm_read_probe(a, 24, a, null) == 2                 # not a multiple of 16
+    assert lib.sdpa_hbm_read_probe(null, 16, a, null) == 1
+    assert lib.sdpa_hbm_read_probe(a, 16, null, null) == 1
+    assert lib.sdpa_hbm_read_probe(ctypes.c_void_p(0x1008), 16, a, null) == 5
+    assert lib.sdpa_hbm_read_probe(a, 16, ctypes.c_void_p(0x1002), null) == 5
+    assert lib.sdpa_hbm_read_probe(null, 0, null, null) == 0            # empty: a no-op
+    with pytest.raises(ValueError):
+        sdpa.hbm_read_probe(torch.zeros(16))                            # host tensor
+
+
 def test_masked_prefill_argument_errors_before_any_launch():
     import ctypes
 

@@ -53,3 +53,16 @@ def test_mask_convert_bool_input_and_empty(dev):
     assert np.array_equal(_bits(out), om.mask_convert(m.numpy().astype(np.uint8), "f16").view(np.uint16))
     e = sdpa.mask_convert(torch.zeros(0, dtype=torch.bool, device=dev))
     assert e.numel() == 0
+
+
+def test_hbm_read_probe_reads_without_writing(dev):
+    # the probe's only store is guarded by a fold value random data does not
+    # produce: the sink keeps its fill, and the stream stays usable
+    print("hbm_read_probe 64 MiB", flush=True)
+    g = torch.Generator().manual_seed(3)
+    data = torch.randint(-2**31, 2**31 - 1, (16 * 1024 * 1024,), generator=g, dtype=torch.int32).to(dev)
+    sink = torch.full((2048,), 7, dtype=torch.int32, device=dev)
+    sdpa.hbm_read_probe(data, sink=sink)
+    sdpa.hbm_read_probe(data[:4], sink=sink)                # 16 bytes: one partial workgroup
+    torch.cuda.synchronize()
+    assert bool((sink == 7).all())
