@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsdpa_mi355x.so")
 SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_cached.hip", "prefill_o2.hip",
-           "prefill_fp8.hip", "decode.hip", "mask.hip", "masked.hip"]
+           "prefill_fp8.hip", "decode.hip", "mask.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -19,6 +19,14 @@
 //    ("xe2-sdp-kernels", section "Assets", two-phase decode), which gives
 //    every SIMD two waves where the one-range grid would give it one.
 //
+// The masked prefill runs the first shape with the full additive mask of
+// the mainloop's optional mask argument ("Xe SDPA Forward Mainloop",
+// section "Runtime args / params"), added to every score in the mask step
+// (section "Compact shape table", row "Mask"): each lane loads the bias of
+// its own scores (its query row, 4 keys per 8-byte load) straight into
+// registers one block ahead, and the softmax forms scale*S + bias before the
+// row max; causal and ragged limits apply on top in the masked blocks.
+//
 // Software pipeline: iteration j issues the QK MFMAs of block j+1 before the
 // softmax of block j is finished, then runs the PV MFMAs of block j; K(j+2)
 // and V(j+1) are loaded during iteration j.  Buffer parity is a compile-time
@@ -48,6 +56,28 @@ int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal,
     case kSplitBf16D64: return launch_o2_t<Bf16, 64, 8, 4, 32>(a, causal, stream);
     case kSplitF16D128: return launch_o2_t<F16, 128, 8, 4, 32>(a, causal, stream);
     case kSplitBf16D128: return launch_o2_t<Bf16, 128, 8, 4, 32>(a, causal, stream);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+template <class T, int D>
+static int launch_o2_bias_t(const PrefillArgs& a, int causal, ihipStream_t* stream) {
+  dim3 grid(a.num_groups), block(64 * 4);
+  if (causal)
+    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, true, 4, 1, 64, false, true>), grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((prefill_o2_kernel<T, D, D, false, 4, 1, 64, false, true>), grid, block, 0, (hipStream_t)stream,
+                       a);
+  return (int)hipGetLastError();
+}
+
+// The masked prefill: the one-range, four-wave shape with the additive bias.
+int launch_prefill_o2_bias(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
+  switch (plan.kernel) {
+    case kOccF16D64: return launch_o2_bias_t<F16, 64>(a, causal, stream);
+    case kOccBf16D64: return launch_o2_bias_t<Bf16, 64>(a, causal, stream);
+    case kOccF16D128: return launch_o2_bias_t<F16, 128>(a, causal, stream);
+    case kOccBf16D128: return launch_o2_bias_t<Bf16, 128>(a, causal, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -1,7 +1,8 @@
 // prefill_o2_kernel.h -- the 32-row prefill mainloop in its two-waves-per-SIMD
-// form (prefill_o2_kernel<T, D, DV, CAUSAL, NW, KS, BK, CACHED>), included
-// by prefill_o2.hip (dense keys) and prefill_cached.hip (cached prefix + new
-// keys).  The design is described at the top of prefill_o2.hip.
+// form (prefill_o2_kernel<T, D, DV, CAUSAL, NW, KS, BK, CACHED, BIAS>),
+// included by prefill_o2.hip (dense keys, and with BIAS the full additive
+// mask) and prefill_cached.hip (cached prefix + new keys).  The design is
+// described at the top of prefill_o2.hip.
 #pragma once
 
 #include <math.h>
@@ -14,7 +15,7 @@
 
 namespace sdpa {
 
-template <class T, int D, int DV, bool CAUSAL, int NW, int KS, int BKT, bool CACHED>
+template <class T, int D, int DV, bool CAUSAL, int NW, int KS, int BKT, bool CACHED, bool BIAS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_o2_kernel(const PrefillArgs a) {
   constexpr int BK = BKT;                     // keys per block
@@ -29,6 +30,8 @@ void prefill_o2_kernel(const PrefillArgs a) {
   constexpr int NT = DV / 32;                    // O^T accumulator tiles
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "block too small for the fill");
   static_assert(NW % KS == 0 && (BK == 32 || BK == 64), "shape");
+  static_assert(!BIAS || (KS == 1 && !CACHED), "the bias form streams one dense key range");
+  constexpr int ML = BIAS ? NTL * 4 : 0;         // 8-byte bias loads per lane per block
   // LDS per key range: K buffers 0/1, then V buffers 0/1
   constexpr uint32_t KBUF0 = 0, KBUF1 = KBYTES;
   constexpr uint32_t VBUF0 = 2 * KBYTES, VBUF1 = 2 * KBYTES + VBYTES;
@@ -106,6 +109,32 @@ void prefill_o2_kernel(const PrefillArgs a) {
         global_load_16_untracked<32 * S>(qf[S], qptr);
     });
   }
+
+  // ---- additive bias (BIAS): the values of this lane's scores, straight from
+  // memory into registers one block ahead.  Register r of score tile t holds
+  // key kb*BK + 32t + 8(r/4) + 4*hl + r%4, so load c of tile t brings the four
+  // keys from kb*BK + 32t + 8c + 4*hl (8 bytes) of row qrow (clamped to the
+  // last row); the start is clamped to the row's last four elements, which
+  // only moves the loads of keys past kv_len (masked anyway) and keeps every
+  // read inside the row.  One register set: iteration j reads block j's
+  // values, then loads block j+1's into the same registers, which the
+  // next iteration's K/V wait covers (the compiler does not count these
+  // loads; an ISA scan checks that nothing touches the registers before it).
+  const elem_t* mrow = nullptr;
+  if constexpr (BIAS)
+    mrow = (const elem_t*)a.mask + (size_t)b * a.mask_sb + (size_t)h * a.mask_sh +
+           (size_t)min(qrow, Sq - 1) * a.mask_row + 4 * hl;
+  u32x2_t mv[BIAS ? NTL * 4 : 1];
+  auto load_bias = [&](int kb, u32x2_t (&m)[BIAS ? NTL * 4 : 1]) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          global_load_8_untracked(m[4 * t + c], mrow + min(kb * BK + 32 * t + 8 * c, a.mask_row - 4 - 4 * hl));
+    }
+  };
+  const float s_nat = a.s_nat;
 
   // ---- direct global -> LDS fills ------------------------------------------
   // Instruction i of this wave covers the 64 16-byte slots starting at slot
@@ -281,10 +310,32 @@ void prefill_o2_kernel(const PrefillArgs a) {
 
   // Softmax part 1: mask (tail blocks only), block row max, lazy rescale.
   // Returns the subtrahend m of P = 2^(s2*S - m).
-  auto softmax_max = [&](int kb, f32x16_t (&sc)[NTL], auto masked_tag) __attribute__((always_inline)) -> float {
+  auto softmax_max = [&](int kb, f32x16_t (&sc)[NTL], const u32x2_t (&mv)[BIAS ? NTL * 4 : 1], auto masked_tag)
+      __attribute__((always_inline)) -> float {
     constexpr bool MASKED = decltype(masked_tag)::value;
     float bmax;
-    if constexpr (MASKED) {
+    if constexpr (BIAS) {
+      // scores become scale*S + bias (natural-log domain) in place; the block
+      // max is taken there and moved to the log2 domain of the running max
+      const int lim = MASKED ? (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl) : 0;
+      bmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t w = (r & 2) ? mv[4 * t + (r >> 2)].y : mv[4 * t + (r >> 2)].x;
+          float bias;
+          if constexpr (T::is_bf16)
+            bias = __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+          else
+            bias = (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (w >> 16) : (w & 0xffffu)));
+          float x = fmaf(sc[t][r], s_nat, bias);
+          if constexpr (MASKED) x = (32 * t + 8 * (r >> 2) + (r & 3)) <= lim ? x : -INFINITY;
+          sc[t][r] = x;
+          bmax = fmaxf(bmax, x);
+        }
+      bmax *= kLog2e;
+    } else if constexpr (MASKED) {
       // register r of tile t holds key kb*BK + 4*hl + 32t + 8(r/4) + r%4; it is
       // visible iff that key <= the row's last visible key
       const int lim = (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl);
@@ -313,7 +364,8 @@ void prefill_o2_kernel(const PrefillArgs a) {
     const float m_new = fmaxf(m_run, bmax);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kSlack)) {
       // rows that have seen no visible key keep m = -inf (masked blocks only)
-      const float m_tgt = MASKED ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
+      // (with a bias, any block: a bias of -inf can remove every key of a row)
+      const float m_tgt = MASKED || BIAS ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
       const float alpha = fast_exp2(m_run - m_tgt);
       l_run *= alpha;
 #pragma unroll
@@ -322,7 +374,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
         for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
       m_run = m_new;
     }
-    return MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+    return MASKED || BIAS ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
   };
 
   // Softmax part 2: P = 2^(s2*S - m) packed to 16 bits as the PV B operand;
@@ -335,7 +387,10 @@ void prefill_o2_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0, p1;
-        if constexpr (MASKED) {
+        if constexpr (BIAS) {  // scores in the natural-log domain
+          p0 = fast_exp2(fmaf(sc[t][r], kLog2e, -m_sub));
+          p1 = fast_exp2(fmaf(sc[t][r + 1], kLog2e, -m_sub));
+        } else if constexpr (MASKED) {
           p0 = fast_exp2(sc[t][r] - m_sub);
           p1 = fast_exp2(sc[t][r + 1] - m_sub);
         } else {
@@ -380,15 +435,17 @@ void prefill_o2_kernel(const PrefillArgs a) {
       fill_v(kb0 + j + 1, VB_FREE);
       if (j + 2 < cnt) {
         fill_k(kb0 + j + 2, KB_FREE);
-        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) have landed
+        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) (and the bias of block j) have landed
       } else {
         wait_vmcnt<V_INSTR>();
       }
     } else {
       wait_vmcnt<0>();
     }
+    if constexpr (BIAS) pin_regs(mv);
     __syncthreads();
-    const float m_sub = softmax_max(kb0 + j, s_cur, masked_tag);
+    const float m_sub = softmax_max(kb0 + j, s_cur, mv, masked_tag);
+    if constexpr (BIAS && NEXT) load_bias(kb0 + j + 1, mv);
     u32x4_t pf[NCH];
     // Phase fence, then the QK MFMAs of block j+1 interleaved with the
     // exponentials of block j: after each K fragment read and MFMA the wave
@@ -435,10 +492,11 @@ void prefill_o2_kernel(const PrefillArgs a) {
   fill_k(kb0, KBUF0);
   fill_v(kb0, VBUF0);
   fill_k(kb0 + min(1, cnt - 1), KBUF1);
+  load_bias(kb0, mv);  // waited for by the first iteration
   if constexpr (CACHED)
     wait_vmcnt<K_INSTR + V_INSTR>();
   else
-    wait_vmcnt_pin<K_INSTR + V_INSTR>(qf);
+    wait_vmcnt_pin<K_INSTR + V_INSTR + ML>(qf);
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = row_ok ? qf[s] : u32x4_t{0, 0, 0, 0};
   __syncthreads();

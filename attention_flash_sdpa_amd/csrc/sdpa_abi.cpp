@@ -319,12 +319,10 @@ sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void*
               mask_stride_row, p.kv_len);
     return SDPA_ERR_BAD_SHAPE;
   }
-  const int64_t rows_per_group = 16 * kMaskedRowTiles * kMaskedWaves;
-  const int64_t row_tiles = ((int64_t)p.q_len + rows_per_group - 1) / rows_per_group;
-  if ((int64_t)p.batch * p.head_q * row_tiles >= ((int64_t)1 << 31)) {
-    set_error("grid too large (%lld workgroups)", (long long)((int64_t)p.batch * p.head_q * row_tiles));
-    return SDPA_ERR_BAD_SHAPE;
-  }
+  // the two-waves-per-SIMD shape (one key range, 64-key blocks, four waves)
+  // with the bias added in its softmax
+  st = make_plan(p, false, device_cus(), 0, &plan, 5);
+  if (st != SDPA_OK) return st;
   if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
   if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr || mask == nullptr))) {
     set_error("q, k, v, mask and o must not be NULL");
@@ -335,11 +333,10 @@ sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void*
     set_error("q, k, v, mask, o must be 16-byte aligned and lse 4-byte aligned");
     return SDPA_ERR_MISALIGNED;
   }
-  MaskedArgs a{};
+  PrefillArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
-  a.mask = mask;
   a.o = o;
   a.lse = lse;
   a.batch = p.batch;
@@ -348,13 +345,19 @@ sdpa_status_t sdpa_prefill_masked_fwd(const sdpa_problem_t* problem, const void*
   a.head_q = p.head_q;
   a.head_kv = p.head_kv;
   a.group = p.head_q / p.head_kv;
+  a.heads_per_group = plan.heads_per_group;
+  a.qtiles_per_group = plan.qtiles_per_group;
+  a.q_tiles = plan.q_tiles;
+  a.head_groups = (a.group + plan.heads_per_group - 1) / plan.heads_per_group;
+  a.num_groups = plan.num_groups;
+  a.s2 = (float)((double)p.scale * 1.4426950408889634);
+  a.s_nat = p.scale;
+  a.v_descale = 1.f;
+  a.mask = mask;
   a.mask_sb = mask_stride_b;
   a.mask_sh = mask_stride_h;
   a.mask_row = mask_stride_row;
-  a.row_tiles = (int32_t)row_tiles;
-  a.s2 = (float)((double)p.scale * 1.4426950408889634);
-  return hip_status(launch_prefill_masked(a, p.in_dtype, p.d_qk, p.causal != 0, (ihipStream_t*)stream),
-                    "masked prefill launch");
+  return hip_status(launch_prefill_o2_bias(a, plan, p.causal != 0, (ihipStream_t*)stream), "masked prefill launch");
 }
 
 // Shared by the dense and the paged decode entry points; cache rows per

@@ -320,6 +320,12 @@ __device__ __forceinline__ void global_load_16_untracked(u32x4_t& d, const void*
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=&v"(d) : "v"(p), "i"(OFF) : "memory");
 }
 
+// 8-byte global load into a VGPR pair, untracked like global_load_16_untracked
+// (read only after an explicit wait and pin_regs / wait_vmcnt_pin).
+__device__ __forceinline__ void global_load_8_untracked(u32x2_t& d, const void* p) {
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(d) : "v"(p) : "memory");
+}
+
 // As global_to_lds_16_off with a per-lane 64-bit address (the lane's address
 // less OFF) instead of a scalar base: used where the lanes of one load read
 // from different tensors.  A vector address carries no SGPR hazard, so only
@@ -380,10 +386,18 @@ __device__ __forceinline__ void global_to_lds_16_off(const void* sbase, uint32_t
 // Waits until at most N vector-memory operations of this wave are in flight,
 // then marks the registers of d as written here, so no use of them can be
 // scheduled before the wait.
-template <int N, int K>
-__device__ __forceinline__ void wait_vmcnt_pin(u32x4_t (&d)[K]) {
+template <int N, int K, class V>
+__device__ __forceinline__ void wait_vmcnt_pin(V (&d)[K]) {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+#pragma unroll
+  for (int k = 0; k < K; ++k) asm volatile("" : "+v"(d[k]));
+}
+
+// Marks the registers of d as written here (after an explicit wait that
+// covers their untracked loads), so no use of them moves above it.
+template <int K, class V>
+__device__ __forceinline__ void pin_regs(V (&d)[K]) {
 #pragma unroll
   for (int k = 0; k < K; ++k) asm volatile("" : "+v"(d[k]));
 }

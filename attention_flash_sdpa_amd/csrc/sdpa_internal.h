@@ -43,9 +43,6 @@ constexpr int kLdsPerCu = 160 * 1024;  // LDS bytes per CU (gfx950)
 constexpr int kCombineRows = 4;    // decode combine: (batch, query head) rows per workgroup
 constexpr int kDecodeMaxGroup = 16;  // decode: query heads per wave (MFMA N); larger groups take several waves
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
-constexpr int kMaskedWaves = 4;    // masked prefill: waves per workgroup
-constexpr int kMaskedRowTiles = 4; // masked prefill: 16-row tiles per wave
-constexpr int kMaskedBlockK = 32;  // masked prefill: keys per K/V/mask block
 constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
 
@@ -81,6 +78,13 @@ struct PrefillArgs {
   const void* k_cache;
   const void* v_cache;
   int32_t cache_len, cache_cap;
+  // additive bias (the masked prefill; NULL otherwise): the value for (b, h,
+  // row i, key j) is mask[b*mask_sb + h*mask_sh + i*mask_row + j] in the
+  // inputs' 16-bit type; mask_row is a multiple of 8 and >= max(kv_len, 8)
+  const void* mask;
+  int64_t mask_sb, mask_sh;
+  int32_t mask_row;
+  float s_nat;      // the softmax scale itself (natural-log domain)
 };
 
 struct DecodeArgs {
@@ -106,27 +110,14 @@ struct DecodeArgs {
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_fp8(const PrefillArgs& a, int causal, ihipStream_t* stream);
 int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+// the two-waves-per-SIMD kernel with the additive bias a.mask (masked prefill)
+int launch_prefill_o2_bias(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream);
 // HBM streaming-read probe (mask.hip): kProbeGroups workgroups
 constexpr int kProbeGroups = 2048;
 int launch_hbm_read_probe(const void* data, int64_t bytes, uint32_t* sink, ihipStream_t* stream);
 
-// prefill with a full additive mask (one wave per 16 query rows of one head)
-struct MaskedArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* mask;   // [.., q_len, mask_row] additive, the inputs' 16-bit type
-  void* o;
-  float* lse;
-  int32_t batch, q_len, kv_len, head_q, head_kv, group;
-  int64_t mask_sb, mask_sh;  // element strides of the mask's batch and head (0: broadcast)
-  int32_t mask_row;          // element stride between mask rows (multiple of 8, >= max(kv_len, 8))
-  int32_t row_tiles;         // workgroups per (batch, head): ceil(q_len / (16 * tiles * waves))
-  float s2;                  // scale * log2(e)
-};
-int launch_prefill_masked(const MaskedArgs& a, int in_dtype, int d, int causal, ihipStream_t* stream);
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
 
 // The no-allocation decode keeps its split partials in a static device array

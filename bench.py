@@ -174,7 +174,7 @@ _SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "pr
                         "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
             "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"],
             "fp8": ["prefill_fp8.hip", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
-            "masked": ["masked.hip", "sdpa_device.h", "sdpa_internal.h"],
+            "masked": ["prefill_o2.hip", "prefill_o2_kernel.h", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
             "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"]}
 def _cached_chunk():
     from attention_flash_sdpa_amd import inputs
@@ -197,6 +197,8 @@ def _masked_workload():
 
 
 MASKED = _masked_workload()
+# the masked prefill runs the two-waves-per-SIMD kernel with the bias form on
+MASKED_KERNEL = "prefill_o2_kernel<sdpa::Bf16, 128, 128, false, 4, 1, 64, false, true>"
 CACHED_LEN = 3584
 
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
@@ -307,8 +309,7 @@ def _sq_profiles():
             out.append((f"{fam}_{wname}", kname, grid, src, wname))
     for kname, grid in _kernels_of(sdpa, CACHED_CHUNK, cached=True):
         out.append((f"{kname.split('<')[0]}_{CACHED_CHUNK.name}", kname, grid, _SOURCES["prefill"], CACHED_CHUNK.name))
-    out.append((f"prefill_masked_kernel_{MASKED.name}", "prefill_masked_kernel<sdpa::Bf16, 128, 128, false>", None,
-                _SOURCES["masked"], MASKED.name))
+    out.append((f"prefill_o2_kernel_{MASKED.name}", MASKED_KERNEL, None, _SOURCES["masked"], MASKED.name))
     return out
 
 
@@ -383,7 +384,7 @@ def _summarize_trace(d):
         if paged == "mask":
             kernels = [("mask_convert_kernel", None)]
         elif paged == "masked":
-            kernels = [("prefill_masked_kernel<sdpa::Bf16, 128, 128, false>", None)]
+            kernels = [(MASKED_KERNEL, None)]
         else:
             kernels = _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached")
         for kname, grid in kernels:

@@ -81,10 +81,83 @@ class _Program:
             else:
                 nxt = [i + 1]
             self.succ.append([j for j in nxt if j < n])
+        self._prune_constant_vcc_branches(labels)
         self.pred = [[] for _ in range(n)]
         for i, nxt in enumerate(self.succ):
             for j in nxt:
                 self.pred[j].append(i)
+
+    def _prune_constant_vcc_branches(self, labels):
+        """The compiler's if/else flow blocks set a 64-bit SGPR to -1 or 0
+        (s_mov_b64), derive VCC from it (s_andn2_b64 vcc, exec, X) and branch
+        on VCC.  A forward constant propagation of those SGPRs over the
+        control-flow graph finds where X is -1 on every path, so VCC is 0 and
+        the branch can go one way only; the other edge is dropped."""
+        n = len(self.ins)
+        tracked = {_operands(t)[2] for t in self.ins
+                   if t.startswith("s_andn2_b64") and _operands(t)[:2] == ["vcc", "exec"]}
+        if not tracked:
+            return
+        UNK = object()
+
+        def transfer(state, t):
+            ops = _operands(t)
+            if not ops:
+                return state
+            d = ops[0]
+            if t.startswith("s_mov_b64") and d in tracked and ops[1] in ("-1", "0"):
+                state = dict(state)
+                state[d] = int(ops[1])
+                return state
+            written = _sregs(d)
+            hit = [r for r in state if _sregs(r) & written]
+            if hit:
+                state = dict(state)
+                for r in hit:
+                    state[r] = UNK
+            return state
+
+        # every instruction without a predecessor starts a function: no
+        # constant known there
+        has_pred = [False] * n
+        for nxt in self.succ:
+            for j in nxt:
+                has_pred[j] = True
+        ins_state = [None] * n
+        work = []
+        for i in range(n):
+            if not has_pred[i]:
+                ins_state[i] = {}
+                work.append(i)
+        while work:
+            i = work.pop()
+            out = transfer(ins_state[i], self.ins[i])
+            for j in self.succ[i]:
+                cur = ins_state[j]
+                if cur is None:
+                    new = dict(out)
+                else:
+                    new = {r: (v if cur.get(r, UNK) == v and r in cur else UNK) for r, v in out.items()}
+                    for r in cur:
+                        if r not in out:
+                            new[r] = UNK
+                if new != cur:
+                    ins_state[j] = new
+                    work.append(j)
+        for i, t in enumerate(self.ins):
+            if not t.startswith(("s_cbranch_vccz", "s_cbranch_vccnz")) or i == 0:
+                continue
+            prev = self.ins[i - 1]
+            ops = _operands(prev)
+            if not (prev.startswith("s_andn2_b64") and ops[:2] == ["vcc", "exec"]) or ins_state[i - 1] is None:
+                continue
+            # only X = -1 is certain (VCC = 0); X = 0 gives VCC = EXEC, which
+            # can be 0 in divergent code
+            if ins_state[i - 1].get(ops[2], UNK) != -1:
+                continue
+            taken = t.startswith("s_cbranch_vccz")
+            target = labels[t.split()[1]]
+            self.succ[i] = [target] if taken else [i + 1]
 
     def walk(self, i, need, forward, visit):
         """Calls visit(j, ws) for every instruction j reachable from i (after
@@ -281,4 +354,41 @@ def asm_lds_reads_waited(text):
                 bad.append(f"{t} -> {u} with {later} LDS instructions after it and no covering wait")
                 continue
             stack.extend((k, min(later + u.startswith("ds_"), 16)) for k in prog.succ[j])
+    return bad, n
+
+
+def global_loads_waited(text):
+    """Every global load into registers (the inline-asm ones the compiler does
+    not count included): on every path, nothing touches its destination
+    registers (a use, a copy, a spill) before the next `s_waitcnt` on vmcnt.
+    The kernels wait for their uncounted loads with explicit counts placed
+    right before the first use; this scan checks that the compiler put no
+    instruction on those registers ahead of that wait (the counts themselves
+    follow the issue order the code fixes)."""
+    prog = _Program(text)
+    bad, n = [], 0
+    for i, t in enumerate(prog.ins):
+        if not t.startswith("global_load") or t.startswith("global_load_lds"):
+            continue
+        dst = _vregs(_operands(t)[0])
+        if not dst:
+            continue
+        n += 1
+        seen = set()
+        stack = list(prog.succ[i])
+        while stack:
+            j = stack.pop()
+            if j in seen:
+                continue
+            seen.add(j)
+            u = prog.ins[j]
+            if u.startswith("s_waitcnt") and "vmcnt" in u:
+                continue
+            touched = set()
+            for o in _operands(u):
+                touched |= _vregs(o)
+            if touched & dst:
+                bad.append(f"{t} -> {u} before any vmcnt wait")
+                continue
+            stack.extend(prog.succ[j])
     return bad, n
