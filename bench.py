@@ -66,6 +66,11 @@ def _traffic(profile_name, src_names):
     return float(t.group(1))
 
 
+def _progress(msg):
+    """A progress line on stderr (the JSON line stays alone on stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def _cpu_line(value, unit, cores, sample):
     """The oracle as it stands, timed on the host beside a GPU leg."""
     return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
@@ -202,6 +207,7 @@ MASKED_KERNEL = "prefill_o2_kernel<sdpa::Bf16, 128, 128, false, 4, 1, 64, false,
 CACHED_LEN = 3584
 
 _PROFILED = {"gqa_causal_prefill_bf16": "prefill_gqa_causal_bf16", "splitkv_decode_bf16": "decode_splitkv_bf16"}
+PAGED_PROFILED = (64, 16)  # page sizes of the paged decode in the counters pass, in this order
 
 
 def _counters_pass():
@@ -239,6 +245,16 @@ def _counters_pass():
         sdpa.decode(dqd, sets[i % 4][0], sets[i % 4][1], scale=dw.scale, out=dout, workspace=ws)
     torch.cuda.synchronize()
     del sets
+    # the paged decode over set 0: 5 calls in 64-key pages, then 5 in 16-key
+    # pages (its 537 MB of K/V exceed the last-level cache, so every call
+    # reads from HBM)
+    full = torch.full((dw.batch,), dw.kv_len, dtype=torch.int32, device=dev)
+    for ps in PAGED_PROFILED:
+        kp, vp, table = (t.to(dev) for t in inputs.paginate(dk0, dv0, ps, seed=dw.seed + 1))
+        for _ in range(5):
+            sdpa.decode_paged(dqd, kp, vp, page_table=table, seq_lens=full, scale=dw.scale, out=dout, workspace=ws)
+        torch.cuda.synchronize()
+        del kp, vp, table
     msets = [(torch.rand(MASK_SHAPE, device=dev) < 0.5, torch.empty(MASK_SHAPE, dtype=torch.bfloat16, device=dev))
              for _ in range(2)]
     for i in range(6):
@@ -267,8 +283,8 @@ def _counters_pass():
     for _ in range(3):
         sdpa.prefill_masked(mq, mk, mv, mbias, scale=MASKED.scale)
     torch.cuda.synchronize()
-    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20, mask conversion x6, "
-          f"unaligned / fp8 / cached / masked prefill x3 each", flush=True)
+    print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20, paged decode x5 per page size, "
+          f"mask conversion x6, unaligned / fp8 / cached / masked prefill x3 each", flush=True)
 
 
 def _masked_inputs(dev):
@@ -482,6 +498,44 @@ def _summarize_counters(fetch_dir, write_dir):
             f.write(f"ratio to algorithmic: {total / alg:.3f}\n")
             f.write(f"source_sha256: {_src_hash(*_SOURCES[kind])}\n")
         print("wrote", out)
+    # paged decode: its split-kernel dispatches in order (5 per page size),
+    # each with the combine dispatch that follows it
+    dw = inputs.WORKLOADS["splitkv_decode_bf16"]
+    ptot = {ps: 0.0 for ps in PAGED_PROFILED}
+    plines = {ps: [] for ps in PAGED_PROFILED}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        kib_copy, factor, _, cname = res[counter]
+        rows = {int(r["Dispatch_Id"]): r for r in _read_csv(os.path.join(d, "run_counter_collection.csv"))
+                if r["Counter_Name"] == counter}
+        split_ids = sorted(i for i, r in rows.items()
+                           if "decode_split_kernel" in r["Kernel_Name"] and "true>" in r["Kernel_Name"])
+        for k, ps in enumerate(PAGED_PROFILED):
+            ids = split_ids[5 * k:5 * k + 5]
+            if len(ids) < 5:
+                continue
+            sk = statistics.mean(float(rows[i]["Counter_Value"]) for i in ids)
+            ck = statistics.mean(float(rows[i + 1]["Counter_Value"]) for i in ids
+                                 if i + 1 in rows and "decode_combine_kernel" in rows[i + 1]["Kernel_Name"])
+            b = (sk + ck) * 1024.0 * factor
+            ptot[ps] += b
+            plines[ps].append(f"{counter}: scale factor {factor:.4f} ({cname}); paged split kernel {sk:.1f} KiB + "
+                              f"combine {ck:.1f} KiB per call over {len(ids)} calls -> {b:.0f} B\n")
+    for ps in PAGED_PROFILED:
+        if len(plines[ps]) != 2:
+            continue
+        out = os.path.join(ROOT, "profiles", f"decode_paged{ps}_splitkv_bf16_counters.txt")
+        alg = dw.bytes_moved() + (dw.kv_len // ps) * dw.batch * 4 + dw.batch * 4
+        with open(out, "w") as f:
+            f.write(f"workload: splitkv_decode_bf16 in {ps}-key pages (shuffled physical order, every sequence full)\n")
+            f.write("commands: as for decode_splitkv_bf16_counters.txt (the counters pass runs 5 paged calls per "
+                    "page size after the dense decode)\n")
+            for line in plines[ps]:
+                f.write(line)
+            f.write(f"algorithmic bytes per call (Q+K+V+O once, page table, lengths): {alg}\n")
+            f.write(f"hbm_bytes_per_launch: {ptot[ps]:.0f}\n")
+            f.write(f"ratio to algorithmic: {ptot[ps] / alg:.3f}\n")
+            f.write(f"source_sha256: {_src_hash(*_SOURCES['decode'])}\n")
+        print("wrote", out)
     if len(mres) == 2:
         out = os.path.join(ROOT, "profiles", "mask_convert_16x4096x4096_counters.txt")
         total = 0.0
@@ -567,6 +621,7 @@ def main():
     prefill_err = float(np.abs(got - ref).max())
     prefill_nan = int(np.isnan(got).sum())
 
+    _progress("prefill leg done")
     # ---------------- split-KV decode, 4 rotating K/V sets ----------------
     dw = inputs.WORKLOADS["splitkv_decode_bf16"]
     dq, dk0, dv0, _ = inputs.make_qkv(dw)
@@ -620,6 +675,7 @@ def main():
         dcpu = _cpu_line(round(dbytes / sec / 1e9, 3), "GB/s", threads,
                          f"whole decode workload ({dw.batch * dw.head_q} rows x {dw.kv_len} keys) in {sec:.2f} s, fp64")
 
+    _progress("decode leg done")
     # ------- the same decode over a paged cache: 64- and 16-key pages, shuffled -------
     from oracle import paged as opaged
 
@@ -665,7 +721,8 @@ def main():
             "eager_ms_per_call": round(peager_ms, 6), "steps": args.decode_steps, "kv_sets": dw.kv_sets,
             "algorithmic_bytes": pbytes,
             "roofline": {"bound": "hbm", "achieved": round(pgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(pgbs / PEAK_HBM_GBS, 5), "traffic": None},
+                         "frac": round(pgbs / PEAK_HBM_GBS, 5),
+                         "traffic": _traffic(f"decode_paged{PS}_splitkv_bf16_counters.txt", _SOURCES["decode"])},
             "parity": {"max_abs_err": max(paged_err, paged_err_rest),
                        "set0": {"max_abs_err": paged_err, "rows": dw.batch * dw.head_q},
                        "sets1_3": {"max_abs_err": paged_err_rest, "rows_per_set": int(len(drows))}},
@@ -675,6 +732,7 @@ def main():
 
     del cpu_sets
 
+    _progress("paged decode legs done")
     # ---------------- other prefill workloads (context lines) ----------------
     extra = {}
     for name in ("single_head_f16_128", "unaligned_full_bf16", "tiny_causal_bf16", "mla_fp8_causal_prefill"):
@@ -697,6 +755,7 @@ def main():
                        "algorithmic_gflop": round(xw.flops() / 1e9, 4), "peak": peak,
                        "frac_of_peak": round(xt / peak, 5)}
         del xq, xk, xv, xo
+    _progress("other prefill workloads done")
     # ------- cached-KV (chunked) prefill: 512 new queries/keys over 3584 cached -------
     from oracle import cached as ocached
 
@@ -734,6 +793,7 @@ def main():
                                              f"fp64")}
     del cqd, ckcd, cvcd, ckd, cvd
 
+    _progress("cached prefill leg done")
     # ------- boolean -> additive mask conversion, 4 rotating buffer sets -------
     from oracle import mask as omask
 
@@ -773,6 +833,7 @@ def main():
                                            f"through the numpy oracle in {msec:.2f} s")}
     del msets
 
+    _progress("mask conversion leg done")
     # ------- prefill with a full additive mask (per-head bias) -------
     from oracle import mask as omask2
 
@@ -813,6 +874,7 @@ def main():
     floor_eager = _time(lambda i: one.add_(1.0), args.steps, args.warmup, stream)
     floor_graph = _graph_time(lambda i: one.add_(1.0), args.steps, args.warmup)
 
+    _progress("masked prefill leg done")
     # ---------------- CPU baseline: the oracle on the host cores ----------------
     cpu = None
     if not args.no_cpu_baseline:
