@@ -117,13 +117,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   for (int i = 0; i < K_INSTR; ++i) {
     const int slot = i * 64 + lane, r = slot / KCPR;
     krow[i] = r;
-    kcol[i] = ((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16;
+    kcol[i] = fill_chunk_decode_k<KCPR>(slot) * 16;
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int slot = i * 64 + lane, r = slot / VCPR;
     vrow[i] = r;
-    vcol[i] = ((slot % VCPR) ^ (int)swz_decode<VCPR>(r)) * 16;
+    vcol[i] = fill_chunk_decode<VCPR>(slot) * 16;
   }
   const int last_key = seq_len - 1;
 
@@ -214,22 +214,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   // K fragment (A operand of 16x16x32): key row 16t + l%16, slot 4s + l/16
   uint32_t koff[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) koff[s] = n16 * KROW + (((4 * s + gq) ^ (int)swz_prefill<KCPR>(n16)) << 4);
+  for (int s = 0; s < KS; ++s) koff[s] = decode_k_read<KCPR>(lane, s);
   // V^T fragment offsets for ds_read_b64_tr_b16: lane (gq, s = l%16) addresses
   // key row 4*gq + s/4 (+16 for the second half) at value columns 16t + 4*(s%4)
   uint32_t voff[2][NT];
-  {
-    const int s = lane & 15;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int r = 16 * hf + 4 * gq + (s >> 2);
+  for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int col = 16 * t + 4 * (s & 3);
-        voff[hf][t] = r * VROW + (((col >> 3) ^ (int)swz_decode<VCPR>(r)) << 4) + ((col & 7) << 1);
-      }
-    }
-  }
+    for (int t = 0; t < NT; ++t) voff[hf][t] = decode_vt_read<VCPR>(lane, hf, t);
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -259,8 +251,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
         x[4 * t + r] = v;
         bmax = fmaxf(bmax, v);
       }
-    bmax = fmaxf(bmax, xor_lane(bmax, 16));
-    bmax = fmaxf(bmax, xor_lane(bmax, 32));
+    bmax = pair_max(pair16_max(bmax));
     const float m_new = fmaxf(m_run, bmax);
     const float m_sub = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_sub);
@@ -304,8 +295,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   }
 
   // partial results: unnormalised O^T (lane holds head n16, values 16t + 4*gq + r)
-  float l_tot = l_run + xor_lane(l_run, 16);
-  l_tot += xor_lane(l_tot, 32);
+  float l_tot = pair_sum(pair16_sum(l_run));
   if constexpr (PAGED) {
     if (pt_bad) {  // a page-table entry was out of range: poison the rows
       l_tot = __builtin_nanf("");

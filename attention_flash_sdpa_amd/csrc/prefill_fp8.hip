@@ -48,6 +48,7 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   constexpr int NW = kPrefillWaves;
   constexpr int KAROW = 128, KBROW = 64, VROW = 128;         // LDS bytes per key row
   constexpr int KABYTES = BK * KAROW, KBBYTES = BK * KBROW, VBYTES = BK * VROW;
+  static_assert(KAROW == 128 && KBROW == 64 && VROW == 128, "row sizes of fp8_k*_read / fp8_vt_read");
   constexpr int KBYTES = KABYTES + KBBYTES;                  // 12 KiB per K block
   constexpr int KA_INSTR = KABYTES / 1024 / NW;              // 2 per wave
   constexpr int KB_INSTR = KBBYTES / 1024 / NW;              // 1 per wave
@@ -125,19 +126,19 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   for (int i = 0; i < KA_INSTR; ++i) {
     const int slot = (wave * KA_INSTR + i) * 64 + lane, r = slot / 8;
     ka_row[i] = r;
-    ka_col[i] = ((slot % 8) ^ (int)swz_prefill<8>(r)) * 16;
+    ka_col[i] = fill_chunk_prefill<8>(slot) * 16;
   }
 #pragma unroll
   for (int i = 0; i < KB_INSTR; ++i) {
     const int slot = (wave * KB_INSTR + i) * 64 + lane, r = slot / 4;
     kb_row[i] = r;
-    kb_col[i] = KAROW + ((slot % 4) ^ (int)swz_quarter(r)) * 16;  // dims 128.. of the row
+    kb_col[i] = KAROW + fill_chunk_quarter(slot) * 16;  // dims 128.. of the row
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int slot = (wave * V_INSTR + i) * 64 + lane, r = slot / 8;
     v_row[i] = r;
-    v_col[i] = ((slot % 8) ^ (int)swz_prefill<8>(r)) * 16;
+    v_col[i] = fill_chunk_prefill<8>(slot) * 16;
   }
   const int last_key = Sk - 1;
   auto fill_k = [&](int kb, uint32_t buf) __attribute__((always_inline)) {
@@ -168,25 +169,17 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      ka_off[s][c] = lds0 + l32 * KAROW + (((4 * s + 2 * hl + c) ^ (int)swz_prefill<8>(l32)) << 4);
+      ka_off[s][c] = lds0 + fp8_ka_read(lane, s, c);
 #pragma unroll
   for (int c = 0; c < 2; ++c)
-    kb_off[c] = lds0 + KABYTES + l32 * KBROW + (((2 * hl + c) ^ (int)swz_quarter(l32)) << 4);
+    kb_off[c] = lds0 + KABYTES + fp8_kb_read(lane, c);
   // V^T fragment (A operand of the bf16 32x32x16 MFMA) via ds_read_b64_tr_b8:
   // lane (group gq = l/16, s = l%16) addresses key row 8*(r/4) + 4*(gq/2) +
   // r%4 with r = s/2 (+16 per key chunk) and value bytes 32t + 16*(gq%2) +
   // 8*(s%2); its group partner lanes then hold 8 keys of one value column.
   uint32_t v_off[NT];
-  {
-    const int gq = lane >> 4, s = lane & 15;
-    const int r = s >> 1;
-    const int row = 8 * (r >> 2) + 4 * (gq >> 1) + (r & 3);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = 32 * t + 16 * (gq & 1) + 8 * (s & 1);
-      v_off[t] = lds0 + row * VROW + ((((col >> 4) ^ (int)swz_prefill<8>(row))) << 4) + (col & 15);
-    }
-  }
+  for (int t = 0; t < NT; ++t) v_off[t] = lds0 + fp8_vt_read(lane, t);
 
   f32x16_t acc[NT];
 #pragma unroll

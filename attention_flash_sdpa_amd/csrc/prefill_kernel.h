@@ -138,13 +138,13 @@ void prefill_kernel(const PrefillArgs a) {
   for (int i = 0; i < K_INSTR; ++i) {
     const int slot = (wis * K_INSTR + i) * 64 + lane, r = slot / KCPR;
     krow[i] = r;
-    kch[i] = ((slot % KCPR) ^ (int)swz_prefill<KCPR>(r)) * 16;
+    kch[i] = fill_chunk_prefill<KCPR>(slot) * 16;
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
     const int slot = (wis * V_INSTR + i) * 64 + lane, r = slot / VCPR;
     vrow[i] = r;
-    vch[i] = ((slot % VCPR) ^ (int)swz_prefill<VCPR>(r)) * 16;
+    vch[i] = fill_chunk_prefill<VCPR>(slot) * 16;
   }
   const int last_key = Sk - 1;
   // lane byte offsets within a whole block, less the instruction offset
@@ -221,25 +221,17 @@ void prefill_kernel(const PrefillArgs a) {
   uint32_t koff[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
-    koff[s] = lds0 + l32 * KROW + ((((2 * s + hl)) ^ (int)swz_prefill<KCPR>(l32)) << 4);
+    koff[s] = lds0 + prefill_k_read<KCPR>(lane, s);
   // V^T fragment (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16: lane
   // (group gq = l/16, s = l%16) addresses key row 4*(gq/2) + s/4 (+8 for the
   // second half, +16 per key chunk) at value columns 32t + 16*(gq%2) +
   // 4*(s%4).  The swizzle of rows r and r + 8 differs, so both halves get
   // offsets; +16 rows per key chunk leaves it unchanged.
   uint32_t voff[2][NT];
-  {
-    const int gq = lane >> 4, s = lane & 15;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int r = 8 * hf + 4 * (gq >> 1) + (s >> 2);
+  for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int col = 32 * t + 16 * (gq & 1) + 4 * (s & 3);
-        voff[hf][t] = lds0 + r * VROW + ((((col >> 3) ^ (int)swz_prefill<VCPR>(r))) << 4) + ((col & 7) << 1);
-      }
-    }
-  }
+    for (int t = 0; t < NT; ++t) voff[hf][t] = lds0 + prefill_vt_read<VCPR>(lane, hf, t);
 
   // ---- online softmax state ----------------------------------------------
   f32x16_t acc[NT];

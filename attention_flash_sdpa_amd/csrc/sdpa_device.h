@@ -20,6 +20,8 @@
 
 #include <type_traits>
 
+#include "lds_layout.h"
+
 namespace sdpa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -254,6 +256,18 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The same over the lane pair (l, l ^ 16): v_permlane16_swap(a, b) swaps the
+// odd 16-lane rows of a with the even rows of b, so with a = b = x the pair
+// is (own, partner) in even rows and (partner, own) in odd rows.
+__device__ __forceinline__ float pair16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Butterfly over lanes with the given xor distance (ds_bpermute based).
 __device__ __forceinline__ float xor_lane(float x, int mask) {
   const int lane = __lane_id();
@@ -408,39 +422,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// LDS swizzles of the 16-byte slots within a K/V row: the slot holding
-// chunk c of row r is c ^ f(r).  The LDS serves 16 lanes x 16 bytes (64 banks
-// of 4 bytes) per cycle, so a read is conflict-free when the 16 lanes of each
-// quarter-wave hit 16 distinct 16-byte positions of a 256-byte bank line.
-//
-// Prefill (SLOTS = row bytes / 16 = 16 or 8):
-//  * K fragments (ds_read_b128): 16 consecutive rows at one chunk;
-//  * V^T fragments (ds_read_b64_tr_b16): 4 consecutive rows x 4 chunks per
-//    half-wave.
-// With 16-byte slots per 256-byte row, f swaps the two 2-bit fields of r%16;
-// with 8 slots (two rows per bank line) f applies the 3-bit analogue to r/2.
-// Both patterns then touch 16 distinct positions (checked on the CPU).
-template <int SLOTS>
-__host__ __device__ __forceinline__ uint32_t swz_prefill(uint32_t r) {
-  static_assert(SLOTS == 16 || SLOTS == 8, "row of 128 or 256 bytes");
-  if constexpr (SLOTS == 16) return ((r & 3u) << 2) | ((r >> 2) & 3u);
-  const uint32_t x = r >> 1;
-  return ((x & 1u) << 2) | ((x >> 1) & 3u);
-}
-
-// 64-byte rows (4 slots, four rows per bank line), read as 16 consecutive rows
-// at one chunk: f = (r / 4) % 4 spreads them over the 16 positions.
-__host__ __device__ __forceinline__ uint32_t swz_quarter(uint32_t r) { return (r >> 2) & 3u; }
-
-// Decode V^T fragments (16x16x32 MFMA, ds_read_b64_tr_b16): each half-wave
-// reads 8 consecutive rows x 2 adjacent chunks.
-template <int SLOTS>
-__host__ __device__ __forceinline__ uint32_t swz_decode(uint32_t r) {
-  static_assert(SLOTS == 16 || SLOTS == 8, "row of 128 or 256 bytes");
-  if constexpr (SLOTS == 16) return (r & 7u) << 1;
-  return ((r >> 1) & 3u) << 1;
 }
 
 }  // namespace sdpa
