@@ -423,18 +423,26 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   // ---- epilogue ------------------------------------------------------------
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
+  u32x4_t runs[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x2_t w2[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = 8 * p + 4 * k;
+        w2[k].x = pack2<Bf16>(acc[t][r + 0] * inv, acc[t][r + 1] * inv);
+        w2[k].y = pack2<Bf16>(acc[t][r + 2] * inv, acc[t][r + 3] * inv);
+      }
+      runs[t][p] = pair_runs16(w2[0], w2[1]);
+    }
   if (row_ok) {
     uint16_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int col = 32 * t + 8 * q4 + 4 * hl;
-        u32x2_t w;
-        w.x = pack2<Bf16>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
-        w.y = pack2<Bf16>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
-        *(u32x2_t*)(orow + col) = w;
-      }
+      for (int p = 0; p < 2; ++p) *(u32x4_t*)(orow + 32 * t + 16 * p + 8 * hl) = runs[t][p];
     if (a.lse != nullptr && hl == 0)
       a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }

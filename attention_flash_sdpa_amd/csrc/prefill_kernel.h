@@ -606,18 +606,26 @@ void prefill_kernel(const PrefillArgs a) {
     constexpr int T0 = decltype(t0_tag)::value, T1 = decltype(t1_tag)::value;
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
+    u32x4_t runs[T1 - T0][2];
+#pragma unroll
+    for (int t = T0; t < T1; ++t)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x2_t w[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int r = 8 * p + 4 * k;
+          w[k].x = pack2<T>(acc[t][r + 0] * inv, acc[t][r + 1] * inv);
+          w[k].y = pack2<T>(acc[t][r + 2] * inv, acc[t][r + 3] * inv);
+        }
+        runs[t - T0][p] = pair_runs16(w[0], w[1]);
+      }
     if (row_ok) {
       elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
 #pragma unroll
       for (int t = T0; t < T1; ++t)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = 32 * t + 8 * q4 + 4 * hl;
-          u32x2_t w;
-          w.x = pack2<T>(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv);
-          w.y = pack2<T>(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
-          *(u32x2_t*)(orow + col) = w;
-        }
+        for (int p = 0; p < 2; ++p) *(u32x4_t*)(orow + 32 * t + 16 * p + 8 * hl) = runs[t - T0][p];
       if (a.lse != nullptr && hl == 0 && T0 == 0)
         a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }

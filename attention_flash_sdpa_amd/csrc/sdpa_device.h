@@ -256,6 +256,18 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// O leaves the 32x32 accumulator layout in 4-column pieces: in a value tile,
+// lane l holds columns 8j + 4(l/32) .. +3 of row l%32 (j = 0..3).  Two
+// half-wave swaps turn the pieces j = 2p (w_even) and 2p+1 (w_odd) of the lane
+// pair (l, l+32) into one 8-column run per lane, columns 16p + 8(l/32) .. +7,
+// for one 16-byte store: v_permlane32_swap(a, b) exchanges lanes 32-63 of a
+// with lanes 0-31 of b.
+__device__ __forceinline__ u32x4_t pair_runs16(u32x2_t w_even, u32x2_t w_odd) {
+  const auto sx = __builtin_amdgcn_permlane32_swap(w_even.x, w_odd.x, false, false);
+  const auto sy = __builtin_amdgcn_permlane32_swap(w_even.y, w_odd.y, false, false);
+  return u32x4_t{sx[0], sy[0], sx[1], sy[1]};
+}
+
 // The same over the lane pair (l, l ^ 16): v_permlane16_swap(a, b) swaps the
 // odd 16-lane rows of a with the even rows of b, so with a = b = x the pair
 // is (own, partner) in even rows and (partner, own) in odd rows.
