@@ -168,7 +168,7 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
         return [(f"prefill_fp8_kernel<{c}>", p.num_groups * p.waves_per_group * 64)]
     if 12 <= p.kernel <= 15 or 24 <= p.kernel <= 27:   # the two-waves-per-SIMD 32-row kernel
         shape = "4, 1, 64" if p.kernel <= 15 else "8, 4, 32"   # waves, key ranges, keys per block
-        return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {shape}>",
+        return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {shape}, {'true' if cached else 'false'}, false>",
                  p.num_groups * p.waves_per_group * 64)]
     return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, {'true' if cached else 'false'}>",
              p.num_groups * p.waves_per_group * 64)]
@@ -176,10 +176,11 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
 
 # kernel-source files whose text decides each profiled kernel's code
 _SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "prefill_o2_kernel.h",
-                        "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
-            "decode": ["decode.hip", "sdpa_device.h", "sdpa_internal.h"],
-            "fp8": ["prefill_fp8.hip", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
-            "masked": ["prefill_o2.hip", "prefill_o2_kernel.h", "sdpa_device.h", "sdpa_internal.h", "sdpa_bounds.h"],
+                        "sdpa_device.h", "lds_layout.h", "sdpa_internal.h", "sdpa_bounds.h"],
+            "decode": ["decode.hip", "sdpa_device.h", "lds_layout.h", "sdpa_internal.h"],
+            "fp8": ["prefill_fp8.hip", "sdpa_device.h", "lds_layout.h", "sdpa_internal.h", "sdpa_bounds.h"],
+            "masked": ["prefill_o2.hip", "prefill_o2_kernel.h", "sdpa_device.h", "lds_layout.h", "sdpa_internal.h",
+                       "sdpa_bounds.h"],
             "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"]}
 def _cached_chunk():
     from attention_flash_sdpa_amd import inputs
