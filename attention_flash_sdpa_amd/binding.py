@@ -43,10 +43,18 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kernel", "waves_per_group", "rows_per_wave", "heads_per_group", "qtiles_per_group", "block_q",
         "block_k", "stages", "q_tiles", "kv_blocks", "num_groups", "num_splits", "blocks_per_split",
-        "combine_groups")] + [("lds_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+        "combine_groups")] + [("lds_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
+                              ("range_iters_sum", ctypes.c_int64), ("range_iters_max", ctypes.c_int32),
+                              ("range_iters_min", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
+
+    def imbalance(self) -> float:
+        """Busiest key range's iterations over the mean of all ranges (1 = even;
+        prefill plans only)."""
+        ranges = self.num_groups * self.num_splits
+        return self.range_iters_max * ranges / self.range_iters_sum if self.range_iters_sum else 1.0
 
 
 class LoopCounts(ctypes.Structure):

@@ -7,6 +7,7 @@
 // host ("xe2-sdp-kernels", section "Inner-loop rules").
 #include <math.h>
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -171,6 +172,25 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
       return SDPA_ERR_BAD_SHAPE;
     }
     plan->num_groups = (int32_t)groups;
+    // mainloop iterations per key range: the kernels give every range of a
+    // workgroup ceil(n_blocks / ks) blocks of the workgroup's query rows
+    if (p.batch > 0 && p.q_len > 0 && groups > 0) {
+      const int64_t per_tile = groups / plan->q_tiles;  // workgroups sharing one query tile
+      int32_t mx = 0, mn = INT32_MAX;
+      int64_t sum = 0;
+      for (int qt = 0; qt < plan->q_tiles; ++qt) {
+        const int row0 = qt * plan->block_q;
+        const int row_end = row0 + plan->block_q < p.q_len ? row0 + plan->block_q : p.q_len;
+        const KBlockRange r = kblock_range(row0, row_end, p.q_len, p.kv_len, plan->block_k, p.causal != 0);
+        const int32_t it = (int32_t)ceil_div(r.n_blocks, ks);
+        mx = it > mx ? it : mx;
+        mn = it < mn ? it : mn;
+        sum += (int64_t)it * ks * per_tile;
+      }
+      plan->range_iters_max = mx;
+      plan->range_iters_min = mn;
+      plan->range_iters_sum = sum;
+    }
     const int esz = p.in_dtype == SDPA_FP8_E4M3 ? 1 : 2;
     plan->lds_bytes = (uint64_t)ks * plan->stages * plan->block_k * (p.d_qk + p.d_v) * esz;
     plan->workspace_bytes = 0;

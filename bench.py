@@ -905,6 +905,10 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "head_q": w.head_q, "head_kv": w.head_kv,
                    "q_len": w.q_len, "kv_len": w.kv_len, "d_qk": w.d_qk, "d_v": w.d_v, "causal": True,
                    "algorithmic_gflop": round(flops / 1e9, 4), "grid": plan.num_groups,
+                   "key_ranges_per_group": plan.num_splits,
+                   "range_iters": {"max": plan.range_iters_max, "min": plan.range_iters_min,
+                                   "mean": round(plan.range_iters_sum / (plan.num_groups * plan.num_splits), 3),
+                                   "imbalance": round(plan.imbalance(), 3)},
                    "launch": "hip graph replays of a captured chunk of calls (chunk divides steps; at least one "
                              "untimed replay first)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 1
+#define SDPA_ABI_VERSION 2
 
 typedef enum {
   SDPA_F16 = 0,
@@ -119,6 +119,15 @@ typedef struct sdpa_plan {
   int32_t combine_groups;   /* decode: workgroups of the combine kernel         */
   uint64_t lds_bytes;       /* LDS per workgroup of the main kernel             */
   uint64_t workspace_bytes; /* device workspace the call needs                  */
+  /* Prefill load balance (0 for decode).  Every key range of a workgroup runs
+   * ceil(K blocks of its query rows / num_splits) mainloop iterations (the
+   * causal K-block range of "Xe SDPA Forward Mainloop", section "Outer
+   * K-block loop", cut into num_splits equal parts); with one workgroup per
+   * CU the busiest range sets the launch time.  max / (sum / (num_groups *
+   * num_splits)) is the imbalance factor (1 = even). */
+  int64_t range_iters_sum;  /* iterations summed over all ranges of all groups  */
+  int32_t range_iters_max;  /* iterations of the busiest range                  */
+  int32_t range_iters_min;  /* iterations of the lightest range                 */
 } sdpa_plan_t;
 
 /* Tile-level loop counts of one attention head for a given tiling, in the
