@@ -31,7 +31,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "block too small for the fill");
   static_assert(NW % KS == 0 && (BK == 32 || BK == 64), "shape");
   static_assert(!BIAS || (KS == 1 && !CACHED), "the bias form streams one dense key range");
-  constexpr int ML = BIAS ? NTL * 4 : 0;         // 8-byte bias loads per lane per block
+  constexpr int ML = BIAS ? NTL * 2 : 0;         // 16-byte bias loads per lane per block
   // LDS per key range: K buffers 0/1, then V buffers 0/1
   constexpr uint32_t KBUF0 = 0, KBUF1 = KBYTES;
   constexpr uint32_t VBUF0 = 2 * KBYTES, VBUF1 = 2 * KBYTES + VBYTES;
@@ -112,26 +112,28 @@ void prefill_o2_kernel(const PrefillArgs a) {
 
   // ---- additive bias (BIAS): the values of this lane's scores, straight from
   // memory into registers one block ahead.  Register r of score tile t holds
-  // key kb*BK + 32t + 8(r/4) + 4*hl + r%4, so load c of tile t brings the four
-  // keys from kb*BK + 32t + 8c + 4*hl (8 bytes) of row qrow (clamped to the
-  // last row); the start is clamped to the row's last four elements, which
-  // only moves the loads of keys past kv_len (masked anyway) and keeps every
-  // read inside the row.  One register set: iteration j reads block j's
-  // values, then loads block j+1's into the same registers, which the
-  // next iteration's K/V wait covers (the compiler does not count these
-  // loads; an ISA scan checks that nothing touches the registers before it).
+  // key kb*BK + 32t + 8(r/4) + 4*hl + r%4: four runs of four keys.  The lane
+  // pair (l, l+32) loads them as 16-byte pieces of row qrow (clamped to the
+  // last row): load p of tile t brings keys 32t + 16p + 8*hl .. +7, and
+  // bias_runs() exchanges the halves the partner needs.  A start past the
+  // row is clamped to its last eight elements, which only moves loads of
+  // keys past kv_len (masked anyway) and keeps every read inside the row.
+  // One register set: iteration j reads block j's values, then loads block
+  // j+1's into the same registers, which the next iteration's K/V wait
+  // covers (the compiler does not count these loads; an ISA scan checks that
+  // nothing touches the registers before it).
   const elem_t* mrow = nullptr;
   if constexpr (BIAS)
     mrow = (const elem_t*)a.mask + (size_t)b * a.mask_sb + (size_t)h * a.mask_sh +
-           (size_t)min(qrow, Sq - 1) * a.mask_row + 4 * hl;
-  u32x2_t mv[BIAS ? NTL * 4 : 1];
-  auto load_bias = [&](int kb, u32x2_t (&m)[BIAS ? NTL * 4 : 1]) __attribute__((always_inline)) {
+           (size_t)min(qrow, Sq - 1) * a.mask_row;
+  u32x4_t mv[BIAS ? NTL * 2 : 1];
+  auto load_bias = [&](int kb, u32x4_t (&m)[BIAS ? NTL * 2 : 1]) __attribute__((always_inline)) {
     if constexpr (BIAS) {
 #pragma unroll
       for (int t = 0; t < NTL; ++t)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          global_load_8_untracked(m[4 * t + c], mrow + min(kb * BK + 32 * t + 8 * c, a.mask_row - 4 - 4 * hl));
+        for (int p = 0; p < 2; ++p)
+          global_load_16_untracked<0>(m[2 * t + p], mrow + min(kb * BK + 32 * t + 16 * p + 8 * hl, a.mask_row - 8));
     }
   };
   const float s_nat = a.s_nat;
@@ -302,7 +304,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
 
   // Softmax part 1: mask (tail blocks only), block row max, lazy rescale.
   // Returns the subtrahend m of P = 2^(s2*S - m).
-  auto softmax_max = [&](int kb, f32x16_t (&sc)[NTL], const u32x2_t (&mv)[BIAS ? NTL * 4 : 1], auto masked_tag)
+  auto softmax_max = [&](int kb, f32x16_t (&sc)[NTL], const u32x4_t (&mv)[BIAS ? NTL * 2 : 1], auto masked_tag)
       __attribute__((always_inline)) -> float {
     constexpr bool MASKED = decltype(masked_tag)::value;
     float bmax;
@@ -311,11 +313,14 @@ void prefill_o2_kernel(const PrefillArgs a) {
       // max is taken there and moved to the log2 domain of the running max
       const int lim = MASKED ? (CAUSAL ? min(Sk - 1, qrow + off) : Sk - 1) - (kb * BK + 4 * hl) : 0;
       bmax = -INFINITY;
+      u32x2_t mb[NTL * 4];  // mb[4t + c]: the four keys 32t + 8c + 4*hl ..
+#pragma unroll
+      for (int i = 0; i < NTL * 2; ++i) bias_runs(mv[i], mb[2 * i], mb[2 * i + 1]);
 #pragma unroll
       for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t w = (r & 2) ? mv[4 * t + (r >> 2)].y : mv[4 * t + (r >> 2)].x;
+          const uint32_t w = (r & 2) ? mb[4 * t + (r >> 2)].y : mb[4 * t + (r >> 2)].x;
           float bias;
           if constexpr (T::is_bf16)
             bias = __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));

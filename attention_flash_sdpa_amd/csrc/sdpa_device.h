@@ -268,6 +268,18 @@ __device__ __forceinline__ u32x4_t pair_runs16(u32x2_t w_even, u32x2_t w_odd) {
   return u32x4_t{sx[0], sy[0], sx[1], sy[1]};
 }
 
+// The inverse of pair_runs16 for loads: the lane pair (l, l+32) loaded 16
+// bytes each, lane l keys k0 .. k0+7 and lane l+32 keys k0+8 .. k0+15 of one
+// row (two 16-bit keys per dword); afterwards each lane holds its own four of
+// each 8-key run, lane l keys k0 .. +3 (lo) and k0+8 .. +3 (hi), lane l+32
+// keys k0+4 .. +3 (lo) and k0+12 .. +3 (hi).
+__device__ __forceinline__ void bias_runs(const u32x4_t& v, u32x2_t& lo, u32x2_t& hi) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  lo = u32x2_t{s0[0], s1[0]};
+  hi = u32x2_t{s0[1], s1[1]};
+}
+
 // The same over the lane pair (l, l ^ 16): v_permlane16_swap(a, b) swaps the
 // odd 16-lane rows of a with the even rows of b, so with a = b = x the pair
 // is (own, partner) in even rows and (partner, own) in odd rows.
