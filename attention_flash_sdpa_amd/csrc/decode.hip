@@ -258,15 +258,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     m_run = m_new;
     // P^T as the B operand: k = 8*gq + j takes tile 0 register j (j < 4) and
     // tile 1 register j-4 (j >= 4)
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(x[i] - m_sub);
     u32x4_t pf;
-    pf.x = pack2<T>(fast_exp2(x[0] - m_sub), fast_exp2(x[1] - m_sub));
-    pf.y = pack2<T>(fast_exp2(x[2] - m_sub), fast_exp2(x[3] - m_sub));
-    pf.z = pack2<T>(fast_exp2(x[4] - m_sub), fast_exp2(x[5] - m_sub));
-    pf.w = pack2<T>(fast_exp2(x[6] - m_sub), fast_exp2(x[7] - m_sub));
-    float psum = add_pair<T>(pf.x, 0.f);
-    psum = add_pair<T>(pf.y, psum);
-    psum = add_pair<T>(pf.z, psum);
-    psum = add_pair<T>(pf.w, psum);
+    pf.x = pack2<T>(p[0], p[1]);
+    pf.y = pack2<T>(p[2], p[3]);
+    pf.z = pack2<T>(p[4], p[5]);
+    pf.w = pack2<T>(p[6], p[7]);
+    const float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));  // over the fp32 P
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] *= alpha;

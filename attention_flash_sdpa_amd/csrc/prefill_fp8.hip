@@ -19,9 +19,9 @@
 //    32x32x64 fp8 MFMA per value tile and block; the row sum is taken over
 //    the unrounded fp32 P.  Masked blocks (the causal diagonal, the ragged
 //    tail, the last block) run P V in bf16 instead, V widened exactly from
-//    fp8 and P rounded to bf16 (relative error <= 2^-9) with the row sum over
-//    the rounded values, so rows with few visible keys, whose output is an
-//    average of few P values, keep the finer rounding.
+//    fp8 and P rounded to bf16 (relative error <= 2^-9), so rows with few
+//    visible keys, whose output is an average of few P values, keep the
+//    finer rounding.  The row sum is taken over the fp32 P in both cases.
 //  * K rows are 192 bytes, so each K block is kept in LDS as a 128-byte part
 //    (dims 0..127) and a 64-byte part (dims 128..191), each with a
 //    power-of-two swizzle that keeps the fragment reads free of bank
@@ -258,13 +258,12 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     return MASKED ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
   };
 
-  // Softmax part 2: P = 2^(s2*S - m).  Masked blocks: rounded to bf16, four
-  // dwords per 16-key chunk c (the B operand of the bf16 P V), row sum over
-  // the rounded values.  Unmasked blocks: rounded to e4m3, eight dwords for
-  // the 64 keys of the block (the B operand of the fp8 P V): dword 4t + r/4
-  // holds registers r..r+3 (r % 4 == 0) of score tile t, i.e. bytes 4(r/4%2)..
-  // of chunk 2t + r/8, the key order of the transposed V reads; row sum over
-  // the unrounded values.
+  // Softmax part 2: P = 2^(s2*S - m), its row sum taken over the fp32 values.
+  // Masked blocks: rounded to bf16, four dwords per 16-key chunk c (the B
+  // operand of the bf16 P V).  Unmasked blocks: rounded to e4m3, eight dwords
+  // for the 64 keys of the block (the B operand of the fp8 P V): dword
+  // 4t + r/4 holds registers r..r+3 (r % 4 == 0) of score tile t, i.e. bytes
+  // 4(r/4%2).. of chunk 2t + r/8, the key order of the transposed V reads.
   auto softmax_exp = [&](const f32x16_t (&sc)[2], float m_sub, u32x4_t (&pf)[4], i32x8_t& pf8, auto masked_tag)
       __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -275,9 +274,8 @@ void prefill_fp8_kernel(const PrefillArgs a) {
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(sc[t][r] - m_sub);
           const float p1 = fast_exp2(sc[t][r + 1] - m_sub);
-          const uint32_t pk = pack2<Bf16>(p0, p1);
-          pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
-          l_run = add_pair<Bf16>(pk, l_run);
+          pf[2 * t + (r >> 3)][(r & 7) >> 1] = pack2<Bf16>(p0, p1);
+          l_run += p0 + p1;
         }
     } else {
       float la = 0.f, lb = 0.f;

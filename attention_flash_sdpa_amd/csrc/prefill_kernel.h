@@ -437,7 +437,7 @@ void prefill_kernel(const PrefillArgs a) {
                        : "=&v"(p) : "v"(s_cur[TL][r]), "s"(s2), "v"(m_sub));
         if (r & 1) {
           uint32_t pk = pack2<T>(pend[TL], p);
-          l_run = add_pair<T>(pk, l_run);
+          l_run += pend[TL] + p;  // row sum over the fp32 values
           asm volatile("" ::"v"(pk));  // computed in this slot; not tied, so it
                                         // can be formed in its operand register
           pf[2 * TL + (r >> 3)][(r & 7) >> 1] = pk;

@@ -375,7 +375,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
   };
 
   // Softmax part 2: P = 2^(s2*S - m) packed to 16 bits as the PV B operand;
-  // the row sum is taken over the packed values.
+  // the row sum is taken over the fp32 values before the packing.
   auto softmax_exp = [&](const f32x16_t (&sc)[NTL], float m_sub, u32x4_t (&pf)[NCH], auto masked_tag)
       __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -396,7 +396,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
         }
         const uint32_t pk = pack2<T>(p0, p1);
         pf[2 * t + (r >> 3)][(r & 7) >> 1] = pk;
-        l_run = add_pair<T>(pk, l_run);
+        l_run += p0 + p1;  // row sum over the fp32 values
       }
   };
 

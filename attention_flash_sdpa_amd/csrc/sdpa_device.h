@@ -215,19 +215,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
-// acc + lo + hi of a packed pair of 16-bit values (one v_dot2 with ones), so
-// row sums use exactly the rounded probabilities the MFMA consumes.
-template <class T>
-__device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
-  if constexpr (T::is_bf16) {
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), ones, acc, false);
-  } else {
-    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), ones, acc, false);
-  }
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 32x32x64 MFMA on OCP fp8 e4m3 operands (32 bytes per lane), unit block

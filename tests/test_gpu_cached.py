@@ -20,7 +20,9 @@ TOL16 = 2e-2
 
 
 def _lse_tol(dtype):
-    return 1e-3 if dtype == torch.float16 else 4e-3
+    """lse from fp32 row sums of the fp32 probabilities: the sequential sum of
+    n terms is within n * 2^-24 relative, 1e-3 covers rows of 16K keys."""
+    return 1e-3
 
 
 def _say(msg):

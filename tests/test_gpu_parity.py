@@ -22,10 +22,11 @@ TOL8 = 6e-2
 
 
 def _lse_tol(dtype):
-    """The row sum l is taken over the probabilities after rounding to the MFMA
-    operand type, so |d lse| <= |d l| / l <= one half-ulp of that type
-    (2^-9 bf16, 2^-12 fp16); twice that bound plus fp32 slack is allowed."""
-    return 1e-3 if dtype == torch.float16 else 4e-3
+    """The row sum l is taken over the fp32 probabilities (before their rounding
+    to the MFMA operand type), so lse carries fp32 rounding only: the
+    sequential sum of n terms is within n * 2^-24 relative, and 1e-3 covers
+    rows of 16K keys."""
+    return 1e-3
 
 
 def _say(msg):
@@ -210,7 +211,8 @@ def test_prefill_special_values(dev, oracle_mod):
     # scale = 0: uniform average of the visible values
     _prefill_case(dev, oracle_mod, q, k, v, causal=True, scale=0.0, what="scale=0")
     # constant V rows give that constant exactly (bf16-representable 0.75):
-    # the row sum is taken over the same rounded probabilities the PV MFMA uses
+    # the row sum is over the fp32 probabilities, their bf16 roundings differ
+    # from it by at most 2^-9 relative, 0.0015 at 0.75, under half a bf16 ulp
     vc = torch.full_like(v, 0.75)
     out = _prefill_case(dev, oracle_mod, q, k, vc, causal=True, scale=0.1, what="constant V")
     assert torch.equal(out.float().cpu(), torch.full((B, Sq, Hq, D), 0.75))
