@@ -1,5 +1,5 @@
 // prefill_kernel.h -- the one-wave-per-SIMD prefill kernel template
-// (prefill_kernel<T, D, DV, CAUSAL, KS, CACHED>), included by prefill.hip
+// (prefill_kernel<T, D, DV, CAUSAL, KS, CACHED, CALIGN>), included by prefill.hip
 // (dense keys) and prefill_cached.hip (cached prefix + new keys), which
 // compile their instantiations in parallel.  The design is described at the
 // top of prefill.hip.
@@ -24,7 +24,7 @@ __host__ __device__ constexpr int reads_in(int a, int b) {
   return c;
 }
 
-template <class T, int D, int DV, bool CAUSAL, int KS, bool CACHED>
+template <class T, int D, int DV, bool CAUSAL, int KS, bool CACHED, bool CALIGN = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(const PrefillArgs a) {
   constexpr int BK = kPrefillBlockK;
@@ -369,7 +369,16 @@ void prefill_kernel(const PrefillArgs a) {
       // first load from each base waits for its SGPRs, the first of each
       // group of four for its M0 write, the rest for nothing
       constexpr int WAITS = i == 0 ? 5 : (i % 4 == 0 ? 1 : 0);
-      if constexpr (CACHED) {
+      if constexpr (CACHED && CALIGN) {
+        // cache length and key count are multiples of the RSTEP rows one
+        // load covers, so every load lies in one tensor: its base is a
+        // scalar choice and the lane offsets are the dense form's
+        constexpr int RSTEP = 64 / (IS_V ? VCPR : KCPR);
+        const int first = (IS_V ? vrow0 : krow0) + (wis * (IS_V ? V_INSTR : K_INSTR) + i) * RSTEP;
+        const uint64_t base = first < Sc ? (IS_V ? vcb : kcb) : (IS_V ? vnb : knb);
+        global_to_lds_16_off<(i % 4) * 1024, WAITS>((const void*)(uintptr_t)base, IS_V ? vfo[i] : kfo[i],
+                                                  (IS_V ? vl : kl) + (i / 4) * 4096);
+      } else if constexpr (CACHED) {
         // per-lane addresses (the block may straddle cache and new keys).
         // The lane's key row in load i is row[0] + i * 64 / CPR, so whether
         // it is cached is one compare against a scalar bound; the address is

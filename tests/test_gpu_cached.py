@@ -84,6 +84,10 @@ CASES = [
     (1, 40, 700, 700, 0, 8, 2, 128, torch.bfloat16, False),      # no new keys: the cache only
     (2, 96, 64, 64, 40, 8, 4, 64, torch.float16, False),         # full attention, more queries than new keys
     (1, 300, 4000, 4096, 300, 16, 2, 128, torch.float16, True),  # fp16, d 128, long cache, 8 query heads per KV head
+    # cache and key counts multiples of the rows one 1 KiB fill covers (4 at
+    # d 128, 8 at d 64), with a block straddling the two: the scalar-base form
+    (1, 60, 100, 128, 60, 8, 2, 128, torch.bfloat16, True),
+    (1, 72, 200, 256, 72, 8, 2, 64, torch.bfloat16, True),
 ]
 
 
