@@ -339,16 +339,12 @@ __device__ __forceinline__ void global_to_lds_16_sbase(const void* sbase, uint32
 // compiler's wait-count tracking does not see it: it can then be issued
 // ahead of direct-to-LDS loads and waited for with a vmcnt that leaves those
 // in flight (the compiler would otherwise wait for all of them before the
-// first use).  Its result is read only after wait_vmcnt_pin<N>().
+// first use).  Its result is read only after a vmcnt wait that covers it and
+// a pin of the registers (wait_vmcnt_pin<N>(), or wait_vmcnt<N>() then
+// pin_regs()); an ISA scan checks that nothing touches them before the wait.
 template <int OFF>
 __device__ __forceinline__ void global_load_16_untracked(u32x4_t& d, const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=&v"(d) : "v"(p), "i"(OFF) : "memory");
-}
-
-// 8-byte global load into a VGPR pair, untracked like global_load_16_untracked
-// (read only after an explicit wait and pin_regs / wait_vmcnt_pin).
-__device__ __forceinline__ void global_load_8_untracked(u32x2_t& d, const void* p) {
-  asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(d) : "v"(p) : "memory");
 }
 
 // As global_to_lds_16_off with a per-lane 64-bit address (the lane's address
