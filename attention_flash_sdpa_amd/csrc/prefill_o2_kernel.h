@@ -428,19 +428,15 @@ void prefill_o2_kernel(const PrefillArgs a) {
     constexpr uint32_t VB_FREE = PAR ? VBUF0 : VBUF1;   // receives V(j+1)
     f32x16_t(&s_cur)[NTL] = PAR ? sb : sa;
     f32x16_t(&s_nxt)[NTL] = PAR ? sa : sb;
+    wait_vmcnt<0>();  // K(j+1), V(j) (and the bias of block j) have landed
+    if constexpr (BIAS) pin_regs(mv);
+    // every wave's loads have landed, and every wave is past iteration j-1,
+    // whose reads of K(j) and V(j-1) were the last of the buffers refilled here
+    __syncthreads();
     if constexpr (NEXT) {
       fill_v(kb0 + j + 1, VB_FREE);
-      if (j + 2 < cnt) {
-        fill_k(kb0 + j + 2, KB_FREE);
-        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) (and the bias of block j) have landed
-      } else {
-        wait_vmcnt<V_INSTR>();
-      }
-    } else {
-      wait_vmcnt<0>();
+      if (j + 2 < cnt) fill_k(kb0 + j + 2, KB_FREE);
     }
-    if constexpr (BIAS) pin_regs(mv);
-    __syncthreads();
     const float m_sub = softmax_max(kb0 + j, s_cur, mv, masked_tag);
     if constexpr (BIAS && NEXT) load_bias(kb0 + j + 1, mv);
     u32x4_t pf[NCH];
@@ -462,7 +458,6 @@ void prefill_o2_kernel(const PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) __syncthreads();  // this iteration's buffers are refilled next
   };
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
@@ -498,7 +493,6 @@ void prefill_o2_kernel(const PrefillArgs a) {
   for (int s = 0; s < D / 16; ++s) qf[s] = row_ok ? qf[s] : u32x4_t{0, 0, 0, 0};
   __syncthreads();
   qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
-  __syncthreads();  // K buffer 0 is refilled by the first iteration
   const int n_next = cnt - 1;  // iterations that have a next block
   const int j_mask = min(n_unmasked, n_next);
   run(0, j_mask, Unmasked{}, Next{});

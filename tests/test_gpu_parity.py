@@ -120,11 +120,11 @@ def test_unaligned_full_bf16_reduced(dev, oracle_mod):
     _prefill_case(dev, oracle_mod, q, k, v, causal=w.causal, scale=w.scale, what=w.name + " reduced")
 
 
-def test_unaligned_full_bf16_full_size_sampled(dev, oracle_mod):
+def test_unaligned_full_bf16_full_size(dev, oracle_mod):
+    """The full C3a workload, every one of its 56,056 rows against the oracle."""
     w = inputs.WORKLOADS["unaligned_full_bf16"]
     q, k, v, _ = inputs.make_qkv(w)
-    rows = _sample_rows(w.batch, w.q_len, w.head_q, 400, 7)
-    _prefill_case(dev, oracle_mod, q, k, v, causal=w.causal, scale=w.scale, rows=rows, what=w.name)
+    _prefill_case(dev, oracle_mod, q, k, v, causal=w.causal, scale=w.scale, what=w.name)
 
 
 def test_tiny_causal_bf16(dev, oracle_mod):
@@ -150,7 +150,7 @@ def test_mla_fp8_prefill_reduced(dev, oracle_mod):
 def test_mla_fp8_causal_prefill_full_size_sampled(dev, oracle_mod):
     w = inputs.WORKLOADS["mla_fp8_causal_prefill"]
     q, k, v, ds = inputs.make_qkv(w)
-    rows = _sample_rows(w.batch, w.q_len, w.head_q, 300, 11)
+    rows = _sample_rows(w.batch, w.q_len, w.head_q, 4000, 11)
     extra = np.array([(0, i, h) for i in range(0, 9) for h in (0, 77)], dtype=np.int64)   # rows with few keys
     rows = np.concatenate([rows, extra])
     _prefill_case(dev, oracle_mod, q, k, v, causal=True, scale=w.scale, tol=TOL8, rows=rows, descale=ds,
