@@ -342,18 +342,14 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     constexpr uint32_t VB_FREE = PAR ? VBUF0 : VBUF1;   // receives V(j+1)
     f32x16_t(&s_cur)[2] = PAR ? sb : sa;
     f32x16_t(&s_nxt)[2] = PAR ? sa : sb;
+    wait_vmcnt<0>();  // K(j+1), V(j) have landed
+    // every wave's loads have landed, and every wave is past iteration j-1,
+    // whose reads of K(j) and V(j-1) were the last of the buffers refilled here
+    __syncthreads();
     if constexpr (NEXT) {
       fill_v(j + 1, VB_FREE);
-      if (j + 2 < n_blocks) {
-        fill_k(j + 2, KB_FREE);
-        wait_vmcnt<K_INSTR + V_INSTR>();  // K(j+1), V(j) have landed
-      } else {
-        wait_vmcnt<V_INSTR>();
-      }
-    } else {
-      wait_vmcnt<0>();
+      if (j + 2 < n_blocks) fill_k(j + 2, KB_FREE);
     }
-    __syncthreads();
     constexpr bool MASKED = decltype(masked_tag)::value;
     const float m_sub = softmax_max(j, s_cur, masked_tag);
     u32x4_t pf[4];
@@ -377,7 +373,6 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     else
       pv_fp8(std::integral_constant<uint32_t, VB_CUR>{}, pf8);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) __syncthreads();  // this iteration's buffers are refilled next
   };
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
@@ -406,7 +401,6 @@ void prefill_fp8_kernel(const PrefillArgs a) {
   }
   __syncthreads();
   qk(std::integral_constant<uint32_t, KBUF0>{}, sa);
-  __syncthreads();  // K buffer 0 is refilled by the first iteration
   const int n_next = n_blocks - 1;  // iterations that have a next block
   const int j_mask = min(n_full, n_next);
   run(0, j_mask, Unmasked{}, Next{});
