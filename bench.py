@@ -170,7 +170,14 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
         shape = "4, 1, 64" if p.kernel <= 15 else "8, 4, 32"   # waves, key ranges, keys per block
         return [(f"prefill_o2_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {shape}, {'true' if cached else 'false'}, false>",
                  p.num_groups * p.waves_per_group * 64)]
-    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, {'true' if cached else 'false'}>",
+    if cached:
+        # the cached form whose fills take a scalar base: cache length and key
+        # count multiples of the 512 / D rows one fill instruction covers
+        rstep = 512 // w.d_qk
+        align = "true" if CACHED_LEN % rstep == 0 and w.kv_len % rstep == 0 else "false"
+        return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, true, {align}>",
+                 p.num_groups * p.waves_per_group * 64)]
+    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, false, false>",
              p.num_groups * p.waves_per_group * 64)]
 
 
