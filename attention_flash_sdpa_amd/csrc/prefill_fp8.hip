@@ -355,6 +355,9 @@ void prefill_fp8_kernel(const PrefillArgs a) {
     u32x4_t pf[4];
     i32x8_t pf8;
     __builtin_amdgcn_sched_barrier(0);
+    // the matrix-core part of the block at raised issue priority (as in the
+    // two-wave 16-bit kernel)
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (NEXT) qk(std::integral_constant<uint32_t, KB_NEXT>{}, s_nxt);
     softmax_exp(s_cur, m_sub, pf, pf8, masked_tag);
     if constexpr (NEXT) {
@@ -372,6 +375,7 @@ void prefill_fp8_kernel(const PrefillArgs a) {
       pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
     else
       pv_fp8(std::integral_constant<uint32_t, VB_CUR>{}, pf8);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
   using Par0 = std::integral_constant<int, 0>;

@@ -445,6 +445,9 @@ void prefill_o2_kernel(const PrefillArgs a) {
     // issues a few independent VALU instructions, which execute while the
     // matrix core works on that MFMA.
     __builtin_amdgcn_sched_barrier(0);
+    // the matrix-core part of the block at raised issue priority: the other
+    // wave on this SIMD, in its softmax, waits or barrier, yields to it
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (NEXT) qk(std::integral_constant<uint32_t, KB_NEXT>{}, s_nxt);
     softmax_exp(s_cur, m_sub, pf, masked_tag);
     if constexpr (NEXT) {
@@ -457,6 +460,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     pv(std::integral_constant<uint32_t, VB_CUR>{}, pf);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
   using Par0 = std::integral_constant<int, 0>;
