@@ -455,7 +455,7 @@ void prefill_o2_kernel(const PrefillArgs a) {
       for (int i = 0; i < NTL * D / 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
       }
     }
     __builtin_amdgcn_sched_barrier(0);
