@@ -829,12 +829,29 @@ def main():
     mrows = slice(0, 64)
     mref = omask.mask_convert(msets[0][0][0, mrows].cpu().numpy().astype(np.uint8), "bf16")
     mexact = bool(np.array_equal(msets[0][1][0, mrows].view(torch.int16).cpu().numpy().view(np.uint16), mref))
+    # the same HBM traffic as a plain device-to-device copy (read and write
+    # 1.5 bytes per mask element each), rotating four buffer pairs: what the
+    # memory system gives a kernel that does nothing else
+    csets = [(torch.empty(mbytes // 2, dtype=torch.uint8, device=dev).fill_(s_),
+              torch.empty(mbytes // 2, dtype=torch.uint8, device=dev)) for s_ in range(4)]
+
+    def cstep(i):
+        src, dst = csets[i % len(csets)]
+        dst.copy_(src)
+
+    cms = _time(cstep, max(MIN_LEG_CALLS, args.decode_steps // 4), max(4, args.warmup), torch.cuda.current_stream())
+    copy_ceiling = {"value": round(mbytes / (cms * 1e-3) / 1e9, 2), "unit": "GB/s", "ms_per_copy": round(cms, 6),
+                    "bytes": mbytes, "frac_of_it": round(mgbs / (mbytes / (cms * 1e-3) / 1e9), 5),
+                    "method": "torch copy_ of half the conversion's bytes (its read plus write are the "
+                              "conversion's traffic), four rotating buffer pairs, back-to-back eager calls"}
+    del csets
     mask_line = {"workload": f"bool mask {list(mshape)} -> bf16 additive", "value": round(mgbs, 2), "unit": "GB/s",
                  "ms_per_call": round(mms, 6), "steps": args.decode_steps, "buffer_sets": len(msets),
                  "algorithmic_bytes": mbytes,
                  "roofline": {"bound": "hbm", "achieved": round(mgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(mgbs / PEAK_HBM_GBS, 5),
                               "traffic": _traffic("mask_convert_16x4096x4096_counters.txt", _SOURCES["mask"])},
+                 "copy_ceiling": copy_ceiling,
                  "parity": {"bit_exact_rows": 64, "exact": mexact},
                  "cpu_baseline": _cpu_line(round(3 * msample.size / msec / 1e9, 3), "GB/s", 1,
                                            f"one [{MASK_SHAPE[1]}, {MASK_SHAPE[2]}] slice ({msample.size} elements) "
