@@ -250,10 +250,14 @@ def _decode_case(dev, oracle_mod, q, k, v, *, scale, num_splits=0, tol=TOL16, wh
     return out
 
 
-def test_splitkv_decode_bf16(dev, oracle_mod):
+@pytest.mark.parametrize("kv_set", [0, 1, 2, 3])
+def test_splitkv_decode_bf16(dev, oracle_mod, kv_set):
+    """The full decode workload, every row, on each of its four rotating K/V
+    sets (the seeded recipe: seed + 100 * set)."""
     w = inputs.WORKLOADS["splitkv_decode_bf16"]
-    q, k, v, _ = inputs.make_qkv(w)
-    _decode_case(dev, oracle_mod, q.reshape(w.batch, w.head_q, w.d_qk), k, v, scale=w.scale, what=w.name)
+    q, k, v, _ = inputs.make_qkv(w, kv_set=kv_set)
+    _decode_case(dev, oracle_mod, q.reshape(w.batch, w.head_q, w.d_qk), k, v, scale=w.scale,
+                 what=f"{w.name} set {kv_set}")
 
 
 DECODE_EDGE = [
