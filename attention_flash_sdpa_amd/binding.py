@@ -45,7 +45,7 @@ class Plan(ctypes.Structure):
         "block_k", "stages", "q_tiles", "kv_blocks", "num_groups", "num_splits", "blocks_per_split",
         "combine_groups")] + [("lds_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
                               ("range_iters_sum", ctypes.c_int64), ("range_iters_max", ctypes.c_int32),
-                              ("range_iters_min", ctypes.c_int32)]
+                              ("range_iters_min", ctypes.c_int32), ("kv_splits", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -53,7 +53,7 @@ class Plan(ctypes.Structure):
     def imbalance(self) -> float:
         """Busiest key range's iterations over the mean of all ranges (1 = even;
         prefill plans only)."""
-        ranges = self.num_groups * self.num_splits
+        ranges = self.num_groups * self.num_splits  # num_groups counts the kv_splits workgroups
         return self.range_iters_max * ranges / self.range_iters_sum if self.range_iters_sum else 1.0
 
 
@@ -126,13 +126,17 @@ def _check(status: int):
         raise SdpaError(status, (load().sdpa_last_error() or b"").decode())
 
 
-def _dtype_code(t) -> int:
+def _code_of(dtype) -> int:
     import torch
 
     m = {torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
-    if t.dtype not in m:
-        raise TypeError(f"unsupported dtype {t.dtype}")
-    return m[t.dtype]
+    if dtype not in m:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return m[dtype]
+
+
+def _dtype_code(t) -> int:
+    return _code_of(t.dtype)
 
 
 def make_problem(*, batch, q_len, kv_len, head_q, head_kv, d_qk, d_v, in_dtype, out_dtype, causal, scale,
@@ -157,8 +161,8 @@ def loop_counts(*, q_len, kv_len, d_qk, d_v, block_q, block_k, block_d, block_v,
 
 def set_prefill_variant(name: str | None) -> None:
     """Forces one form of the 16-bit prefill kernels ("narrow1", "narrow2",
-    "occ2", "split4") for later calls in this process; None or "" restores the
-    planner's choice.  For tuning sweeps and tests."""
+    "occ2", "split4", "kvsplit") for later calls in this process; None or ""
+    restores the planner's choice.  For tuning sweeps and tests."""
     _check(load().sdpa_set_prefill_variant((name or "").encode()))
 
 
@@ -213,13 +217,32 @@ def _out_dtypes(q):
     return (torch.bfloat16, torch.float16) if q.dtype == torch.float8_e4m3fn else (q.dtype,)
 
 
+def prefill_workspace_bytes(q, k, v, *, causal=False, descale=(1.0, 1.0, 1.0), out_dtype=None) -> int:
+    """Workspace bytes ``prefill`` uses for these shapes (0 unless the planner
+    splits the key range across workgroups)."""
+    import torch
+
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    pr = make_problem(batch=B, q_len=Sq, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=v.shape[-1],
+                      in_dtype=_dtype_code(q), out_dtype=_code_of(out_dtype), causal=causal, scale=1.0,
+                      descale=descale)
+    return int(load().sdpa_prefill_workspace_bytes(ctypes.byref(pr)))
+
+
 def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1.0, 1.0, 1.0), out_dtype=None,
-            stream=None):
+            workspace=None, stream=None):
     """O = softmax(Q K^T * scale + mask) V on the GPU.
 
     q [B, Sq, Hq, D], k [B, Sk, Hkv, D], v [B, Sk, Hkv, Dv] contiguous device
     tensors; returns O [B, Sq, Hq, Dv] (``out`` if given).  ``lse`` is an
-    optional fp32 [B, Hq, Sq] tensor to receive the log-sum-exp."""
+    optional fp32 [B, Hq, Sq] tensor to receive the log-sum-exp.
+    ``workspace``: a device uint8 tensor for the partials of a key range
+    split across workgroups (``prefill_workspace_bytes``); None allocates one
+    when the plan splits; a smaller one (an empty tensor included) runs the
+    problem without that split."""
     import torch
 
     _check_inputs(("q", "k", "v"), (q, k, v))
@@ -239,8 +262,14 @@ def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1
                       in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=causal, scale=scale,
                       descale=descale)
     lib = load()
-    ws_bytes = lib.sdpa_prefill_workspace_bytes(ctypes.byref(pr))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if workspace is None:
+        ws_bytes = lib.sdpa_prefill_workspace_bytes(ctypes.byref(pr))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    else:
+        _require(workspace.dtype == torch.uint8 and workspace.is_contiguous() and workspace.device == q.device,
+                 "workspace must be a contiguous uint8 tensor on q's device")
+        ws_bytes = workspace.numel()
+        ws = workspace if ws_bytes else None
     _check(lib.sdpa_prefill_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                                 ws_bytes, _stream_handle(stream)))
     return out

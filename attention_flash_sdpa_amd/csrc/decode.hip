@@ -23,6 +23,8 @@
 // Phase 2 (decode_combine_kernel): one wavefront per (batch, query head)
 // merges the splits: M = max_s m_s, w_s = 2^(m_s - M), O = sum w_s O_s /
 // sum w_s l_s (0 when nothing was visible), lse = ln2 * (M + log2 den).
+// The prefill split across workgroups reuses it with one row per (batch,
+// query row, query head) (launch_split_combine).
 //
 // Variable-length and paged caches (the mainloop's optional paged-KV
 // arguments and its logical-to-physical K tile helper, "Xe SDPA Forward
@@ -318,6 +320,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 // splits combined from registers in one pass (more use the looped path)
 constexpr int kCombineFast = 32;
 
+// lse position of combine row bh = b' * head_q + h: bh itself for decode;
+// for the prefill's rows b' = b * lse_q_len + i, [b, h, i] of [batch, head_q,
+// q_len]
+__device__ inline size_t combine_lse_index(const DecodeArgs& a, int bh) {
+  if (a.lse_q_len <= 1) return (size_t)bh;
+  const int h = bh % a.head_q, bq = bh / a.head_q;
+  return ((size_t)(bq / a.lse_q_len) * a.head_q + h) * a.lse_q_len + bq % a.lse_q_len;
+}
+
 template <class T, int DV>
 __global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int PER = DV / 64;   // value columns per lane (contiguous)
@@ -361,7 +372,8 @@ __global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const
     } else {
       o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
     }
-    if (a.lse != nullptr && lane == 0) a.lse[bh] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
+    if (a.lse != nullptr && lane == 0)
+      a.lse[combine_lse_index(a, bh)] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
     return;
   }
 
@@ -405,7 +417,8 @@ __global__ __launch_bounds__(64 * kCombineRows) void decode_combine_kernel(const
   } else {
     o[0] = (uint16_t)(pack2<T>(num[0] * inv, 0.f) & 0xffff);
   }
-  if (a.lse != nullptr && lane == 0) a.lse[bh] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
+  if (a.lse != nullptr && lane == 0)
+      a.lse[combine_lse_index(a, bh)] = den == 0.f ? -INFINITY : (M + log2f(den)) * kLn2;
 }
 
 // ---- scratch of the no-allocation decode entry point -----------------------
@@ -446,6 +459,22 @@ static int launch_decode_t(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStr
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(plan.combine_groups), dim3(64 * kCombineRows), 0, (hipStream_t)stream,
                      a);
+  return (int)hipGetLastError();
+}
+
+int launch_split_combine(const DecodeArgs& a, int in_dtype, int d_v, int groups, ihipStream_t* stream) {
+  const dim3 grid(groups), block(64 * kCombineRows);
+  const bool bf = in_dtype == SDPA_BF16;
+  if (in_dtype != SDPA_BF16 && in_dtype != SDPA_F16) return (int)hipErrorInvalidValue;
+  if (d_v == 64) {
+    if (bf) hipLaunchKernelGGL((decode_combine_kernel<Bf16, 64>), grid, block, 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((decode_combine_kernel<F16, 64>), grid, block, 0, (hipStream_t)stream, a);
+  } else if (d_v == 128) {
+    if (bf) hipLaunchKernelGGL((decode_combine_kernel<Bf16, 128>), grid, block, 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((decode_combine_kernel<F16, 128>), grid, block, 0, (hipStream_t)stream, a);
+  } else {
+    return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

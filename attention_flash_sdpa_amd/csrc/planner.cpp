@@ -58,7 +58,7 @@ void clear_error() { g_last_error[0] = 0; }
 const char* last_error_text() { return g_last_error; }
 
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
-                        sdpa_plan_t* plan, int variant, bool cached) {
+                        sdpa_plan_t* plan, int variant, bool cached, bool kv_split) {
   memset(plan, 0, sizeof *plan);
   if (num_cus <= 0) num_cus = kDefaultCUs;
   if (p.batch < 0 || p.q_len < 0 || p.kv_len < 0) {
@@ -138,7 +138,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // at the end, which doubles the workgroup count.
     bool split = kid != kPrefillFp8D192 && groups < num_cus && plan->kv_blocks >= 2;
     if (variant == 3 || variant == 5) split = false;
-    if (variant == 4) split = kid != kPrefillFp8D192;
+    if (variant == 4 || variant == 7) split = kid != kPrefillFp8D192;
     if (split) {
       ks = 2;
       groups = shape(kPrefillWaves / 2, &hp, &qtiles);
@@ -146,7 +146,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // More workgroups than CUs: the two-waves-per-SIMD form keeps two of them
     // on every CU at once (the one-wave form would run in rounds).
     bool occ2 = kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
-    if (variant == 3 || variant == 4) occ2 = false;
+    if (variant == 3 || variant == 4 || variant == 7) occ2 = false;
     if (variant == 5) occ2 = kid != kPrefillFp8D192;
     if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
     // Four key ranges of 32-key blocks, two waves (heads or query tiles) per
@@ -162,30 +162,67 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
       plan->block_k = kSplitBlockK;
       plan->kv_blocks = (int32_t)ceil_div(p.kv_len, plan->block_k);
     }
+    // Even the two-range split leaves more than half the CUs idle (short
+    // queries over a long key sequence): split each tile's K blocks across
+    // kvs workgroups as well, up to one workgroup per CU, no range shorter
+    // than kMinSplitBlocks blocks.  They write fp32 partials that a second
+    // kernel combines, which only pays when it multiplies the grid; the
+    // range count is then evened out so that no range is left empty.
+    // Short-query rows are few, so the partials stay small next to K/V.
+    int64_t kvs = 1;
+    const int64_t rows_all = (int64_t)p.batch * p.q_len * p.head_q;
+    const bool one_wave = plan->kernel == kid && kid != kPrefillFp8D192 && ks == 2;
+    if (kv_split && !cached && one_wave && groups > 0 && (variant == 0 || variant == 7)) {
+      if (variant == 7) {
+        // forced (tests): at least two workgroups, as many as the blocks
+        // allow, even when some of their ranges then hold no block
+        kvs = ceil_div(num_cus, groups);
+        if (kvs > plan->kv_blocks) kvs = plan->kv_blocks;
+        if (kvs < 2) kvs = 2;
+      } else if (2 * groups <= num_cus) {
+        kvs = ceil_div(num_cus, groups);
+        const int64_t by_len = plan->kv_blocks / (ks * kMinSplitBlocks);
+        if (kvs > by_len) kvs = by_len;
+        if (kvs >= 2) {
+          const int64_t per = ceil_div(plan->kv_blocks, ks * kvs);  // blocks per range
+          kvs = ceil_div(plan->kv_blocks, ks * per);
+        } else {
+          kvs = 1;
+        }
+      }
+      // partial and combine indices are 32-bit rows
+      if (kvs > 1 && (rows_all * kvs * (p.d_v > 2 ? p.d_v : 2) >= lim || groups * kvs >= lim)) kvs = 1;
+    }
     plan->num_splits = ks;
+    plan->kv_splits = (int32_t)kvs;
     plan->heads_per_group = hp;
     plan->qtiles_per_group = qtiles;
     plan->block_q = rows * qtiles;
     plan->q_tiles = (int32_t)ceil_div(p.q_len, plan->block_q);
-    if (groups >= lim) {
-      set_error("grid too large (%lld workgroups)", (long long)groups);
+    if (groups * kvs >= lim) {
+      set_error("grid too large (%lld workgroups)", (long long)(groups * kvs));
       return SDPA_ERR_BAD_SHAPE;
     }
-    plan->num_groups = (int32_t)groups;
-    // mainloop iterations per key range: the kernels give every range of a
-    // workgroup ceil(n_blocks / ks) blocks of the workgroup's query rows
+    plan->num_groups = (int32_t)(groups * kvs);
+    // mainloop iterations per key range: the kernels cut the K blocks of a
+    // workgroup's query rows into ks * kvs ranges of ceil(n_blocks / (ks *
+    // kvs)) blocks each, ks per workgroup; a workgroup whose first range
+    // starts past the last block runs none
     if (p.batch > 0 && p.q_len > 0 && groups > 0) {
-      const int64_t per_tile = groups / plan->q_tiles;  // workgroups sharing one query tile
+      const int64_t per_tile = groups / plan->q_tiles;  // workgroups sharing one query tile (per split)
       int32_t mx = 0, mn = INT32_MAX;
       int64_t sum = 0;
       for (int qt = 0; qt < plan->q_tiles; ++qt) {
         const int row0 = qt * plan->block_q;
         const int row_end = row0 + plan->block_q < p.q_len ? row0 + plan->block_q : p.q_len;
         const KBlockRange r = kblock_range(row0, row_end, p.q_len, p.kv_len, plan->block_k, p.causal != 0);
-        const int32_t it = (int32_t)ceil_div(r.n_blocks, ks);
-        mx = it > mx ? it : mx;
-        mn = it < mn ? it : mn;
-        sum += (int64_t)it * ks * per_tile;
+        const int64_t cnt = ceil_div(r.n_blocks, ks * kvs);
+        for (int64_t s = 0; s < kvs; ++s) {
+          const int32_t it = s * ks * cnt < r.n_blocks ? (int32_t)cnt : 0;
+          mx = it > mx ? it : mx;
+          mn = it < mn ? it : mn;
+          sum += (int64_t)it * ks * per_tile;
+        }
       }
       plan->range_iters_max = mx;
       plan->range_iters_min = mn;
@@ -194,6 +231,11 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     const int esz = p.in_dtype == SDPA_FP8_E4M3 ? 1 : 2;
     plan->lds_bytes = (uint64_t)ks * plan->stages * plan->block_k * (p.d_qk + p.d_v) * esz;
     plan->workspace_bytes = 0;
+    if (kvs > 1) {
+      const uint64_t po = (uint64_t)rows_all * kvs * p.d_v * 4;
+      plan->workspace_bytes = ((po + 255) / 256) * 256 + (uint64_t)rows_all * kvs * 2 * 4;
+      plan->combine_groups = (int32_t)ceil_div(rows_all, kCombineRows);
+    }
     return SDPA_OK;
   }
 

@@ -55,7 +55,12 @@ void prefill_kernel(const PrefillArgs a) {
   const int l32 = lane & 31;
 
   // ---- work decode -------------------------------------------------------
+  // kv_splits workgroups share one tile's K blocks (consecutive after the
+  // remap, so on one XCD): workgroup ksp of them takes its KS key ranges
+  const int nsp = CACHED ? 1 : a.kv_splits;
   int wg = remap_xcd(blockIdx.x, a.num_groups);
+  const int ksp = nsp > 1 ? wg % nsp : 0;
+  if (nsp > 1) wg /= nsp;
   int qt = wg % a.q_tiles;
   int rest = wg / a.q_tiles;
   const int hg = rest % a.head_groups;
@@ -83,23 +88,41 @@ void prefill_kernel(const PrefillArgs a) {
   const bool row_ok = head_ok && qrow < Sq;
   typedef uint16_t elem_t;
   elem_t* __restrict__ optr = (elem_t*)a.o;
+  // split across workgroups: this row's partial (row-major over (batch, query
+  // row, query head), then split); formed where it is stored, so that
+  // nothing of it stays live through the mainloop
+  auto partial_row = [&]() __attribute__((always_inline)) -> size_t {
+    return ((size_t)(b * Sq + qrow) * a.head_q + h) * nsp + ksp;
+  };
 
-  if (n_blocks == 0) {  // no visible key for any row of this workgroup
+  // Key ranges: the tile's n_blocks blocks are cut into R = KS * kv_splits
+  // ranges of cnt = ceil(n_blocks / R) blocks; range r = ksp * KS + kr_i
+  // takes blocks [r * cnt, (r + 1) * cnt).  Blocks past n_blocks lie past
+  // every visible key and are masked entirely, so all ranges of a workgroup
+  // run the same number of iterations.
+  const int nr = KS * nsp;
+  const int cnt = nr == 1 ? n_blocks : (n_blocks + nr - 1) / nr;
+  const int kb0 = (ksp * KS + kr_i) * cnt;
+  const int n_unmasked = min(max(n_full - kb0, 0), cnt);
+
+  // no visible key for any row of this workgroup (or, split across
+  // workgroups, none in its ranges): O = 0 and lse = -inf, or the empty
+  // partial (max -inf, sum 0, zero output)
+  if (n_blocks == 0 || ksp * KS * cnt >= n_blocks) {
     if (row_ok && kr_i == 0) {
-      elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
-      for (int c = hl * (DV / 2); c < (hl + 1) * (DV / 2); c += 8) *(u32x4_t*)(orow + c) = u32x4_t{0, 0, 0, 0};
-      if (a.lse != nullptr && hl == 0) a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = -INFINITY;
+      if (nsp > 1) {
+        const size_t prow = partial_row();
+        float* po = a.part_o + prow * DV;
+        for (int c = hl * (DV / 2); c < (hl + 1) * (DV / 2); c += 4) *(f32x4_t*)(po + c) = f32x4_t{0, 0, 0, 0};
+        if (hl == 0) *(f32x2_t*)(a.part_ml + 2 * prow) = f32x2_t{-INFINITY, 0.f};
+      } else {
+        elem_t* orow = optr + ((size_t)(b * Sq + qrow) * a.head_q + h) * DV;
+        for (int c = hl * (DV / 2); c < (hl + 1) * (DV / 2); c += 8) *(u32x4_t*)(orow + c) = u32x4_t{0, 0, 0, 0};
+        if (a.lse != nullptr && hl == 0) a.lse[((size_t)b * a.head_q + h) * Sq + qrow] = -INFINITY;
+      }
     }
     return;
   }
-
-  // Key range of this wave: with two ranges, range 0 takes blocks
-  // [0, half) and range 1 blocks [half, n_blocks); when n_blocks is odd,
-  // range 1 ends with one block past the visible keys, which the mask
-  // removes entirely, so both ranges run the same number of iterations.
-  const int cnt = KS == 1 ? n_blocks : (n_blocks + 1) / 2;
-  const int kb0 = kr_i * cnt;
-  const int n_unmasked = min(max(n_full - kb0, 0), cnt);
 
   // ---- direct global -> LDS fills ------------------------------------------
   // Instruction i of this wave covers the 64 16-byte slots starting at slot
@@ -614,6 +637,22 @@ void prefill_kernel(const PrefillArgs a) {
   auto store = [&](auto t0_tag, auto t1_tag) __attribute__((always_inline)) {
     constexpr int T0 = decltype(t0_tag)::value, T1 = decltype(t1_tag)::value;
     const float l_tot = pair_sum(l_run);
+    if (nsp > 1) {
+      // split across workgroups: the unnormalized accumulators (register r
+      // of tile t holds value column 32t + 8(r/4) + 4*hl + r%4) and (m, l)
+      if (row_ok) {
+        const size_t prow = partial_row();
+        float* po = a.part_o + prow * DV + 4 * hl;
+#pragma unroll
+        for (int t = T0; t < T1; ++t)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(f32x4_t*)(po + 32 * t + 8 * q4) =
+                f32x4_t{acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]};
+        if (hl == 0 && T0 == 0) *(f32x2_t*)(a.part_ml + 2 * prow) = f32x2_t{m_run, l_tot};
+      }
+      return;
+    }
     const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
     u32x4_t runs[T1 - T0][2];
 #pragma unroll

@@ -37,7 +37,8 @@ int device_cus() {
 
 // A forced form of the 16-bit prefill kernels (for tuning sweeps and tests):
 // narrow1 / narrow2 = one wave per SIMD with one / two key ranges, occ2 = two
-// waves per SIMD, split4 = its four-key-range form; "" or "auto" = the
+// waves per SIMD, split4 = its four-key-range form, kvsplit = narrow2 with
+// the key range also split across workgroups; "" or "auto" = the
 // planner's choice.  The environment variable SDPA_PREFILL_VARIANT sets the
 // initial value, read once per process; sdpa_set_prefill_variant changes it.
 int variant_code(const char* e) {
@@ -46,6 +47,7 @@ int variant_code(const char* e) {
   if (!strcmp(e, "narrow2")) return 4;
   if (!strcmp(e, "occ2")) return 5;
   if (!strcmp(e, "split4")) return 6;
+  if (!strcmp(e, "kvsplit")) return 7;
   return -1;
 }
 
@@ -108,7 +110,9 @@ sdpa_status_t sdpa_plan(const sdpa_problem_t* problem, int is_decode, int num_cu
     set_error("problem and plan must not be NULL");
     return SDPA_ERR_NULL_PTR;
   }
-  return make_plan(*problem, is_decode != 0, num_cus, num_splits, plan, is_decode ? 0 : prefill_variant());
+  // a prefill plan is the one sdpa_prefill_fwd runs when given its workspace
+  return make_plan(*problem, is_decode != 0, num_cus, num_splits, plan, is_decode ? 0 : prefill_variant(), false,
+                   is_decode == 0);
 }
 
 sdpa_status_t sdpa_loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k,
@@ -124,7 +128,7 @@ sdpa_status_t sdpa_loop_counts(int q_len, int kv_len, int d_qk, int d_v, int blo
 size_t sdpa_prefill_workspace_bytes(const sdpa_problem_t* problem) {
   if (problem == nullptr) return 0;
   sdpa_plan_t plan;
-  if (make_plan(*problem, false, kDefaultCUs, 0, &plan) != SDPA_OK) return 0;
+  if (make_plan(*problem, false, device_cus(), 0, &plan, prefill_variant(), false, true) != SDPA_OK) return 0;
   return (size_t)plan.workspace_bytes;
 }
 
@@ -135,10 +139,12 @@ size_t sdpa_decode_workspace_bytes(const sdpa_problem_t* problem, int num_splits
   return (size_t)plan.workspace_bytes;
 }
 
-// Fills the kernel arguments of a planned prefill and launches it.
+// Fills the kernel arguments of a planned prefill and launches it; a plan
+// split across workgroups (kv_splits > 1) keeps its partials in workspace and
+// is followed by the combine.
 static sdpa_status_t prefill_launch(const sdpa_problem_t& p, const sdpa_plan_t& plan, const void* q, const void* k,
                                     const void* v, void* o, float* lse, const void* k_cache, const void* v_cache,
-                                    int32_t cache_len, int32_t cache_cap, void* stream) {
+                                    int32_t cache_len, int32_t cache_cap, void* stream, void* workspace = nullptr) {
   PrefillArgs a{};
   a.q = q;
   a.k = k;
@@ -162,7 +168,28 @@ static sdpa_status_t prefill_launch(const sdpa_problem_t& p, const sdpa_plan_t& 
   a.v_cache = v_cache;
   a.cache_len = cache_len;
   a.cache_cap = cache_cap;
-  return hip_status(launch_prefill(a, plan, p.causal != 0, (ihipStream_t*)stream), "prefill launch");
+  const int64_t rows = (int64_t)p.batch * p.q_len * p.head_q;
+  if (plan.kv_splits > 1) {
+    const uint64_t po = (uint64_t)rows * plan.kv_splits * p.d_v * 4;
+    a.kv_splits = plan.kv_splits;
+    a.part_o = (float*)workspace;
+    a.part_ml = (float*)((char*)workspace + ((po + 255) / 256) * 256);
+  }
+  sdpa_status_t st = hip_status(launch_prefill(a, plan, p.causal != 0, (ihipStream_t*)stream), "prefill launch");
+  if (st != SDPA_OK || plan.kv_splits <= 1) return st;
+  // the combine sees one row per (batch, query row, query head)
+  DecodeArgs c{};
+  c.o = o;
+  c.lse = lse;
+  c.part_o = a.part_o;
+  c.part_ml = a.part_ml;
+  c.batch = p.batch * p.q_len;
+  c.head_q = p.head_q;
+  c.num_splits = plan.kv_splits;
+  c.v_descale = a.v_descale;
+  c.lse_q_len = p.q_len;
+  return hip_status(launch_split_combine(c, p.in_dtype, p.d_v, plan.combine_groups, (ihipStream_t*)stream),
+                    "prefill combine launch");
 }
 
 sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, const void* k, const void* v,
@@ -174,23 +201,25 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
   }
   const sdpa_problem_t& p = *problem;
   sdpa_plan_t plan;
-  sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan, prefill_variant());
+  sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan, prefill_variant(), false, true);
   if (st != SDPA_OK) return st;
   if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
   if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr))) {
     set_error("q, k, v and o must not be NULL");
     return SDPA_ERR_NULL_PTR;
   }
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u)) {
-    set_error("q, k, v, o must be 16-byte aligned and lse 4-byte aligned");
+  const bool use_ws = plan.workspace_bytes > 0 && workspace != nullptr && workspace_bytes >= plan.workspace_bytes;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (use_ws && !aligned16(workspace)) ||
+      ((uintptr_t)lse & 3u)) {
+    set_error("q, k, v, o, workspace must be 16-byte aligned and lse 4-byte aligned");
     return SDPA_ERR_MISALIGNED;
   }
-  if (plan.workspace_bytes > workspace_bytes || (plan.workspace_bytes > 0 && workspace == nullptr)) {
-    set_error("workspace of %llu bytes needed, %llu given", (unsigned long long)plan.workspace_bytes,
-              (unsigned long long)workspace_bytes);
-    return SDPA_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && !use_ws) {
+    // no room for the partials: the same problem without the split
+    st = make_plan(p, false, device_cus(), 0, &plan, prefill_variant(), false, false);
+    if (st != SDPA_OK) return st;
   }
-  return prefill_launch(p, plan, q, k, v, o, lse, nullptr, nullptr, 0, 0, stream);
+  return prefill_launch(p, plan, q, k, v, o, lse, nullptr, nullptr, 0, 0, stream, workspace);
 }
 
 sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void* q, const void* k_cache,

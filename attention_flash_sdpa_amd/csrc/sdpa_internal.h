@@ -45,16 +45,20 @@ constexpr int kDecodeMaxGroup = 16;  // decode: query heads per wave (MFMA N); l
 constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
 constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
+constexpr int kMinSplitBlocks = 4;  // prefill split across workgroups: K blocks per key range, at least
 
 // Validates the problem; fills *plan.  Writes a detail message through
 // set_error() on failure.  Pure host code.
 // variant: 0 = planner's choice, 3 / 4 = the one-wave-per-SIMD 32-row
 // kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
 // 32-row kernel, 6 = its 8-wave, four-key-range form (tuning sweeps and tests
-// only).  cached: a cached-KV prefill (kv_len counts cache and new keys),
-// which the 16-bit kernels implement (not the fp8 one).
+// only), 7 = variant 4 with the key range also split across workgroups
+// (kv_splits >= 2).  cached: a cached-KV prefill (kv_len counts cache and new
+// keys), which the 16-bit kernels implement (not the fp8 one).  kv_split:
+// whether the plan may split key ranges across workgroups (the caller has a
+// workspace for the partials); cached plans never do.
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
-                        sdpa_plan_t* plan, int variant = 0, bool cached = false);
+                        sdpa_plan_t* plan, int variant = 0, bool cached = false, bool kv_split = false);
 
 sdpa_status_t loop_counts(int q_len, int kv_len, int d_qk, int d_v, int block_q, int block_k, int block_d,
                           int block_v, bool causal, sdpa_loop_counts_t* out);
@@ -85,6 +89,13 @@ struct PrefillArgs {
   int64_t mask_sb, mask_sh;
   int32_t mask_row;
   float s_nat;      // the softmax scale itself (natural-log domain)
+  // key range split across kv_splits workgroups (one-wave kernel only): each
+  // writes unnormalized fp32 partials of its rows to part_o [batch, q_len,
+  // head_q, kv_splits, d_v] and (max in log2 domain, sum) to part_ml [...,
+  // 2] instead of O and lse; 1 = no split, O and lse written directly
+  int32_t kv_splits = 1;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
 };
 
 struct DecodeArgs {
@@ -105,6 +116,11 @@ struct DecodeArgs {
   const int32_t* seq_lens;    // [batch] keys per sequence, or NULL
   const int32_t* page_table;  // [batch, pages_per_seq] physical page ids, or NULL
   int32_t num_pages, page_size, pages_per_seq;
+  // combine only: query rows per (batch, head) lse row.  The combine's rows
+  // are bh = b' * head_q + h over b' < batch; its lse goes to lse[bh] when
+  // lse_q_len <= 1 (decode), else to the prefill layout [batch / lse_q_len,
+  // head_q, lse_q_len] with b' = b * lse_q_len + i
+  int32_t lse_q_len;
 };
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
@@ -119,6 +135,9 @@ constexpr int kProbeGroups = 2048;
 int launch_hbm_read_probe(const void* data, int64_t bytes, uint32_t* sink, ihipStream_t* stream);
 
 int launch_decode(const DecodeArgs& a, const sdpa_plan_t& plan, ihipStream_t* stream);
+// the decode combine kernel alone over `groups` workgroups (the prefill's
+// split across workgroups), for 16-bit in_dtype and d_v 64 / 128
+int launch_split_combine(const DecodeArgs& a, int in_dtype, int d_v, int groups, ihipStream_t* stream);
 
 // The no-allocation decode keeps its split partials in a static device array
 // of this size (per GPU); larger problems are refused.

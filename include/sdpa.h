@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 2
+#define SDPA_ABI_VERSION 3
 
 typedef enum {
   SDPA_F16 = 0,
@@ -128,6 +128,15 @@ typedef struct sdpa_plan {
   int64_t range_iters_sum;  /* iterations summed over all ranges of all groups  */
   int32_t range_iters_max;  /* iterations of the busiest range                  */
   int32_t range_iters_min;  /* iterations of the lightest range                 */
+  /* Prefill: workgroups sharing one query tile's K blocks (1 = none).  With
+   * kv_splits > 1 each of them takes num_splits of the tile's kv_splits *
+   * num_splits equal key ranges ("Xe SDPA Forward Mainloop", section "Outer
+   * K-block loop": a K-block subrange per work item), writes unnormalized
+   * fp32 partial outputs with their running (max, sum) to the workspace, and
+   * a second kernel merges the partials of every query row (combine_groups
+   * workgroups), as the split-KV decode does.  num_groups counts all
+   * workgroups, splits included. */
+  int32_t kv_splits;
 } sdpa_plan_t;
 
 /* Tile-level loop counts of one attention head for a given tiling, in the
@@ -169,6 +178,11 @@ const char* sdpa_last_error(void);
  *                           workgroup merged at the end;
  *   "occ2"                : two waves per SIMD, one key range;
  *   "split4"              : two waves per SIMD, four key ranges of 32-key blocks;
+ *   "kvsplit"             : "narrow2" with the key range also split across
+ *                           at least two workgroups (plan.kv_splits), even on
+ *                           shapes where some ranges hold no key (sdpa_prefill_fwd
+ *                           with a workspace only; other entry points run
+ *                           "narrow2");
  *   "" / "auto" / NULL    : the planner's choice (the default).
  * The environment variable SDPA_PREFILL_VARIANT gives the initial value (read
  * once).  Unknown names return SDPA_ERR_UNSUPPORTED and change nothing.
@@ -184,7 +198,13 @@ sdpa_status_t sdpa_set_prefill_variant(const char* name);
 sdpa_status_t sdpa_plan(const sdpa_problem_t* problem, int is_decode, int num_cus,
                         int num_splits, sdpa_plan_t* plan);
 
-/* Device workspace bytes sdpa_prefill_fwd needs (0 for every current plan). */
+/* Device workspace bytes sdpa_prefill_fwd needs for the planned split of the
+ * key range across workgroups (plan.kv_splits > 1): fp32 partial outputs
+ * [batch, q_len, head_q, kv_splits, d_v] (rounded up to 256 bytes) followed
+ * by partial (max, sum) pairs [batch, q_len, head_q, kv_splits, 2].  0 when
+ * the plan does not split (most shapes: the split is planned only when the
+ * problem has too few query tiles to occupy half the GPU) and for an invalid
+ * problem. */
 size_t sdpa_prefill_workspace_bytes(const sdpa_problem_t* problem);
 
 /* Device workspace bytes sdpa_decode_fwd needs for num_splits (0 = the
@@ -201,8 +221,13 @@ size_t sdpa_decode_workspace_bytes(const sdpa_problem_t* problem, int num_splits
  *   q, k, v : device inputs in the layouts above, dtype problem->in_dtype
  *   o       : device output, dtype problem->out_dtype
  *   lse     : device fp32 [batch, head_q, q_len] or NULL
- *   workspace, workspace_bytes: may be NULL / 0 while
- *             sdpa_prefill_workspace_bytes() returns 0
+ *   workspace, workspace_bytes: caller-owned device scratch, 16-byte
+ *             aligned, of sdpa_prefill_workspace_bytes() bytes, which the
+ *             call overwrites (stream-ordered: calls that share one workspace
+ *             must be ordered on one stream).  NULL / a smaller size runs the
+ *             same problem without the cross-workgroup split (the result
+ *             agrees to rounding; it may take longer); a workspace is never
+ *             required.
  *   stream  : hipStream_t or NULL
  * batch == 0 or q_len == 0 is a successful no-op. */
 sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, const void* k,

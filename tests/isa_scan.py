@@ -295,27 +295,30 @@ def lds_dma_scalar_base(text):
 def untracked_loads_waited(text):
     """Registers filled by the asm 16-byte loads the compiler does not track
     (`global_load_dwordx4 v[..], v[..], off`) are neither read nor written
-    before the wave's first `s_waitcnt vmcnt`."""
+    between the issue of their load and the wave's first `s_waitcnt vmcnt`
+    (before the issue they still hold an earlier value, which may be read or
+    moved)."""
+    load_re = r"global_load_dwordx4 v\[\d+:\d+\], v\[\d+:\d+\], off"
     bad, n = [], 0
     for m in re.finditer(r"^(_ZN4sdpa\w+):", text, re.M):
         body = _instructions(text[m.end():text.index(".Lfunc_end", m.end())])
-        loads = [k for k, u in enumerate(body) if re.match(r"global_load_dwordx4 v\[\d+:\d+\], v\[\d+:\d+\], off", u)]
+        loads = [k for k, u in enumerate(body) if re.match(load_re, u)]
         waits = [k for k, u in enumerate(body) if u.startswith("s_waitcnt") and "vmcnt" in u]
         if not loads or not waits:
             continue
         first_wait = waits[0]
-        regs = set()
-        for k in loads:
-            if k < first_wait:
-                regs |= _vregs(_operands(body[k])[0])
+        in_flight = set()
+        for u in body[loads[0]:first_wait]:
+            if re.match(load_re, u):
+                if _vregs(_operands(u)[1]) & in_flight:
+                    bad.append(f"{m.group(1)[:60]}: {u} addressed by a load in flight")
+                in_flight |= _vregs(_operands(u)[0])
                 n += 1
-        for u in body[loads[0] + 1:first_wait]:
-            if re.match(r"global_load_dwordx4 v\[\d+:\d+\], v\[\d+:\d+\], off", u):
                 continue
             touched = set()
             for o in _operands(u):
                 touched |= _vregs(o)
-            if touched & regs:
+            if touched & in_flight:
                 bad.append(f"{m.group(1)[:60]}: {u} before the wait")
     return bad, n
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(binding.EXPORTS)
-    assert lib.sdpa_abi_version() == 2
+    assert lib.sdpa_abi_version() == 3
 
 
 def test_status_strings():

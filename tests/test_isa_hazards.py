@@ -98,3 +98,24 @@ def test_lds_dma_m0_wait_state(asm, src):
 def test_untracked_q_loads_waited_for(asm, src):
     bad, n = isa_scan.untracked_loads_waited(asm[src])
     assert n > 0 and not bad, bad[:5]
+
+
+def test_untracked_load_scan_on_hand_written_code():
+    """The scan itself: a register of a load in flight read before the wait is
+    caught, as is a later load addressed by one; its earlier value read
+    before the load issues, and any read after the wait, are not."""
+    def fn(*ins):
+        return "_ZN4sdpa1fEv:\n" + "\n".join("\t" + i for i in ins) + "\n.Lfunc_end0:\n"
+
+    ok = fn("v_mov_b32_e32 v5, v1",
+            "global_load_dwordx4 v[0:3], v[8:9], off",
+            "v_accvgpr_write_b32 a1, v4",          # not a load destination
+            "global_load_dwordx4 v[4:7], v[8:9], off offset:16",
+            "s_waitcnt vmcnt(0)",
+            "v_add_f32_e32 v10, v0, v4")
+    assert isa_scan.untracked_loads_waited(ok) == ([], 2)
+    read = fn("global_load_dwordx4 v[0:3], v[8:9], off", "v_accvgpr_write_b32 a1, v2", "s_waitcnt vmcnt(0)")
+    assert len(isa_scan.untracked_loads_waited(read)[0]) == 1
+    addr = fn("global_load_dwordx4 v[0:3], v[8:9], off", "global_load_dwordx4 v[4:7], v[2:3], off",
+              "s_waitcnt vmcnt(0)")
+    assert len(isa_scan.untracked_loads_waited(addr)[0]) == 1

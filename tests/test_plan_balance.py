@@ -15,17 +15,23 @@ from attention_flash_sdpa_amd import inputs
 def _expected(B, Sq, Sk, Hq, Hkv, causal, plan):
     """(max, min, sum) of the iterations per key range, from the definition:
     the workgroups of one query tile cover block_q rows of heads_per_group
-    heads; their K blocks reach the last key any of those rows sees."""
+    heads; their K blocks reach the last key any of those rows sees.  With
+    the split across kv_splits workgroups, the blocks are cut into
+    num_splits * kv_splits ranges of equal length, num_splits per
+    workgroup; a workgroup whose first range starts past the last block runs
+    none."""
+    ks, kvs = plan.num_splits, plan.kv_splits
     iters = []
     for qt in range(math.ceil(Sq / plan.block_q)):
         last_row = min((qt + 1) * plan.block_q, Sq) - 1
         last_key = min(last_row + Sk - Sq, Sk - 1) if causal else Sk - 1
         blocks = math.ceil((last_key + 1) / plan.block_k) if last_key >= 0 else 0
-        iters.append(math.ceil(blocks / plan.num_splits))
-    per_tile = plan.num_groups // len(iters)
+        cnt = math.ceil(blocks / (ks * kvs))
+        iters += [cnt if s * ks * cnt < blocks else 0 for s in range(kvs)]
+    per_tile = plan.num_groups // len(iters)  # workgroups per (tile, split)
     assert per_tile * len(iters) == plan.num_groups
     assert per_tile == B * Hkv * math.ceil(Hq // Hkv / plan.heads_per_group)
-    return max(iters), min(iters), sum(iters) * plan.num_splits * per_tile
+    return max(iters), min(iters), sum(iters) * ks * per_tile
 
 
 def _problem(B, Sq, Sk, Hq, Hkv, D, causal):
