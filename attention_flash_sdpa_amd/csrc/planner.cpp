@@ -166,8 +166,9 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // queries over a long key sequence): split each tile's K blocks across
     // kvs workgroups as well, up to one workgroup per CU, no range shorter
     // than kMinSplitBlocks blocks.  They write fp32 partials that a second
-    // kernel combines, which only pays when it multiplies the grid; the
-    // range count is then evened out so that no range is left empty.
+    // kernel combines, which only pays when it multiplies the grid and
+    // shortens the ranges by at least kMinSplitSaving iterations; the range
+    // count is then evened out so that no range is left empty.
     // Short-query rows are few, so the partials stay small next to K/V.
     int64_t kvs = 1;
     const int64_t rows_all = (int64_t)p.batch * p.q_len * p.head_q;
@@ -186,6 +187,8 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
         if (kvs >= 2) {
           const int64_t per = ceil_div(plan->kv_blocks, ks * kvs);  // blocks per range
           kvs = ceil_div(plan->kv_blocks, ks * per);
+          // the combine costs about what four mainloop iterations do
+          if (ceil_div(plan->kv_blocks, ks) - per < kMinSplitSaving) kvs = 1;
         } else {
           kvs = 1;
         }

@@ -1,5 +1,5 @@
 // prefill_kernel.h -- the one-wave-per-SIMD prefill kernel template
-// (prefill_kernel<T, D, DV, CAUSAL, KS, CACHED, CALIGN>), included by prefill.hip
+// (prefill_kernel<T, D, DV, CAUSAL, KS, CACHED, CALIGN, KVSPLIT>), included by prefill.hip
 // (dense keys) and prefill_cached.hip (cached prefix + new keys), which
 // compile their instantiations in parallel.  The design is described at the
 // top of prefill.hip.
@@ -24,7 +24,7 @@ __host__ __device__ constexpr int reads_in(int a, int b) {
   return c;
 }
 
-template <class T, int D, int DV, bool CAUSAL, int KS, bool CACHED, bool CALIGN = false>
+template <class T, int D, int DV, bool CAUSAL, int KS, bool CACHED, bool CALIGN = false, bool KVSPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(const PrefillArgs a) {
   constexpr int BK = kPrefillBlockK;
@@ -55,9 +55,12 @@ void prefill_kernel(const PrefillArgs a) {
   const int l32 = lane & 31;
 
   // ---- work decode -------------------------------------------------------
-  // kv_splits workgroups share one tile's K blocks (consecutive after the
-  // remap, so on one XCD): workgroup ksp of them takes its KS key ranges
-  const int nsp = CACHED ? 1 : a.kv_splits;
+  // KVSPLIT: kv_splits workgroups share one tile's K blocks (consecutive
+  // after the remap, so on one XCD): workgroup ksp of them takes its KS key
+  // ranges and writes partials (a form of its own, so that the other forms
+  // keep their compile-time range arithmetic)
+  static_assert(!(KVSPLIT && CACHED), "the cached form takes no workspace");
+  const int nsp = KVSPLIT ? a.kv_splits : 1;
   int wg = remap_xcd(blockIdx.x, a.num_groups);
   const int ksp = nsp > 1 ? wg % nsp : 0;
   if (nsp > 1) wg /= nsp;

@@ -46,6 +46,7 @@ constexpr int kDecodeWaves = 4;    // decode: waves (= splits) per workgroup
 constexpr int64_t kMaskMaxGroups = (int64_t)1 << 30;  // mask conversion: grid cap (beyond it, a grid-stride loop)
 constexpr int kDefaultCUs = 256;
 constexpr int kMinSplitBlocks = 4;  // prefill split across workgroups: K blocks per key range, at least
+constexpr int kMinSplitSaving = 5;  // ... and mainloop iterations it saves per range, at least
 
 // Validates the problem; fills *plan.  Writes a detail message through
 // set_error() on failure.  Pure host code.

@@ -177,6 +177,10 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
         align = "true" if CACHED_LEN % rstep == 0 and w.kv_len % rstep == 0 else "false"
         return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, true, {align}>",
                  p.num_groups * p.waves_per_group * 64)]
+    if p.kv_splits > 1:  # keys split across workgroups: the partials' combine follows
+        return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, false, false, true>",
+                 p.num_groups * p.waves_per_group * 64),
+                (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 256)]
     return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, false, false>",
              p.num_groups * p.waves_per_group * 64)]
 
@@ -199,6 +203,18 @@ def _cached_chunk():
 
 
 CACHED_CHUNK = _cached_chunk()
+
+
+def _split_chunk():
+    from attention_flash_sdpa_amd import inputs
+
+    # a 16-query chunk over 8192 keys: too few query tiles to fill the GPU,
+    # so the planner splits each tile's keys across workgroups
+    return inputs.Workload("short_chunk16_over8192_bf16", 1, 32, 8, 16, 8192, 128, 128, "bf16", "bf16", True, 1009,
+                           kv_sets=8)
+
+
+SPLIT_CHUNK = _split_chunk()
 MASK_SHAPE = (16, 4096, 4096)  # bool mask elements converted per call
 
 
@@ -397,11 +413,19 @@ def _summarize_trace(d):
     from attention_flash_sdpa_amd import inputs
 
     rows = _read_csv(os.path.join(d, "run_kernel_trace.csv"))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # a prefill split across workgroups launches its kernel and then the
+    # combine, whose name and grid are the decode's: told apart by the launch
+    # beside it (one stream, in order)
+    for i, r in enumerate(rows):
+        r["_next"] = rows[i + 1]["Kernel_Name"] if i + 1 < len(rows) else ""
+        r["_prev"] = rows[i - 1]["Kernel_Name"] if i > 0 else ""
     cmd = open(os.path.join(d, "command.txt")).read().strip() if os.path.exists(os.path.join(d, "command.txt")) \
         else "(command not recorded)"
     todo = [(wname, w, False) for wname, w in inputs.WORKLOADS.items()]
     todo.append(("splitkv_decode_bf16_paged_16_and_64", inputs.WORKLOADS["splitkv_decode_bf16"], True))
     todo.append((CACHED_CHUNK.name, CACHED_CHUNK, "cached"))
+    todo.append((SPLIT_CHUNK.name, SPLIT_CHUNK, False))
     todo.append(("mask_convert_16x4096x4096", None, "mask"))
     todo.append((MASKED.name, MASKED, "masked"))
     for wname, w, paged in todo:
@@ -411,12 +435,20 @@ def _summarize_trace(d):
             kernels = [(MASKED_KERNEL, None)]
         else:
             kernels = _kernels_of(sdpa, w, paged=paged is True, cached=paged == "cached")
+        split = w is not None and not w.decode and paged is False and \
+            sdpa.plan(_problem(sdpa, w), num_cus=256).kv_splits > 1
         for kname, grid in kernels:
             if paged is True and "true>" not in kname:
                 continue  # the combine kernel is the dense one
 
             def hit(r):
-                return kname in r["Kernel_Name"] and (grid is None or int(r["Grid_Size_X"]) == grid)
+                if kname not in r["Kernel_Name"] or (grid is not None and int(r["Grid_Size_X"]) != grid):
+                    return False
+                if kname.startswith("prefill_kernel<"):
+                    return ("decode_combine_kernel" in r["_next"]) == split
+                if kname.startswith("decode_combine_kernel<"):
+                    return ("prefill_kernel<" in r["_prev"]) == split
+                return True
 
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if hit(r)]
             if not durs:
@@ -425,8 +457,8 @@ def _summarize_trace(d):
             grid = int(r0["Grid_Size_X"])
             fam = kname.split("<")[0]
             out = os.path.join(ROOT, "profiles", f"{fam}_{wname}_trace.txt")
-            byte_bound = w is None or w.decode
-            alg = 3 * int(np.prod(MASK_SHAPE)) if w is None else (w.bytes_moved() if w.decode else w.flops())
+            byte_bound = w is None or w.decode or split
+            alg = 3 * int(np.prod(MASK_SHAPE)) if w is None else (w.bytes_moved() if byte_bound else w.flops())
             with open(out, "w") as f:
                 f.write(f"kernel: {r0['Kernel_Name']}\nworkload: {wname}\n")
                 f.write(f"command: {cmd}\n")
@@ -441,6 +473,8 @@ def _summarize_trace(d):
                             f"GB/s at median: {alg / statistics.median(durs) / 1e3:.1f}\n")
                 elif byte_bound:
                     f.write(f"algorithmic bytes per call (Q+K+V+O): {alg}\n")
+                    if split:
+                        f.write("the call is this kernel and the combine of its partials\n")
                 else:
                     med = statistics.median(durs)
                     f.write(f"algorithmic flop per call: {alg}\nTFLOP/s at median: {alg / med / 1e6:.1f}\n")
@@ -802,6 +836,54 @@ def main():
     del cqd, ckcd, cvcd, ckd, cvd
 
     _progress("cached prefill leg done")
+    # ------- short chunk over long keys: the split across workgroups -------
+    sw = SPLIT_CHUNK
+    g = torch.Generator().manual_seed(sw.seed)
+    sq = torch.randn(sw.batch, sw.q_len, sw.head_q, sw.d_qk, generator=g).to(torch.bfloat16)
+    s_sets_cpu = [tuple(torch.randn(sw.batch, sw.kv_len, sw.head_kv, sw.d_qk, generator=g).to(torch.bfloat16)
+                        for _ in range(2)) for _ in range(sw.kv_sets)]
+    sqd = sq.to(dev)
+    s_sets = [(a_.to(dev), b_.to(dev)) for a_, b_ in s_sets_cpu]
+    so = torch.empty(sw.batch, sw.q_len, sw.head_q, sw.d_v, dtype=torch.bfloat16, device=dev)
+    splan = sdpa.plan(_problem(sdpa, sw), num_cus=ncu)
+    sws = torch.empty(max(splan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    s_none = torch.empty(0, dtype=torch.uint8, device=dev)
+
+    def sstep(i, ws_=sws):
+        kk, vv = s_sets[i % len(s_sets)]
+        sdpa.prefill(sqd, kk, vv, causal=True, scale=sw.scale, out=so, workspace=ws_)
+
+    sn = max(args.steps // 4, MIN_LEG_CALLS * sw.kv_sets)
+    seager = _time(sstep, sn, args.warmup, stream)
+    sms = _graph_time(sstep, sn, args.warmup, period=sw.kv_sets)
+    s1ms = _graph_time(lambda i: sstep(i, s_none), sn, args.warmup, period=sw.kv_sets)
+    sstep(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sref = oracle.sdpa(sq, *s_sets_cpu[0], scale=sw.scale, causal=True, want_lse=False)["out"]
+    ssec = time.perf_counter() - t0
+    serr = float(np.abs(so.double().cpu().numpy() - sref).max())
+    snan = int(torch.isnan(so.float()).sum().item())
+    sgbs = sw.bytes_moved() / (sms * 1e-3) / 1e9
+    split_line = {"workload": f"{sw.q_len}-query chunk over {sw.kv_len} keys, Hq {sw.head_q} / Hkv {sw.head_kv}, "
+                              f"d {sw.d_qk}, bf16, causal; {sw.kv_sets} rotating K/V sets "
+                              f"({sw.kv_sets * 2 * sw.kv_len * sw.head_kv * sw.d_qk * 2 >> 20} MiB, past the "
+                              f"256 MiB last-level cache)",
+                  "value": round(sgbs, 2), "unit": "GB/s", "ms_per_call": round(sms, 6),
+                  "eager_ms_per_call": round(seager, 6), "steps": _graph_chunk(sn, sw.kv_sets)[0],
+                  "kv_splits": splan.kv_splits, "key_ranges_per_group": splan.num_splits,
+                  "grid": splan.num_groups, "workspace_bytes": splan.workspace_bytes,
+                  "unsplit_ms_per_call": round(s1ms, 6), "speedup_over_unsplit": round(s1ms / sms, 3),
+                  "tflops": round(sw.flops() / (sms * 1e-3) / 1e12, 3),
+                  "algorithmic_bytes": sw.bytes_moved(),
+                  "roofline": {"bound": "hbm", "achieved": round(sgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(sgbs / PEAK_HBM_GBS, 5), "traffic": None},
+                  "parity": {"max_abs_err": serr, "nan": snan, "rows": sw.q_len * sw.head_q},
+                  "cpu_baseline": _cpu_line(round(sw.bytes_moved() / ssec / 1e9, 3), "GB/s",
+                                            torch.get_num_threads(),
+                                            f"whole chunk (one K/V set) through the oracle in {ssec:.2f} s, fp64")}
+    del sqd, s_sets, sws
+    _progress("split prefill leg done")
     # ------- boolean -> additive mask conversion, 4 rotating buffer sets -------
     from oracle import mask as omask
 
@@ -958,6 +1040,7 @@ def main():
         "decode_paged": paged_lines[64],
         "decode_paged_16": paged_lines[16],
         "prefill_cached": cached_line,
+        "prefill_split": split_line,
         "mask_convert": mask_line,
         "prefill_masked": masked_line,
         "other_workloads": extra,

@@ -88,7 +88,7 @@ AUTO = [
     (2, 5, 3000, 8, 2, 64, torch.float16, True),
     (1, 64, 4096, 8, 8, 128, torch.bfloat16, True),     # two 32-row tiles of one head per workgroup
     (1, 1, 2048, 4, 1, 128, torch.bfloat16, False),     # one query row
-    (3, 40, 999, 6, 3, 64, torch.bfloat16, True),       # ragged key count, odd group
+    (3, 40, 1999, 6, 3, 64, torch.bfloat16, True),      # ragged key count, odd group
     (1, 33, 4000, 2, 1, 128, torch.float16, False),     # a ragged second query tile
     (1, 8, 16384, 16, 4, 64, torch.bfloat16, True),
 ]

@@ -133,13 +133,20 @@ def test_short_chunk_over_long_keys_splits_to_fill_the_gpu():
     assert p.combine_groups == rows // 4
 
 
-@pytest.mark.parametrize("Sk", [1000, 2048, 2049, 5000, 65536])
+@pytest.mark.parametrize("Sk", [1000, 1200, 2048, 2049, 5000, 65536])
 def test_auto_split_leaves_no_range_empty_on_full_attention(Sk):
+    """Full attention: every split has work, ranges of four blocks or more,
+    at least five iterations saved per range, at most one workgroup per CU
+    plus one tile's worth from rounding."""
     p = sdpa.plan(_problem(1, 8, Sk, 16, 4, 64, False), num_cus=256)
+    unsplit = math.ceil(p.kv_blocks / p.num_splits)
     if p.kv_splits > 1:
         assert p.range_iters_min == p.range_iters_max  # no empty workgroup
         assert p.range_iters_max >= 4  # no range shorter than four blocks
+        assert unsplit - p.range_iters_max >= 5
         assert p.num_groups <= 256 + p.num_groups // p.kv_splits
+    else:
+        assert unsplit <= 9  # two ranges of half the blocks would save fewer than five
 
 
 def test_workload_plans_do_not_split():
