@@ -27,10 +27,11 @@ from .binding import (  # noqa: F401
     plan,
     prefill,
     prefill_cached,
+    prefill_cached_workspace_bytes,
     prefill_masked,
     prefill_workspace_bytes,
     set_prefill_variant,
 )
 
-__all__ = ["prefill", "prefill_workspace_bytes", "prefill_cached", "prefill_masked", "decode", "decode_noalloc", "decode_paged", "decode_workspace", "hbm_read_probe", "mask_convert", "plan",
+__all__ = ["prefill", "prefill_workspace_bytes", "prefill_cached", "prefill_cached_workspace_bytes", "prefill_masked", "decode", "decode_noalloc", "decode_paged", "decode_workspace", "hbm_read_probe", "mask_convert", "plan",
            "loop_counts", "set_prefill_variant", "make_problem", "load", "Problem", "Plan", "SdpaError", "F16", "BF16", "FP8_E4M3"]

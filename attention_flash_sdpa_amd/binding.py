@@ -26,6 +26,7 @@ EXPORTS = (
     "sdpa_prefill_workspace_bytes", "sdpa_decode_workspace_bytes", "sdpa_prefill_fwd", "sdpa_decode_fwd",
     "sdpa_decode_paged_fwd", "sdpa_prefill_cached_fwd", "sdpa_mask_convert", "sdpa_prefill_masked_fwd",
     "sdpa_loop_counts", "sdpa_set_prefill_variant", "sdpa_decode_fwd_noalloc", "sdpa_hbm_read_probe",
+    "sdpa_prefill_cached_workspace_bytes",
 )
 
 
@@ -97,6 +98,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_set_prefill_variant.argtypes = [ctypes.c_char_p]
     lib.sdpa_prefill_workspace_bytes.restype = sz
     lib.sdpa_prefill_workspace_bytes.argtypes = [P]
+    lib.sdpa_prefill_cached_workspace_bytes.restype = sz
+    lib.sdpa_prefill_cached_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.sdpa_decode_workspace_bytes.restype = sz
     lib.sdpa_decode_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.sdpa_prefill_fwd.restype = ctypes.c_int
@@ -109,7 +112,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_mask_convert.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
     lib.sdpa_hbm_read_probe.restype = ctypes.c_int
     lib.sdpa_hbm_read_probe.argtypes = [vp, ctypes.c_int64, vp, vp]
-    lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.sdpa_prefill_cached_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp, sz,
+                                            vp]
     lib.sdpa_decode_fwd.restype = ctypes.c_int
     lib.sdpa_decode_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     lib.sdpa_decode_fwd_noalloc.restype = ctypes.c_int
@@ -262,26 +266,43 @@ def prefill(q, k, v, *, scale=None, causal=False, out=None, lse=None, descale=(1
                       in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=causal, scale=scale,
                       descale=descale)
     lib = load()
-    if workspace is None:
-        ws_bytes = lib.sdpa_prefill_workspace_bytes(ctypes.byref(pr))
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
-    else:
-        _require(workspace.dtype == torch.uint8 and workspace.is_contiguous() and workspace.device == q.device,
-                 "workspace must be a contiguous uint8 tensor on q's device")
-        ws_bytes = workspace.numel()
-        ws = workspace if ws_bytes else None
+    ws, ws_bytes = _prefill_workspace(workspace, lib.sdpa_prefill_workspace_bytes(ctypes.byref(pr)), q.device)
     _check(lib.sdpa_prefill_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                                 ws_bytes, _stream_handle(stream)))
     return out
 
 
+def _prefill_workspace(workspace, need, device):
+    """(tensor or None, bytes) for a prefill call: `workspace` as given (an
+    empty one passes NULL), or a new one of `need` bytes when None."""
+    import torch
+
+    if workspace is None:
+        return (torch.empty(need, dtype=torch.uint8, device=device) if need else None), need
+    _require(workspace.dtype == torch.uint8 and workspace.is_contiguous() and workspace.device == device,
+             "workspace must be a contiguous uint8 tensor on q's device")
+    return (workspace if workspace.numel() else None), workspace.numel()
+
+
+def prefill_cached_workspace_bytes(q, k, v, *, cache_len, causal=False) -> int:
+    """Workspace bytes ``prefill_cached`` uses for a chunk (q, k, v: its
+    queries and new keys) over ``cache_len`` cached keys (0 unless the
+    planner splits the keys across workgroups)."""
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    pr = make_problem(batch=B, q_len=Sq, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=v.shape[-1],
+                      in_dtype=_dtype_code(q), out_dtype=_dtype_code(q), causal=causal, scale=1.0)
+    return int(load().sdpa_prefill_cached_workspace_bytes(ctypes.byref(pr), int(cache_len)))
+
+
 def prefill_cached(q, k_cache, v_cache, k, v, *, cache_len, scale=None, causal=False, out=None, lse=None,
-                   stream=None):
+                   workspace=None, stream=None):
     """Cached-KV (chunked) prefill (``sdpa_prefill_cached_fwd``): the chunk's
     queries q [B, Sq, Hq, D] attend to cache keys 0 .. cache_len-1 of
     k_cache / v_cache [B, cap, Hkv, D|Dv] followed by the chunk's own keys
     k / v [B, Sk, Hkv, D|Dv]; with ``causal`` only the new keys are masked
-    (bottom-right, Sq <= Sk).  Returns O [B, Sq, Hq, Dv]."""
+    (bottom-right, Sq <= Sk).  Returns O [B, Sq, Hq, Dv].  ``workspace`` as
+    for ``prefill`` (``prefill_cached_workspace_bytes``)."""
     import torch
 
     _check_inputs(("q", "k_cache", "v_cache", "k", "v"), (q, k_cache, v_cache, k, v))
@@ -304,9 +325,12 @@ def prefill_cached(q, k_cache, v_cache, k, v, *, cache_len, scale=None, causal=F
         scale = 1.0 / math.sqrt(D)
     pr = make_problem(batch=B, q_len=Sq, kv_len=Sk, head_q=Hq, head_kv=Hkv, d_qk=D, d_v=Dv,
                       in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=causal, scale=scale)
-    _check(load().sdpa_prefill_cached_fwd(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len),
-                                          int(k_cache.shape[1]), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                          _stream_handle(stream)))
+    lib = load()
+    ws, ws_bytes = _prefill_workspace(workspace, lib.sdpa_prefill_cached_workspace_bytes(ctypes.byref(pr),
+                                                                                         int(cache_len)), q.device)
+    _check(lib.sdpa_prefill_cached_fwd(ctypes.byref(pr), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(cache_len),
+                                       int(k_cache.shape[1]), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
+                                       ws_bytes, _stream_handle(stream)))
     return out
 
 

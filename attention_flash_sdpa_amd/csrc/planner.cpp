@@ -173,7 +173,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     int64_t kvs = 1;
     const int64_t rows_all = (int64_t)p.batch * p.q_len * p.head_q;
     const bool one_wave = plan->kernel == kid && kid != kPrefillFp8D192 && ks == 2;
-    if (kv_split && !cached && one_wave && groups > 0 && (variant == 0 || variant == 7)) {
+    if (kv_split && one_wave && groups > 0 && (variant == 0 || variant == 7)) {
       if (variant == 7) {
         // forced (tests): at least two workgroups, as many as the blocks
         // allow, even when some of their ranges then hold no block

@@ -59,7 +59,6 @@ void prefill_kernel(const PrefillArgs a) {
   // after the remap, so on one XCD): workgroup ksp of them takes its KS key
   // ranges and writes partials (a form of its own, so that the other forms
   // keep their compile-time range arithmetic)
-  static_assert(!(KVSPLIT && CACHED), "the cached form takes no workspace");
   const int nsp = KVSPLIT ? a.kv_splits : 1;
   int wg = remap_xcd(blockIdx.x, a.num_groups);
   const int ksp = nsp > 1 ? wg % nsp : 0;

@@ -222,9 +222,21 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
   return prefill_launch(p, plan, q, k, v, o, lse, nullptr, nullptr, 0, 0, stream, workspace);
 }
 
+size_t sdpa_prefill_cached_workspace_bytes(const sdpa_problem_t* problem, int32_t cache_len) {
+  if (problem == nullptr || cache_len < 0 || problem->kv_len < 0 ||
+      (int64_t)problem->kv_len + cache_len > INT32_MAX)
+    return 0;
+  sdpa_problem_t vp = *problem;
+  vp.kv_len = cache_len + problem->kv_len;
+  sdpa_plan_t plan;
+  if (make_plan(vp, false, device_cus(), 0, &plan, prefill_variant(), cache_len > 0, true) != SDPA_OK) return 0;
+  return (size_t)plan.workspace_bytes;
+}
+
 sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void* q, const void* k_cache,
                                       const void* v_cache, int32_t cache_len, int32_t cache_cap, const void* k,
-                                      const void* v, void* o, float* lse, void* stream) {
+                                      const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
   clear_error();
   if (problem == nullptr) {
     set_error("problem must not be NULL");
@@ -243,27 +255,24 @@ sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void*
     set_error("cache_len + kv_len out of range (%d + %d)", cache_len, p.kv_len);
     return SDPA_ERR_BAD_SHAPE;
   }
-  if (cache_len == 0) {  // nothing cached: the plain prefill
-    sdpa_plan_t plan;
-    sdpa_status_t st = make_plan(p, false, device_cus(), 0, &plan, prefill_variant());
-    if (st != SDPA_OK) return st;
-    if (p.batch == 0 || p.q_len == 0) return SDPA_OK;
-    if (o == nullptr || q == nullptr || (p.kv_len > 0 && (k == nullptr || v == nullptr))) {
-      set_error("q, k, v and o must not be NULL");
-      return SDPA_ERR_NULL_PTR;
-    }
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u)) {
-      set_error("q, k, v, o must be 16-byte aligned and lse 4-byte aligned");
-      return SDPA_ERR_MISALIGNED;
-    }
-    return prefill_launch(p, plan, q, k, v, o, lse, nullptr, nullptr, 0, 0, stream);
-  }
+  if (cache_len == 0)  // nothing cached: the plain prefill
+    return sdpa_prefill_fwd(problem, q, k, v, o, lse, workspace, workspace_bytes, stream);
   // one sequence of cache_len + kv_len keys for the planner and the kernel
   sdpa_problem_t vp = p;
   vp.kv_len = cache_len + p.kv_len;
   sdpa_plan_t plan;
-  sdpa_status_t st = make_plan(vp, false, device_cus(), 0, &plan, prefill_variant(), true);
+  sdpa_status_t st = make_plan(vp, false, device_cus(), 0, &plan, prefill_variant(), true, true);
   if (st != SDPA_OK) return st;
+  const bool use_ws = plan.workspace_bytes > 0 && workspace != nullptr && workspace_bytes >= plan.workspace_bytes;
+  if (use_ws && !aligned16(workspace)) {
+    set_error("workspace must be 16-byte aligned");
+    return SDPA_ERR_MISALIGNED;
+  }
+  if (plan.workspace_bytes > 0 && !use_ws) {
+    // no room for the partials: the same problem without the split
+    st = make_plan(vp, false, device_cus(), 0, &plan, prefill_variant(), true, false);
+    if (st != SDPA_OK) return st;
+  }
   if ((int64_t)cache_cap * p.head_kv * (p.d_qk > p.d_v ? p.d_qk : p.d_v) >= (int64_t)1 << 31) {
     set_error("one batch entry of the cache exceeds 2^31 elements (cache_cap=%d)", cache_cap);
     return SDPA_ERR_BAD_SHAPE;
@@ -279,7 +288,7 @@ sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void*
     set_error("q, k, v, o, k_cache, v_cache must be 16-byte aligned and lse 4-byte aligned");
     return SDPA_ERR_MISALIGNED;
   }
-  return prefill_launch(vp, plan, q, k, v, o, lse, k_cache, v_cache, cache_len, cache_cap, stream);
+  return prefill_launch(vp, plan, q, k, v, o, lse, k_cache, v_cache, cache_len, cache_cap, stream, workspace);
 }
 
 sdpa_status_t sdpa_mask_convert(const uint8_t* mask, void* out, int64_t n, int32_t out_dtype, void* stream) {

@@ -57,7 +57,7 @@ constexpr int kMinSplitSaving = 5;  // ... and mainloop iterations it saves per 
 // (kv_splits >= 2).  cached: a cached-KV prefill (kv_len counts cache and new
 // keys), which the 16-bit kernels implement (not the fp8 one).  kv_split:
 // whether the plan may split key ranges across workgroups (the caller has a
-// workspace for the partials); cached plans never do.
+// workspace for the partials).
 sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, int num_splits,
                         sdpa_plan_t* plan, int variant = 0, bool cached = false, bool kv_split = false);
 

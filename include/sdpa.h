@@ -252,12 +252,22 @@ sdpa_status_t sdpa_prefill_fwd(const sdpa_problem_t* problem, const void* q, con
  *              be NULL when cache_len == 0 (then this is sdpa_prefill_fwd)
  *   k, v     : [batch, kv_len, head_kv, d_qk|d_v] (the chunk's own keys)
  *   o, lse   : as for sdpa_prefill_fwd
+ *   workspace, workspace_bytes: as for sdpa_prefill_fwd, sized by
+ *             sdpa_prefill_cached_workspace_bytes(problem, cache_len): a
+ *             short chunk over a long cache spreads its keys over several
+ *             workgroups; NULL / smaller runs it unsplit
  * 16-bit inputs only (fp16/bf16, d 64 or 128; fp8 gives
- * SDPA_ERR_UNSUPPORTED).  No workspace; errors as for sdpa_prefill_fwd. */
+ * SDPA_ERR_UNSUPPORTED).  Errors as for sdpa_prefill_fwd. */
 sdpa_status_t sdpa_prefill_cached_fwd(const sdpa_problem_t* problem, const void* q,
                                       const void* k_cache, const void* v_cache, int32_t cache_len,
                                       int32_t cache_cap, const void* k, const void* v, void* o,
-                                      float* lse, void* stream);
+                                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace bytes sdpa_prefill_cached_fwd uses for a chunk over
+ * cache_len cached keys: the layout of sdpa_prefill_workspace_bytes for the
+ * cache_len + kv_len keys of the whole sequence; 0 when the plan does not
+ * split and for an invalid problem. */
+size_t sdpa_prefill_cached_workspace_bytes(const sdpa_problem_t* problem, int32_t cache_len);
 
 /* Boolean -> additive mask conversion, the memory-bound mask_convert kernel
  * of "xe2-sdp-kernels" (section "Performance testing"), producing the full

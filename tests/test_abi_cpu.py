@@ -293,7 +293,7 @@ def test_cached_prefill_argument_errors_before_any_launch():
 
     def call(problem, cache_len=1024, cap=1024, kc=a, k=a, q=a):
         return lib.sdpa_prefill_cached_fwd(None if problem is None else ctypes.byref(problem), q, kc, kc, cache_len,
-                                           cap, k, k, a, null, null)
+                                           cap, k, k, a, null, null, 0, null)
 
     pr = _problem(w, q_len=512, kv_len=512)
     assert call(None) == 1

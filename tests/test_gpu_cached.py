@@ -1,5 +1,6 @@
 """GPU parity of the cached-KV (chunked) prefill (``sdpa_prefill_cached_fwd``)
-against the fp64 oracle ``oracle.cached.prefill_cached``.
+against the fp64 oracle ``oracle.cached.prefill_cached``, with and without
+the keys split across workgroups.
 
 Cache tensors carry slots past cache_len filled with NaN, so a read of a slot
 that holds no key shows in the output.  Bar as for the plain prefill: no NaN,
@@ -55,8 +56,12 @@ def _case(dev, q, kc, vc, k, v, *, cache_len, causal, scale):
     B, Sq, Hq, _ = q.shape
     out = torch.full((B, Sq, Hq, v.shape[-1]), float("nan"), dtype=q.dtype, device=dev)
     lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    # a key range split across workgroups keeps partials in the workspace:
+    # NaN bytes first, so a partial row left unwritten shows in the output
+    n = sdpa.prefill_cached_workspace_bytes(q, k, v, cache_len=cache_len, causal=causal)
+    ws = torch.full((max(n, 16),), 255, dtype=torch.uint8, device=dev)
     sdpa.prefill_cached(*(t.to(dev) for t in (q, kc, vc, k, v)), cache_len=cache_len, causal=causal, scale=scale,
-                        out=out, lse=lse)
+                        out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     ref = oc.prefill_cached(q, kc, vc, k, v, cache_len=cache_len, scale=scale, causal=causal)
     got = out.double().cpu().numpy()
@@ -91,7 +96,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["", "narrow1", "narrow2", "occ2", "split4"])
+@pytest.mark.parametrize("variant", ["", "narrow1", "narrow2", "occ2", "split4", "kvsplit"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_q{c[1]}_c{c[2]}of{c[3]}_k{c[4]}_h{c[5]}x{c[6]}_d{c[7]}_"
                                              f"{'causal' if c[9] else 'full'}" for c in CASES])
 def test_cached_prefill(dev, case, variant, prefill_variant):
@@ -138,6 +143,17 @@ def test_cached_prefill_chunk_workload_full_size(dev):
     _say("cached prefill chunk workload 512 over 3584")
     q, kc, vc, k, v = _draw(B, Sq, Sc, Sc, Sq, Hq, Hkv, D, torch.bfloat16, 1006)
     _case(dev, q, kc, vc, k, v, cache_len=Sc, causal=True, scale=1 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("cache_len,new", [(8176, 16), (8000, 64), (5000, 3)])
+def test_short_chunk_over_long_cache_splits(dev, cache_len, new):
+    """A short chunk over a long cache: the planner spreads each tile's keys
+    over several workgroups (the partials merged by the combine kernel)."""
+    B, Sq, Hq, Hkv, D = 1, min(new, 16), 32, 8, 128
+    _say(f"split cached prefill: {Sq} queries, {new} new keys over {cache_len} cached")
+    q, kc, vc, k, v = _draw(B, Sq, cache_len, cache_len + 7, new, Hq, Hkv, D, torch.bfloat16, cache_len + new)
+    assert sdpa.prefill_cached_workspace_bytes(q, k, v, cache_len=cache_len, causal=True) > 0
+    _case(dev, q, kc, vc, k, v, cache_len=cache_len, causal=True, scale=1 / math.sqrt(D))
 
 
 def test_cached_prefill_rejects_more_queries_than_new_keys(dev):

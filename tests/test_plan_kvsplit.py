@@ -173,3 +173,19 @@ def test_workspace_query_matches_the_plan(prefill_variant):
             assert (p.workspace_bytes > 0) == (p.kv_splits > 1)
             if variant == "narrow2":
                 assert p.kv_splits == 1
+
+
+def test_cached_workspace_query_covers_cache_and_chunk(prefill_variant):
+    """The cached prefill plans the whole sequence (cache + chunk): a 16-token
+    chunk over 8,176 cached keys gets the workspace of a 16 x 8,192 prefill;
+    nothing cached is the plain prefill's query."""
+    lib = sdpa.load()
+    chunk = _problem(1, 16, 16, 32, 8, 128, True)
+    whole = sdpa.plan(_problem(1, 16, 8192, 32, 8, 128, True), num_cus=0)
+    assert whole.kv_splits > 1
+    assert lib.sdpa_prefill_cached_workspace_bytes(ctypes.byref(chunk), 8176) == whole.workspace_bytes
+    assert lib.sdpa_prefill_cached_workspace_bytes(ctypes.byref(chunk), 0) == \
+        lib.sdpa_prefill_workspace_bytes(ctypes.byref(chunk)) == 0
+    assert lib.sdpa_prefill_cached_workspace_bytes(ctypes.byref(chunk), -1) == 0
+    prefill_variant("narrow2")
+    assert lib.sdpa_prefill_cached_workspace_bytes(ctypes.byref(chunk), 8176) == 0
