@@ -164,7 +164,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     }
     // Even the two-range split leaves more than half the CUs idle (short
     // queries over a long key sequence): split each tile's K blocks across
-    // kvs workgroups as well, up to one workgroup per CU, no range shorter
+    // kvs workgroups as well, at most one workgroup per CU, no range shorter
     // than kMinSplitBlocks blocks.  They write fp32 partials that a second
     // kernel combines, which only pays when it multiplies the grid and
     // shortens the ranges by at least kMinSplitSaving iterations; the range
@@ -181,7 +181,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
         if (kvs > plan->kv_blocks) kvs = plan->kv_blocks;
         if (kvs < 2) kvs = 2;
       } else if (2 * groups <= num_cus) {
-        kvs = ceil_div(num_cus, groups);
+        kvs = num_cus / groups;  // whole rounds: no workgroup waits for a free CU
         const int64_t by_len = plan->kv_blocks / (ks * kMinSplitBlocks);
         if (kvs > by_len) kvs = by_len;
         if (kvs >= 2) {

@@ -1,5 +1,5 @@
 """Seeded random shapes for the paged / variable-length decode, the cached
-prefill and the masked prefill, each against its fp64 oracle (the bar of the
+prefill, the masked prefill and the split prefill, each against its fp64 oracle (the bar of the
 dedicated tests: no NaN, max |gpu - oracle| <= 2e-2).  The shapes are drawn
 once from a fixed seed, so every run checks the same cases."""
 import math
@@ -134,3 +134,37 @@ def test_random_masked_prefill(dev, case):
     torch.cuda.synchronize()
     ref = om.prefill_masked(q, k, v, m, scale=1 / math.sqrt(D), causal=causal)
     _check(out, ref["out"])
+
+
+SPLIT = []
+for _ in range(10):
+    hq, hkv = _heads()
+    SPLIT.append((_R.randint(1, 3), _R.randint(1, 48), _R.randint(300, 8000), hq, hkv, _R.choice([64, 128]),
+                  _R.choice([torch.bfloat16, torch.float16]), _R.random() < 0.6, _R.random() < 0.5))
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=[f"s{i}" for i in range(len(SPLIT))])
+def test_random_split_prefill(dev, oracle_mod, case, prefill_variant):
+    """Short query chunks over long keys through sdpa_prefill_fwd with a
+    NaN-filled workspace, under the planner's choice or the forced split
+    across workgroups (lse included)."""
+    B, Sq, Sk, Hq, Hkv, D, dt, causal, forced = case
+    Sq = min(Sq, Sk) if causal else Sq
+    prefill_variant("kvsplit" if forced else None)
+    g = torch.Generator().manual_seed(Sq * 11 + Sk)
+    q = torch.randn(B, Sq, Hq, D, generator=g).to(dt)
+    k = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    v = torch.randn(B, Sk, Hkv, D, generator=g).to(dt)
+    n = sdpa.prefill_workspace_bytes(q, k, v, causal=causal)
+    _say(f"random split prefill B={B} q={Sq} k={Sk} Hq={Hq} Hkv={Hkv} D={D} {dt} causal={causal} "
+         f"forced={forced} workspace={n}")
+    ws = torch.full((max(n, 16),), 255, dtype=torch.uint8, device=dev)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    out = sdpa.prefill(q.to(dev), k.to(dev), v.to(dev), causal=causal, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle_mod.sdpa(q, k, v, scale=1 / math.sqrt(D), causal=causal)
+    _check(out, ref["out"])
+    gl = lse.double().cpu().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isneginf(gl), np.isneginf(ref["lse"]))
+    assert np.abs(gl[fin] - ref["lse"][fin]).max(initial=0) <= 1e-3

@@ -136,15 +136,14 @@ def test_short_chunk_over_long_keys_splits_to_fill_the_gpu():
 @pytest.mark.parametrize("Sk", [1000, 1200, 2048, 2049, 5000, 65536])
 def test_auto_split_leaves_no_range_empty_on_full_attention(Sk):
     """Full attention: every split has work, ranges of four blocks or more,
-    at least five iterations saved per range, at most one workgroup per CU
-    plus one tile's worth from rounding."""
+    at least five iterations saved per range, at most one workgroup per CU."""
     p = sdpa.plan(_problem(1, 8, Sk, 16, 4, 64, False), num_cus=256)
     unsplit = math.ceil(p.kv_blocks / p.num_splits)
     if p.kv_splits > 1:
         assert p.range_iters_min == p.range_iters_max  # no empty workgroup
         assert p.range_iters_max >= 4  # no range shorter than four blocks
         assert unsplit - p.range_iters_max >= 5
-        assert p.num_groups <= 256 + p.num_groups // p.kv_splits
+        assert p.num_groups <= 256
     else:
         assert unsplit <= 9  # two ranges of half the blocks would save fewer than five
 
@@ -160,6 +159,12 @@ def test_workload_plans_do_not_split():
                                causal=w.causal, scale=1.0)
         p = sdpa.plan(pr, num_cus=256)
         assert p.kv_splits == 1 and p.workspace_bytes == 0, name
+
+
+@pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv", [(3, 18, 5228, 32, 8), (1, 40, 9000, 12, 3), (2, 16, 20000, 40, 8)])
+def test_auto_split_never_needs_a_second_round(B, Sq, Sk, Hq, Hkv):
+    p = sdpa.plan(_problem(B, Sq, Sk, Hq, Hkv, 128, True), num_cus=256)
+    assert p.kv_splits > 1 and p.num_groups <= 256
 
 
 def test_workspace_query_matches_the_plan(prefill_variant):
