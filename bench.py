@@ -175,13 +175,13 @@ def _kernels_of(sdpa, w, num_cus=256, paged=False, cached=False):
         # count multiples of the 512 / D rows one fill instruction covers
         rstep = 512 // w.d_qk
         align = "true" if CACHED_LEN % rstep == 0 and w.kv_len % rstep == 0 else "false"
-        return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, true, {align}>",
+        return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, true, {align}, false>",
                  p.num_groups * p.waves_per_group * 64)]
     if p.kv_splits > 1:  # keys split across workgroups: the partials' combine follows
         return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, false, false, true>",
                  p.num_groups * p.waves_per_group * 64),
                 (f"decode_combine_kernel<sdpa::{t}, {w.d_v}>", p.combine_groups * 256)]
-    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, false, false>",
+    return [(f"prefill_kernel<sdpa::{t}, {w.d_qk}, {w.d_v}, {c}, {p.num_splits}, false, false, false>",
              p.num_groups * p.waves_per_group * 64)]
 
 
