@@ -19,8 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsdpa_mi355x.so")
-SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_cached.hip", "prefill_o2.hip",
-           "prefill_fp8.hip", "decode.hip", "mask.hip"]
+SOURCES = ["sdpa_abi.cpp", "planner.cpp", "prefill.hip", "prefill_cached.hip", "prefill_split.hip",
+           "prefill_o2.hip", "prefill_fp8.hip", "decode.hip", "mask.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -33,7 +33,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 # register files: MFMA results stay in VGPRs (the softmax reads the scores with
 # VALU instructions), AGPRs take what does not fit.
 EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "prefill_cached.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "prefill_cached.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "prefill_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, isa: bool) -> str:
@@ -52,7 +53,7 @@ def _compile(src: str, isa: bool) -> str:
 
 def build(isa: bool = False, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         outs = list(ex.map(lambda s: _compile(s, isa), SOURCES))
     if verbose or isa:
         for s, o in zip(SOURCES, outs):

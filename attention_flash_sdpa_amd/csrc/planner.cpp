@@ -137,7 +137,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // workgroup in two halves, each streamed by half of its waves and merged
     // at the end, which doubles the workgroup count.
     bool split = kid != kPrefillFp8D192 && groups < num_cus && plan->kv_blocks >= 2;
-    if (variant == 3 || variant == 5) split = false;
+    if (variant == 3 || variant == 5 || variant == 8) split = false;
     if (variant == 4 || variant == 7) split = kid != kPrefillFp8D192;
     if (split) {
       ks = 2;
@@ -146,7 +146,7 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // More workgroups than CUs: the two-waves-per-SIMD form keeps two of them
     // on every CU at once (the one-wave form would run in rounds).
     bool occ2 = kid != kPrefillFp8D192 && ks == 1 && groups > num_cus;
-    if (variant == 3 || variant == 4 || variant == 7) occ2 = false;
+    if (variant == 3 || variant == 4 || variant == 7 || variant == 8) occ2 = false;
     if (variant == 5) occ2 = kid != kPrefillFp8D192;
     if (occ2) plan->kernel = kid - kPrefillF16D64 + kOccF16D64;
     // Four key ranges of 32-key blocks, two waves (heads or query tiles) per
@@ -170,27 +170,42 @@ sdpa_status_t make_plan(const sdpa_problem_t& p, bool is_decode, int num_cus, in
     // shortens the ranges by at least kMinSplitSaving iterations; the range
     // count is then evened out so that no range is left empty.
     // Short-query rows are few, so the partials stay small next to K/V.
+    // Once split this way, one key range per workgroup (all four waves on
+    // one K/V stream: four heads of a group, or four query tiles) with twice
+    // the workgroups measured 0-8% faster than two ranges of two waves: each
+    // block is loaded once for four waves instead of twice for two.
     int64_t kvs = 1;
     const int64_t rows_all = (int64_t)p.batch * p.q_len * p.head_q;
-    const bool one_wave = plan->kernel == kid && kid != kPrefillFp8D192 && ks == 2;
-    if (kv_split && one_wave && groups > 0 && (variant == 0 || variant == 7)) {
-      if (variant == 7) {
-        // forced (tests): at least two workgroups, as many as the blocks
-        // allow, even when some of their ranges then hold no block
+    auto auto_kvs = [&](int64_t g, int r) -> int64_t {  // g workgroups per split, r ranges each
+      if (2 * g > num_cus) return 1;
+      int64_t n = num_cus / g;  // whole rounds: no workgroup waits for a free CU
+      const int64_t by_len = plan->kv_blocks / (r * kMinSplitBlocks);
+      if (n > by_len) n = by_len;
+      if (n < 2) return 1;
+      const int64_t per = ceil_div(plan->kv_blocks, r * n);  // blocks per range
+      n = ceil_div(plan->kv_blocks, r * per);
+      // the combine costs about what four mainloop iterations do
+      return ceil_div(plan->kv_blocks, r) - per < kMinSplitSaving ? 1 : n;
+    };
+    const bool one_wave = plan->kernel == kid && kid != kPrefillFp8D192 && (ks == 2 || variant == 8);
+    if (kv_split && one_wave && groups > 0 && (variant == 0 || variant == 7 || variant == 8)) {
+      if (variant == 7 || variant == 8) {
+        // forced (tests): two ranges per workgroup (7) or one (8), at least
+        // two workgroups, as many as the blocks allow, even when some of
+        // their ranges then hold no block
         kvs = ceil_div(num_cus, groups);
         if (kvs > plan->kv_blocks) kvs = plan->kv_blocks;
         if (kvs < 2) kvs = 2;
-      } else if (2 * groups <= num_cus) {
-        kvs = num_cus / groups;  // whole rounds: no workgroup waits for a free CU
-        const int64_t by_len = plan->kv_blocks / (ks * kMinSplitBlocks);
-        if (kvs > by_len) kvs = by_len;
-        if (kvs >= 2) {
-          const int64_t per = ceil_div(plan->kv_blocks, ks * kvs);  // blocks per range
-          kvs = ceil_div(plan->kv_blocks, ks * per);
-          // the combine costs about what four mainloop iterations do
-          if (ceil_div(plan->kv_blocks, ks) - per < kMinSplitSaving) kvs = 1;
-        } else {
-          kvs = 1;
+      } else if ((kvs = auto_kvs(groups, ks)) > 1) {
+        int hp1, qt1;
+        const int64_t g1 = shape(kPrefillWaves, &hp1, &qt1);
+        const int64_t kvs1 = auto_kvs(g1, 1);
+        if (kvs1 > 1 && g1 * kvs1 >= groups * kvs) {
+          ks = 1;
+          groups = g1;
+          hp = hp1;
+          qtiles = qt1;
+          kvs = kvs1;
         }
       }
       // partial and combine indices are 32-bit rows

@@ -46,29 +46,14 @@ static int launch_ks(const PrefillArgs& a, int causal, ihipStream_t* stream) {
   return (int)hipGetLastError();
 }
 
-// two key ranges per workgroup, the tile's K blocks split across kv_splits
-// workgroups that write partials (the combine follows, launched by the caller)
-template <class T, int D>
-static int launch_kvsplit(const PrefillArgs& a, int causal, ihipStream_t* stream) {
-  dim3 grid(a.num_groups), block(64 * kPrefillWaves);
-  if (causal)
-    hipLaunchKernelGGL((prefill_kernel<T, D, D, true, 2, false, false, true>), grid, block, 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<T, D, D, false, 2, false, false, true>), grid, block, 0, (hipStream_t)stream,
-                       a);
-  return (int)hipGetLastError();
-}
-
 template <class T, int D>
 static int launch_one(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
-  if (plan.kv_splits > 1) {
-    if (plan.num_splits != 2) return (int)hipErrorInvalidValue;  // the planner splits two-range plans only
-    return launch_kvsplit<T, D>(a, causal, stream);
-  }
   return plan.num_splits == 2 ? launch_ks<T, D, 2>(a, causal, stream) : launch_ks<T, D, 1>(a, causal, stream);
 }
 
 int launch_prefill(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
+  // keys split across workgroups (dense or cached): prefill_split.hip
+  if (plan.kv_splits > 1) return launch_prefill_split(a, plan, causal, stream);
   if (a.k_cache != nullptr) return launch_prefill_cached(a, plan, causal, stream);
   switch (plan.kernel) {
     case kPrefillF16D64: return launch_one<F16, 64>(a, plan, causal, stream);

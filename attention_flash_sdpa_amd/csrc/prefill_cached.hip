@@ -10,36 +10,30 @@
 
 namespace sdpa {
 
-template <class T, int D, int KS, bool ALIGN, bool KVSPLIT>
+template <class T, int D, int KS, bool ALIGN>
 static void launch_cached_form(const PrefillArgs& a, int causal, ihipStream_t* stream) {
   dim3 grid(a.num_groups), block(64 * kPrefillWaves);
   if (causal)
-    hipLaunchKernelGGL((prefill_kernel<T, D, D, true, KS, true, ALIGN, KVSPLIT>), grid, block, 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, true, KS, true, ALIGN>), grid, block, 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, D, false, KS, true, ALIGN, KVSPLIT>), grid, block, 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, D, false, KS, true, ALIGN>), grid, block, 0, (hipStream_t)stream, a);
 }
 
 // One fill instruction covers 1 KiB, i.e. 512 / D key rows; when the cache
 // length and the key count are multiples of that, no instruction straddles
 // the cache and the new keys, and the fills take a scalar base.
-template <class T, int D, int KS, bool KVSPLIT = false>
+template <class T, int D, int KS>
 static int launch_cached_ks(const PrefillArgs& a, int causal, ihipStream_t* stream) {
   constexpr int RSTEP = 512 / D;
   if (a.cache_len % RSTEP == 0 && a.kv_len % RSTEP == 0)
-    launch_cached_form<T, D, KS, true, KVSPLIT>(a, causal, stream);
+    launch_cached_form<T, D, KS, true>(a, causal, stream);
   else
-    launch_cached_form<T, D, KS, false, KVSPLIT>(a, causal, stream);
+    launch_cached_form<T, D, KS, false>(a, causal, stream);
   return (int)hipGetLastError();
 }
 
 template <class T, int D>
 static int launch_cached_one(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream) {
-  if (plan.kv_splits > 1) {  // the tile's keys split across workgroups: partials, then the combine
-    if (plan.num_splits != 2) return (int)hipErrorInvalidValue;
-    return launch_cached_ks<T, D, 2, true>(a, causal, stream);
-  }
   return plan.num_splits == 2 ? launch_cached_ks<T, D, 2>(a, causal, stream)
                               : launch_cached_ks<T, D, 1>(a, causal, stream);
 }

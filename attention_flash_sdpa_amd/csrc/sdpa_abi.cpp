@@ -38,7 +38,8 @@ int device_cus() {
 // A forced form of the 16-bit prefill kernels (for tuning sweeps and tests):
 // narrow1 / narrow2 = one wave per SIMD with one / two key ranges, occ2 = two
 // waves per SIMD, split4 = its four-key-range form, kvsplit = narrow2 with
-// the key range also split across workgroups; "" or "auto" = the
+// the key range also split across workgroups, kvsplit1 = narrow1 split across
+// workgroups; "" or "auto" = the
 // planner's choice.  The environment variable SDPA_PREFILL_VARIANT sets the
 // initial value, read once per process; sdpa_set_prefill_variant changes it.
 int variant_code(const char* e) {
@@ -48,6 +49,7 @@ int variant_code(const char* e) {
   if (!strcmp(e, "occ2")) return 5;
   if (!strcmp(e, "split4")) return 6;
   if (!strcmp(e, "kvsplit")) return 7;
+  if (!strcmp(e, "kvsplit1")) return 8;
   return -1;
 }
 

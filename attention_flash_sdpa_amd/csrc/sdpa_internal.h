@@ -54,7 +54,7 @@ constexpr int kMinSplitSaving = 5;  // ... and mainloop iterations it saves per 
 // kernel with one / two key ranges per workgroup, 5 = the two-waves-per-SIMD
 // 32-row kernel, 6 = its 8-wave, four-key-range form (tuning sweeps and tests
 // only), 7 = variant 4 with the key range also split across workgroups
-// (kv_splits >= 2).  cached: a cached-KV prefill (kv_len counts cache and new
+// (kv_splits >= 2), 8 = the same with one key range per workgroup.  cached: a cached-KV prefill (kv_len counts cache and new
 // keys), which the 16-bit kernels implement (not the fp8 one).  kv_split:
 // whether the plan may split key ranges across workgroups (the caller has a
 // workspace for the partials).
@@ -130,6 +130,10 @@ int launch_prefill_o2(const PrefillArgs& a, const sdpa_plan_t& plan, int causal,
 // the two-waves-per-SIMD kernel with the additive bias a.mask (masked prefill)
 int launch_prefill_o2_bias(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_prefill_cached(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
+// the one-wave kernel with its keys split across workgroups (plan.kv_splits >
+// 1), dense (a.k_cache == NULL) or cached; partials only, the caller launches
+// the combine
+int launch_prefill_split(const PrefillArgs& a, const sdpa_plan_t& plan, int causal, ihipStream_t* stream);
 int launch_mask_convert(const uint8_t* in, void* out, int64_t n, int out_dtype, ihipStream_t* stream);
 // HBM streaming-read probe (mask.hip): kProbeGroups workgroups
 constexpr int kProbeGroups = 2048;

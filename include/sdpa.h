@@ -183,6 +183,8 @@ const char* sdpa_last_error(void);
  *                           shapes where some ranges hold no key (sdpa_prefill_fwd
  *                           with a workspace only; other entry points run
  *                           "narrow2");
+ *   "kvsplit1"            : the same with one key range per workgroup
+ *                           ("narrow1" split across workgroups);
  *   "" / "auto" / NULL    : the planner's choice (the default).
  * The environment variable SDPA_PREFILL_VARIANT gives the initial value (read
  * once).  Unknown names return SDPA_ERR_UNSUPPORTED and change nothing.

@@ -96,7 +96,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["", "narrow1", "narrow2", "occ2", "split4", "kvsplit"])
+@pytest.mark.parametrize("variant", ["", "narrow1", "narrow2", "occ2", "split4", "kvsplit", "kvsplit1"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_q{c[1]}_c{c[2]}of{c[3]}_k{c[4]}_h{c[5]}x{c[6]}_d{c[7]}_"
                                              f"{'causal' if c[9] else 'full'}" for c in CASES])
 def test_cached_prefill(dev, case, variant, prefill_variant):

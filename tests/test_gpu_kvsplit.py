@@ -116,10 +116,11 @@ FORCED = [
 ]
 
 
+@pytest.mark.parametrize("variant", ["kvsplit", "kvsplit1"])
 @pytest.mark.parametrize("case", FORCED, ids=[f"B{c[0]}_q{c[1]}_k{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_"
                                              f"{'c' if c[7] else 'f'}" for c in FORCED])
-def test_forced_split_with_empty_ranges(dev, oracle_mod, case, prefill_variant):
-    prefill_variant("kvsplit")
+def test_forced_split_with_empty_ranges(dev, oracle_mod, case, variant, prefill_variant):
+    prefill_variant(variant)
     B, Sq, Sk, Hq, Hkv, D, dt, causal = case
     q, k, v = _draw(B, Sq, Sk, Hq, Hkv, D, dt, Sq * 31 + Sk)
     p = _plan(q, k, causal)
@@ -130,8 +131,9 @@ def test_forced_split_with_empty_ranges(dev, oracle_mod, case, prefill_variant):
     _check(oracle_mod, q, k, v, out, lse, causal=causal, scale=1 / math.sqrt(D))
 
 
-def test_forced_split_with_no_keys(dev, prefill_variant):
-    prefill_variant("kvsplit")
+@pytest.mark.parametrize("variant", ["kvsplit", "kvsplit1"])
+def test_forced_split_with_no_keys(dev, variant, prefill_variant):
+    prefill_variant(variant)
     q = torch.randn(2, 5, 4, 128).to(torch.bfloat16)
     k = torch.empty(2, 0, 2, 128, dtype=torch.bfloat16)
     ws, n = _poisoned_workspace(dev, q, k, k, False)

@@ -177,13 +177,13 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "split4", "kvsplit"])
+@pytest.mark.parametrize("variant", ["narrow1", "narrow2", "occ2", "split4", "kvsplit", "kvsplit1"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}_q{c[1]}_k{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_{str(c[6])[6:]}_{'c' if c[7] else 'f'}" for c in EDGE])
 def test_prefill_edge_shapes(dev, oracle_mod, case, variant, prefill_variant):
     """Every edge shape through every 16-bit prefill kernel form: one wave per
-    SIMD with one or two key ranges per workgroup (and the latter split
-    across workgroups, with a combine), two waves per SIMD with one or four
-    key ranges."""
+    SIMD with one or two key ranges per workgroup (and both split across
+    workgroups, with a combine), two waves per SIMD with one or four key
+    ranges."""
     prefill_variant(variant)
     B, Sq, Sk, Hq, Hkv, D, dt, causal = case
     g = torch.Generator().manual_seed(Sq * 1000 + Sk)

@@ -17,7 +17,8 @@ import isa_scan  # tests/ is on sys.path (pytest prepends the test file's folder
 pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
 
-SOURCES = ["prefill.hip", "prefill_cached.hip", "prefill_o2.hip", "prefill_fp8.hip", "decode.hip"]
+SOURCES = ["prefill.hip", "prefill_cached.hip", "prefill_split.hip", "prefill_o2.hip", "prefill_fp8.hip",
+           "decode.hip"]
 
 
 @pytest.fixture(scope="module")
@@ -45,7 +46,7 @@ def _functions(text, marker):
     return "\n".join(parts)
 
 
-@pytest.mark.parametrize("src", ["prefill.hip", "prefill_cached.hip"])
+@pytest.mark.parametrize("src", ["prefill.hip", "prefill_cached.hip", "prefill_split.hip"])
 def test_hand_ordered_mfma_results_drained(asm, src):
     # only the one-wave kernel orders its MFMAs by hand (inline assembly);
     # the compiler places the wait states of builtin MFMAs itself
@@ -82,7 +83,7 @@ def test_transcendental_results_waited_for(asm, src):
     assert n > 0 and not bad, bad[:5]
 
 
-@pytest.mark.parametrize("src", ["prefill.hip", "prefill_o2.hip"])
+@pytest.mark.parametrize("src", ["prefill.hip", "prefill_split.hip", "prefill_o2.hip"])
 def test_lds_dma_scalar_base_wait_states(asm, src):
     bad, n = isa_scan.lds_dma_scalar_base(asm[src])
     assert n > 0 and not bad, bad[:5]
@@ -94,7 +95,7 @@ def test_lds_dma_m0_wait_state(asm, src):
     assert not bad, bad[:5]
 
 
-@pytest.mark.parametrize("src", ["prefill.hip", "prefill_o2.hip"])
+@pytest.mark.parametrize("src", ["prefill.hip", "prefill_split.hip", "prefill_o2.hip"])
 def test_untracked_q_loads_waited_for(asm, src):
     bad, n = isa_scan.untracked_loads_waited(asm[src])
     assert n > 0 and not bad, bad[:5]

@@ -98,15 +98,15 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [None, "kvsplit"])
+@pytest.mark.parametrize("variant", [None, "kvsplit", "kvsplit1"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"B{s[0]}_q{s[1]}_k{s[2]}_h{s[3]}x{s[4]}_{'c' if s[5] else 'f'}"
                                                for s in SHAPES])
 def test_work_decode_covers_every_block_once(shape, variant, prefill_variant):
     B, Sq, Sk, Hq, Hkv, causal = shape
     prefill_variant(variant)
     p = sdpa.plan(_problem(B, Sq, Sk, Hq, Hkv, 128, causal), num_cus=256)
-    if variant == "kvsplit":
-        assert p.kv_splits >= 2 and p.num_splits == 2 and p.kernel in (1, 3)
+    if variant is not None:
+        assert p.kv_splits >= 2 and p.num_splits == (2 if variant == "kvsplit" else 1) and p.kernel in (1, 3)
     seen, writes = _simulate(B, Sq, Sk, Hq, Hkv, causal, p)
     for b in range(B):
         for h in range(Hq):
@@ -121,15 +121,16 @@ def test_work_decode_covers_every_block_once(shape, variant, prefill_variant):
 
 
 def test_short_chunk_over_long_keys_splits_to_fill_the_gpu():
-    """16 queries over 8,192 keys, 32/8 heads: 16 tiles of two heads, two key
-    ranges each, split over 16 workgroups -> 256 workgroups of 4 blocks per
-    range, partials for 512 rows x 16 splits."""
+    """16 queries over 8,192 keys, 32/8 heads: 8 tiles of the four heads of a
+    group, one key range each, split over 32 workgroups -> 256 workgroups of
+    4 blocks, partials for 512 rows x 32 splits.  The two-range form would
+    split 16 tiles of two heads 16 ways."""
     p = sdpa.plan(_problem(1, 16, 8192, 32, 8, 128, True), num_cus=256)
-    assert (p.num_splits, p.kv_splits, p.num_groups) == (2, 16, 256)
+    assert (p.num_splits, p.kv_splits, p.num_groups, p.heads_per_group) == (1, 32, 256, 4)
     assert (p.range_iters_max, p.range_iters_min) == (4, 4)
     rows = 16 * 32
-    po = rows * 16 * 128 * 4
-    assert p.workspace_bytes == -(-po // 256) * 256 + rows * 16 * 2 * 4
+    po = rows * 32 * 128 * 4
+    assert p.workspace_bytes == -(-po // 256) * 256 + rows * 32 * 2 * 4
     assert p.combine_groups == rows // 4
 
 
@@ -169,7 +170,7 @@ def test_auto_split_never_needs_a_second_round(B, Sq, Sk, Hq, Hkv):
 
 def test_workspace_query_matches_the_plan(prefill_variant):
     lib = sdpa.load()
-    for variant in (None, "kvsplit", "narrow2"):
+    for variant in (None, "kvsplit", "kvsplit1", "narrow2"):
         prefill_variant(variant)
         for B, Sq, Sk, Hq, Hkv, causal in SHAPES:
             pr = _problem(B, Sq, Sk, Hq, Hkv, 64, causal)
