@@ -61,6 +61,30 @@ def test_prefill_graph_replay(dev):
     _replays_match(dev, lambda i: sdpa.prefill(qd, kd, vd, scale=w.scale, causal=True, out=out, lse=lse), out, 2)
 
 
+def test_split_prefill_graph_replay(dev):
+    """A 16-token chunk over 8,192 keys: the split kernel and the combine
+    through one workspace, captured and replayed; lse checked too."""
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    q, k, v, _ = inputs.make_qkv(w, q_len=16, kv_len=8192)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    n = sdpa.prefill_workspace_bytes(qd, kd, vd, causal=True)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = torch.empty(w.batch, 16, w.head_q, w.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.batch, w.head_q, 16, dtype=torch.float32, device=dev)
+    _say("split prefill graph: causal GQA bf16 q 16 kv 8192")
+
+    def call(i):
+        sdpa.prefill(qd, kd, vd, scale=w.scale, causal=True, out=out, lse=lse, workspace=ws)
+
+    _replays_match(dev, call, out, 2)
+    lse_want = lse.clone()
+    lse.zero_()
+    call(0)
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse_want)
+
+
 def test_decode_graph_replay(dev):
     w = inputs.WORKLOADS["splitkv_decode_bf16"]
     q, k, v, _ = inputs.make_qkv(w, kv_len=1500)
