@@ -3,7 +3,7 @@
  *
  * A plain, slow, obviously correct fp64 CPU definition of scaled-dot-product
  * attention, used only by tests/, the package smoke check and the benchmark's
- * CPU-baseline leg to judge the HIP kernels.  It shares no code, header, table
+ * CPU-baseline leg to check the HIP kernels.  It shares no code, header, table
  * or helper with the GPU library.
  *
  * What it computes (the definition the pages' blocked algorithm reaches):
