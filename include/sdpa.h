@@ -116,9 +116,11 @@ typedef struct sdpa_plan {
                                prefill: key ranges per workgroup (1, 2 or 4), each
                                streamed by its own waves, merged at the end    */
   int32_t blocks_per_split; /* decode: K/V blocks per split                     */
-  int32_t combine_groups;   /* decode: workgroups of the combine kernel         */
+  int32_t combine_groups;   /* decode, and prefill with kv_splits > 1:
+                               workgroups of the combine kernel                */
   uint64_t lds_bytes;       /* LDS per workgroup of the main kernel             */
-  uint64_t workspace_bytes; /* device workspace the call needs                  */
+  uint64_t workspace_bytes; /* device workspace the call needs (prefill: for
+                               the kv_splits > 1 plan; smaller runs unsplit)   */
   /* Prefill load balance (0 for decode).  Every key range of a workgroup runs
    * ceil(K blocks of its query rows / num_splits) mainloop iterations (the
    * causal K-block range of "Xe SDPA Forward Mainloop", section "Outer
