@@ -192,7 +192,10 @@ _SOURCES = {"prefill": ["prefill.hip", "prefill_kernel.h", "prefill_o2.hip", "pr
             "fp8": ["prefill_fp8.hip", "sdpa_device.h", "lds_layout.h", "sdpa_internal.h", "sdpa_bounds.h"],
             "masked": ["prefill_o2.hip", "prefill_o2_kernel.h", "sdpa_device.h", "lds_layout.h", "sdpa_internal.h",
                        "sdpa_bounds.h"],
-            "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"]}
+            "mask": ["mask.hip", "sdpa_device.h", "sdpa_internal.h"],
+            "split": ["prefill_split.hip", "prefill_kernel.h", "decode.hip", "sdpa_device.h", "lds_layout.h",
+                      "sdpa_internal.h", "sdpa_bounds.h"]}
+SPLIT_COUNTERS = "prefill_split_chunk16_over8192_bf16_counters.txt"
 def _cached_chunk():
     from attention_flash_sdpa_amd import inputs
 
@@ -307,8 +310,21 @@ def _counters_pass():
     for _ in range(3):
         sdpa.prefill_masked(mq, mk, mv, mbias, scale=MASKED.scale)
     torch.cuda.synchronize()
+    del mq, mk, mv, mbias
+    # the split prefill leg: one call per rotating K/V set (past the
+    # last-level cache, so every call reads its keys from HBM)
+    sw = SPLIT_CHUNK
+    g = torch.Generator().manual_seed(sw.seed)
+    sq = torch.randn(sw.batch, sw.q_len, sw.head_q, sw.d_qk, generator=g).to(torch.bfloat16).to(dev)
+    s_sets = [tuple(torch.randn(sw.batch, sw.kv_len, sw.head_kv, sw.d_qk, generator=g).to(torch.bfloat16).to(dev)
+                    for _ in range(2)) for _ in range(sw.kv_sets)]
+    sws = torch.empty(sdpa.prefill_workspace_bytes(sq, *s_sets[0], causal=True), dtype=torch.uint8, device=dev)
+    for kk, vv in s_sets:
+        sdpa.prefill(sq, kk, vv, causal=True, scale=sw.scale, workspace=sws)
+    torch.cuda.synchronize()
     print(f"counters pass done: copy {src.numel()} B x3, prefill x5, decode x20, paged decode x5 per page size, "
-          f"mask conversion x6, unaligned / fp8 / cached / masked prefill x3 each", flush=True)
+          f"mask conversion x6, unaligned / fp8 / cached / masked prefill x3 each, split prefill x{sw.kv_sets}",
+          flush=True)
 
 
 def _masked_inputs(dev):
@@ -577,6 +593,41 @@ def _summarize_counters(fetch_dir, write_dir):
             f.write(f"hbm_bytes_per_launch: {ptot[ps]:.0f}\n")
             f.write(f"ratio to algorithmic: {ptot[ps] / alg:.3f}\n")
             f.write(f"source_sha256: {_src_hash(*_SOURCES['decode'])}\n")
+        print("wrote", out)
+    # split prefill: each split-kernel dispatch with the combine dispatch that
+    # follows it (the combine's name and grid are the decode's)
+    sw = SPLIT_CHUNK
+    skname = _kernels_of(sdpa, sw)[0][0]
+    stot, slines = 0.0, []
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        kib_copy, factor, _, cname = res[counter]
+        rows = {int(r["Dispatch_Id"]): r for r in _read_csv(os.path.join(d, "run_counter_collection.csv"))
+                if r["Counter_Name"] == counter}
+        ids = sorted(i for i, r in rows.items() if skname in r["Kernel_Name"])
+        cids = [i for i in ids if i + 1 in rows and "decode_combine_kernel" in rows[i + 1]["Kernel_Name"]]
+        if not ids or len(cids) != len(ids):
+            continue
+        sk = statistics.mean(float(rows[i]["Counter_Value"]) for i in ids)
+        ck = statistics.mean(float(rows[i + 1]["Counter_Value"]) for i in ids)
+        b = (sk + ck) * 1024.0 * factor
+        stot += b
+        slines.append(f"{counter}: scale factor {factor:.4f} ({cname}); {skname} {sk:.1f} KiB + combine "
+                      f"{ck:.1f} KiB per call over {len(ids)} calls -> {b:.0f} B\n")
+    if len(slines) == 2:
+        out = os.path.join(ROOT, "profiles", SPLIT_COUNTERS)
+        alg = sw.bytes_moved()
+        with open(out, "w") as f:
+            f.write(f"workload: {sw.name} ({sw.q_len} queries over {sw.kv_len} keys, {sw.head_q}/{sw.head_kv} heads, "
+                    f"one call per rotating K/V set)\n")
+            f.write("commands: as for prefill_gqa_causal_bf16_counters.txt (the counters pass ends with the split "
+                    "prefill calls)\n")
+            for line in slines:
+                f.write(line)
+            f.write(f"algorithmic bytes per call (Q+K+V+O once): {alg}\n")
+            f.write(f"hbm_bytes_per_launch: {stot:.0f}\n")
+            f.write(f"ratio to algorithmic: {stot / alg:.3f} (the rest is the fp32 partials, written and read "
+                    f"once)\n")
+            f.write(f"source_sha256: {_src_hash(*_SOURCES['split'])}\n")
         print("wrote", out)
     if len(mres) == 2:
         out = os.path.join(ROOT, "profiles", "mask_convert_16x4096x4096_counters.txt")
@@ -877,7 +928,8 @@ def main():
                   "tflops": round(sw.flops() / (sms * 1e-3) / 1e12, 3),
                   "algorithmic_bytes": sw.bytes_moved(),
                   "roofline": {"bound": "hbm", "achieved": round(sgbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": round(sgbs / PEAK_HBM_GBS, 5), "traffic": None},
+                               "frac": round(sgbs / PEAK_HBM_GBS, 5),
+                               "traffic": _traffic(SPLIT_COUNTERS, _SOURCES["split"])},
                   "parity": {"max_abs_err": serr, "nan": snan, "rows": sw.q_len * sw.head_q},
                   "cpu_baseline": _cpu_line(round(sw.bytes_moved() / ssec / 1e9, 3), "GB/s",
                                             torch.get_num_threads(),
