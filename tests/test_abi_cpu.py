@@ -310,6 +310,27 @@ def test_cached_prefill_argument_errors_before_any_launch():
 
 
 
+def test_split_prefill_workspace_errors_before_any_launch():
+    """A split plan with a large enough workspace checks its alignment before
+    any launch; the cached form likewise."""
+    import ctypes
+
+    lib = sdpa.load()
+    w = inputs.WORKLOADS["gqa_causal_prefill_bf16"]
+    a, null = ctypes.c_void_p(0x1000), ctypes.c_void_p(0)
+    pr = _problem(w, q_len=16, kv_len=8192)
+    need = lib.sdpa_prefill_workspace_bytes(ctypes.byref(pr))
+    assert need > 0
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.sdpa_prefill_fwd(ctypes.byref(pr), a, a, a, a, null, odd, need, null) == 5
+    assert b"workspace" in lib.sdpa_last_error()
+    chunk = _problem(w, q_len=16, kv_len=16)
+    cneed = lib.sdpa_prefill_cached_workspace_bytes(ctypes.byref(chunk), 8176)
+    assert cneed == need
+    assert lib.sdpa_prefill_cached_fwd(ctypes.byref(chunk), a, a, a, 8176, 8192, a, a, a, null, odd, cneed,
+                                       null) == 5
+
+
 def test_mask_convert_argument_errors_before_any_launch():
     import ctypes
 
