@@ -355,7 +355,10 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int NSLOT = NQK + NPV;
   constexpr int kPD = 4;                        // read-ahead distance (slots)
   constexpr int NDMA = K_INSTR + V_INSTR;
-  constexpr int DSTRIDE = NSLOT / NDMA > 0 ? NSLOT / NDMA : 1;
+  // the direct loads go one per DSTRIDE slots; the split form streams its
+  // keys from HBM (no other workgroup shares them), so it issues them in the
+  // first slots and gives them the rest of the iteration to land
+  constexpr int DSTRIDE = KVSPLIT ? 1 : (NSLOT / NDMA > 0 ? NSLOT / NDMA : 1);
   static_assert(NQK % 8 == 0 && NPV % 4 == 0, "slot counts");
 
   auto iteration = [&](int j, float m_sub, auto mcur_tag, auto mnext_tag, auto next_tag, auto par_tag)
